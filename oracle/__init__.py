@@ -1,0 +1,226 @@
+"""CPU oracle for MoE EP dispatch/combine -- test infrastructure only.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  It wraps ``ep_oracle.c`` (plain scalar C, built with gcc)
+through ctypes and shares nothing with the HIP library.
+
+Pinned functions (each checked in ``tests/test_oracle_*.py`` against something
+other than itself): layout, bf16 dispatch, FP8 quantisation (scale exponent and
+e4m3fn codes), dequantisation, combine.  Nothing here is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libep_oracle.so")
+_lib = None
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    lib.eo_bf16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.eo_bf16_to_f32.restype = ctypes.c_float
+    lib.eo_f32_to_bf16.argtypes = [ctypes.c_float]
+    lib.eo_f32_to_bf16.restype = ctypes.c_uint16
+    lib.eo_e4m3_value.argtypes = [ctypes.c_int]
+    lib.eo_e4m3_value.restype = ctypes.c_double
+    lib.eo_e4m3_encode.argtypes = [ctypes.c_double]
+    lib.eo_e4m3_encode.restype = ctypes.c_uint8
+    lib.eo_ue8m0_exponent.argtypes = [ctypes.c_float]
+    lib.eo_ue8m0_exponent.restype = ctypes.c_int
+    lib.eo_quantize_row.argtypes = [P, ctypes.c_int32, P, P]
+    lib.eo_quantize_row.restype = None
+    lib.eo_dequant_row.argtypes = [P, P, ctypes.c_int32, P]
+    lib.eo_dequant_row.restype = None
+    lib.eo_layout.argtypes = [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                              ctypes.c_int64, ctypes.c_int32, P, P, P, P, P, P, P, P]
+    lib.eo_layout.restype = ctypes.c_int64
+    lib.eo_dispatch_bf16.argtypes = [P, ctypes.c_int32, P, ctypes.c_int64, P]
+    lib.eo_dispatch_bf16.restype = None
+    lib.eo_dispatch_fp8.argtypes = [P, ctypes.c_int32, P, ctypes.c_int64, P, P]
+    lib.eo_dispatch_fp8.restype = None
+    lib.eo_combine.argtypes = [P, ctypes.c_int32, P, P, ctypes.c_int64, ctypes.c_int32, P]
+    lib.eo_combine.restype = None
+    lib.eo_combine_gathered.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int32,
+                                        ctypes.c_int32, P]
+    lib.eo_combine_gathered.restype = None
+    lib.eo_e4m3_encode_n.argtypes = [P, ctypes.c_int64, P]
+    lib.eo_e4m3_encode_n.restype = None
+    lib.eo_f32_to_bf16_n.argtypes = [P, ctypes.c_int64, P]
+    lib.eo_f32_to_bf16_n.restype = None
+    lib.eo_ue8m0_exponent_n.argtypes = [P, ctypes.c_int64, P]
+    lib.eo_ue8m0_exponent_n.restype = None
+    _lib = lib
+    return lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def capacity_rows(tokens: int, top_k: int, num_experts: int, block_m: int) -> int:
+    return tokens * top_k + num_experts * (block_m - 1)
+
+
+# ------------------------------------------------------------- scalar forms --
+
+def bf16_to_f32(b: int) -> float:
+    return float(_load().eo_bf16_to_f32(int(b)))
+
+
+def f32_to_bf16(f: float) -> int:
+    return int(_load().eo_f32_to_bf16(float(f)))
+
+
+def e4m3_value(code: int) -> float:
+    return float(_load().eo_e4m3_value(int(code)))
+
+
+def e4m3_encode(v: float) -> int:
+    return int(_load().eo_e4m3_encode(float(v)))
+
+
+def ue8m0_exponent(amax: float) -> int:
+    return int(_load().eo_ue8m0_exponent(float(amax)))
+
+
+# -------------------------------------------------------------- array forms --
+
+def e4m3_encode_n(v: np.ndarray) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float64).ravel()
+    out = np.empty(v.size, dtype=np.uint8)
+    _load().eo_e4m3_encode_n(_p(v), v.size, _p(out))
+    return out
+
+
+def f32_to_bf16_n(f: np.ndarray) -> np.ndarray:
+    shape = np.shape(f)
+    f = np.ascontiguousarray(f, dtype=np.float32).ravel()
+    out = np.empty(f.size, dtype=np.uint16)
+    _load().eo_f32_to_bf16_n(_p(f), f.size, _p(out))
+    return out.reshape(shape)
+
+
+def ue8m0_exponent_n(amax: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(amax, dtype=np.float32).ravel()
+    out = np.empty(a.size, dtype=np.int32)
+    _load().eo_ue8m0_exponent_n(_p(a), a.size, _p(out))
+    return out
+
+
+def quantize_row(x_row: np.ndarray):
+    x_row = np.ascontiguousarray(x_row, dtype=np.uint16)
+    H = x_row.size
+    q = np.empty(H, dtype=np.uint8)
+    s = np.empty(H // 128, dtype=np.uint8)
+    _load().eo_quantize_row(_p(x_row), H, _p(q), _p(s))
+    return q, s
+
+
+def dequant_rows(q: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Dequantise rows q[n, H] with scales[n, H/128] to bf16 bits [n, H]."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    n, H = q.shape
+    out = np.empty((n, H), dtype=np.uint16)
+    lib = _load()
+    for i in range(n):
+        lib.eo_dequant_row(_p(q[i]), _p(scales[i]), H, _p(out[i]))
+    return out
+
+
+# ------------------------------------------------------------------ layout --
+
+def layout(topk_idx: np.ndarray, num_experts: int, block_m: int,
+           cap: Optional[int] = None) -> Dict[str, np.ndarray]:
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    T, K = idx.shape
+    E, BM = int(num_experts), int(block_m)
+    if cap is None:
+        cap = capacity_rows(T, K, E, BM)
+    max_tiles = cap // BM
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    num_tiles = np.zeros(1, np.int32)
+    tile_expert = np.empty(max_tiles, np.int32)
+    tile_target = np.empty(max_tiles, np.int32)
+    slot_to_row = np.empty(T * K, np.int32)
+    recv_token = np.empty(cap, np.int32)
+    error = np.zeros(1, np.int32)
+    P = _load().eo_layout(_p(idx), T, K, E, BM, cap, max_tiles, _p(counts), _p(offsets),
+                          _p(num_tiles), _p(tile_expert), _p(tile_target), _p(slot_to_row),
+                          _p(recv_token), _p(error))
+    if P < 0:
+        raise ValueError("pool capacity too small for this routing")
+    return {"expert_counts": counts, "expert_pool_block_offset": offsets,
+            "num_tiles": int(num_tiles[0]), "tile_expert": tile_expert,
+            "pool_arrival_target": tile_target, "slot_to_pool_row": slot_to_row,
+            "pool_recv_token": recv_token, "error": int(error[0]), "pool_rows": int(P),
+            "capacity_rows": cap, "max_tiles": max_tiles}
+
+
+# ---------------------------------------------------------------- dispatch --
+
+def dispatch_bf16(x: np.ndarray, recv_token: np.ndarray,
+                  pool_init: Optional[np.ndarray] = None) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    recv = np.ascontiguousarray(recv_token, dtype=np.int32)
+    H = x.shape[1]
+    cap = recv.size
+    pool = (np.zeros((cap, H), np.uint16) if pool_init is None
+            else np.array(pool_init, dtype=np.uint16, copy=True, order="C"))
+    _load().eo_dispatch_bf16(_p(x), H, _p(recv), cap, _p(pool))
+    return pool
+
+
+def dispatch_fp8(x: np.ndarray, recv_token: np.ndarray, pool_init: Optional[np.ndarray] = None,
+                 scales_init: Optional[np.ndarray] = None):
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    recv = np.ascontiguousarray(recv_token, dtype=np.int32)
+    H = x.shape[1]
+    cap = recv.size
+    pool = (np.zeros((cap, H), np.uint8) if pool_init is None
+            else np.array(pool_init, dtype=np.uint8, copy=True, order="C"))
+    scales = (np.zeros((cap, H // 128), np.uint8) if scales_init is None
+              else np.array(scales_init, dtype=np.uint8, copy=True, order="C"))
+    _load().eo_dispatch_fp8(_p(x), H, _p(recv), cap, _p(pool), _p(scales))
+    return pool, scales
+
+
+# ----------------------------------------------------------------- combine --
+
+def combine(expert_out: np.ndarray, slot_to_row: np.ndarray, weights: np.ndarray) -> np.ndarray:
+    eo = np.ascontiguousarray(expert_out, dtype=np.uint16)
+    w = np.ascontiguousarray(weights, dtype=np.float32)
+    T, K = w.shape
+    H = eo.shape[1]
+    s2r = np.ascontiguousarray(slot_to_row, dtype=np.int32)
+    y = np.empty((T, H), np.uint16)
+    _load().eo_combine(_p(eo), H, _p(s2r), _p(w), T, K, _p(y))
+    return y
+
+
+def combine_gathered(rows: np.ndarray, valid: np.ndarray, weights: np.ndarray) -> np.ndarray:
+    """rows[n, K, H] bf16 bits, valid[n, K] (bool), weights[n, K] -> y[n, H]."""
+    rows = np.ascontiguousarray(rows, dtype=np.uint16)
+    n, K, H = rows.shape
+    v = np.ascontiguousarray(valid, dtype=np.int32)
+    w = np.ascontiguousarray(weights, dtype=np.float32)
+    y = np.empty((n, H), np.uint16)
+    _load().eo_combine_gathered(_p(rows), _p(v), _p(w), n, K, H, _p(y))
+    return y
