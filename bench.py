@@ -1,0 +1,259 @@
+"""Benchmark: one GPU's share of MoE EP dispatch + combine on MI355X.
+
+A step is one pass of the whole path over one batch: layout (counts, scan,
+tiles, stable ranks), dispatch (pool copy; FP8 quantisation and streaming
+release where the workload asks for them) and combine.  The default workload
+is the prefill share: 16384 tokens, hidden 7168, 256 experts with Zipf(1.2)
+top-8 routing, BLOCK_M 128, bf16.  Inputs are seeded synthetic data already
+resident in HBM when the timed region starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+                    [--no-cpu-baseline] [--copy-calibration]
+
+Prints one JSON line.  Per-kernel times come from HIP events recorded on the
+stream the kernels are launched on (torch's current stream, which is passed
+to the library).  "value" is algorithmic bytes moved per step / step time.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_GBS = 8000.0     # MI355X HBM3E peak, GB/s
+METRIC = "dispatch+combine HBM GB/s and % of MI355X peak; tokens/s at 16384 tok"
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(cfg, idx: np.ndarray, counts: np.ndarray, fp8: bool):
+    """Bytes each kernel must move, every item once (padding rows never move).
+
+    layout:   read topk_idx + topk_weights, write slot_to_pool_row + weights
+              (16*T*K) and pool_recv_token for every capacity row (4*cap)
+    dispatch: read slot_to_pool_row (4*T*K), read each active token's row of
+              x once (2*H*T_act), write N_a pool rows (b*H*N_a, b = 2 bf16 /
+              1 fp8) and, for FP8, N_a*H/128 scale bytes
+    combine:  read slot_to_pool_row + weights (8*T*K), read N_a expert rows
+              (2*H*N_a), write y (2*H*T)
+    """
+    T, K, H = cfg.tokens, cfg.top_k, cfg.hidden
+    valid = idx >= 0
+    n_a = int(valid.sum())
+    t_act = int(valid.any(1).sum())
+    cap = cfg.capacity_rows
+    b = 1 if fp8 else 2
+    layout = 16 * T * K + 4 * cap
+    dispatch = 4 * T * K + 2 * H * t_act + b * H * n_a + (n_a * (H // 128) if fp8 else 0)
+    combine = 8 * T * K + 2 * H * n_a + 2 * H * T
+    return {"layout": layout, "dispatch": dispatch, "combine": combine,
+            "n_a": n_a, "t_act": t_act, "pool_rows": int(((counts + cfg.block_m - 1)
+                                                          // cfg.block_m).sum() * cfg.block_m)}
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "combine_ep_layout_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str, per_launch_alg: float):
+    """HBM traffic of a kernel from the committed rocprofv3 counter summary,
+    or None when there is none or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, _, v = line.partition(":")
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha") != kernel_source_sha():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(cfg, d, eo_host: np.ndarray, alg_total: int, reps: int):
+    """Time the oracle (single-threaded C) on the same workload."""
+    import oracle
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        L = oracle.layout(d["topk_idx"], cfg.num_experts, cfg.block_m)
+        if cfg.fp8:
+            oracle.dispatch_fp8(d["x"], L["pool_recv_token"])
+        else:
+            oracle.dispatch_bf16(d["x"], L["pool_recv_token"])
+        oracle.combine(eo_host, L["slot_to_pool_row"], d["topk_weights"])
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    return {"value": round(alg_total / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seconds_per_pass": round(t, 3),
+            "tokens_per_s": round(cfg.tokens / t, 1),
+            "sample": f"the full {cfg.name} workload ({cfg.tokens} tokens), layout + "
+                      f"dispatch + combine, median of {reps} passes, one host thread"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of EP dispatch/combine; runs on more than "
+              "one GPU are not supported (use --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    import combine_ep_layout_amd as ep
+    from synth import CONFIGS, generate
+
+    cfg = CONFIGS[args.config]
+    fp8, ready = cfg.fp8, cfg.tile_ready
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    log(f"[bench] generating {cfg.name} inputs")
+    d = generate(cfg, 0)
+    T, K, H = cfg.tokens, cfg.top_k, cfg.hidden
+    idx = torch.from_numpy(d["topk_idx"]).to(dev)
+    w = torch.from_numpy(d["topk_weights"]).to(dev)
+    x = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+
+    h = ep.EpHandle(T, K, cfg.num_experts, cfg.block_m)
+    cap = h.capacity_rows
+    pool, scales = h.new_pool(H, fp8=fp8)
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    eo = torch.empty(cap, H, dtype=torch.bfloat16, device=dev)
+    for r0 in range(0, cap, 16384):                       # chunked to bound the fp32 temporary
+        r1 = min(cap, r0 + 16384)
+        eo[r0:r1] = torch.randn(r1 - r0, H, generator=g, device=dev).to(torch.bfloat16)
+    y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        epoch = h.layout(idx, w)
+        if ev is not None:
+            ev[1].record(stream)
+        h.dispatch(x, pool, scales, fp8=fp8, tile_ready=ready)
+        if ev is not None:
+            ev[2].record(stream)
+        h.combine(epoch, eo, y)
+        if ev is not None:
+            ev[3].record(stream)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert h.sync_status() == ep.EP_OK
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    lay = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    dis = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    com = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+
+    counts, _ = h.counts_to_host()
+    ab = algorithmic_bytes(cfg, d["topk_idx"], counts, fp8)
+    total = ab["layout"] + ab["dispatch"] + ab["combine"]
+    value = total / (ms_per_step * 1e-3) / 1e9
+    kern = {"dispatch": (dis, ab["dispatch"]), "combine": (com, ab["combine"])}
+    dom = max(kern, key=lambda k: kern[k][0])
+    dom_ms, dom_bytes = kern[dom]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = read_traffic(dom, cfg.name, dom_bytes)
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 29, dtype=torch.int16, device=dev)       # 1 GiB
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        eo_host = eo.view(torch.int16).cpu().numpy().view(np.uint16)
+        cpu = cpu_baseline(cfg, d, eo_host, total, args.cpu_reps)
+        del eo_host
+
+    mode = "fp8" if fp8 else "bf16"
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": mode,
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {T} tokens, hidden {H}, {cfg.num_experts} experts "
+                               f"{cfg.routing} top-{K}, BLOCK_M {cfg.block_m}, {mode}"
+                               + (", tile_ready" if ready else ""),
+                   "tokens": T, "hidden": H, "top_k": K, "num_experts": cfg.num_experts,
+                   "block_m": cfg.block_m, "routing": cfg.routing},
+        "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "pct_of_peak": round(100.0 * value / PEAK_GBS, 2),
+        "kernels_us": {"layout": round(lay * 1e3, 2), "dispatch": round(dis * 1e3, 2),
+                       "combine": round(com * 1e3, 2)},
+        "alg_bytes": {k: ab[k] for k in ("layout", "dispatch", "combine")},
+        "routing_stats": {"n_assign": ab["n_a"], "active_tokens": ab["t_act"],
+                          "pool_rows": ab["pool_rows"], "max_expert_rows": int(counts.max())},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
+                     "peak": PEAK_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+    }
+    h.close()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,277 @@
+"""Python binding of libep_layout.so: MoE expert-parallel dispatch/combine on
+one MI355X (gfx950).
+
+Argument marshalling only: every step of layout, dispatch and combine runs in
+the library's HIP kernels.  PyTorch provides device memory and streams; the
+library is loaded after torch so that both share torch's HIP runtime.  Import
+fails loudly when the library has not been built (``python -m
+combine_ep_layout_amd.build``).
+
+The names follow the C ABI in include/ep_layout.h (ep_handle_create,
+ep_layout, ep_dispatch, ep_combine, ...); ``EpHandle`` bundles them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libep_layout.so")
+
+EP_OK = 0
+EP_ERR_INVALID_ARGUMENT = 1
+EP_ERR_UNSUPPORTED = 2
+EP_ERR_OUT_OF_MEMORY = 3
+EP_ERR_HANDLE_STATE = 4
+EP_ERR_BAD_ROUTING = 5
+EP_ERR_TIMEOUT = 6
+EP_ERR_HIP = 7
+
+EP_DISPATCH_FP8 = 1 << 0
+EP_DISPATCH_TILE_READY = 1 << 1
+
+ARRAYS = {
+    "expert_counts": (0, torch.int32),
+    "expert_pool_block_offset": (1, torch.int32),
+    "num_tiles": (2, torch.int32),
+    "tile_expert": (3, torch.int32),
+    "pool_arrival_target": (4, torch.int32),
+    "pool_arrival_count": (5, torch.int32),
+    "tile_ready": (6, torch.int32),
+    "slot_to_pool_row": (7, torch.int32),
+    "pool_recv_token": (8, torch.int32),
+    "topk_weights": (9, torch.float32),
+}
+
+EXPORTS = [
+    "ep_handle_create", "ep_handle_destroy", "ep_pool_capacity_rows", "ep_max_tiles",
+    "ep_num_tokens", "ep_layout", "ep_dispatch", "ep_combine", "ep_handle_get_view",
+    "ep_array_bytes", "ep_copy_array", "ep_counts_to_host", "ep_handle_sync_status",
+    "ep_tile_consume", "ep_status_string",
+]
+
+
+class EpError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_lib.ep_status_string(status).decode()} (status {status})")
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [("max_tokens", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("num_experts", ctypes.c_int32), ("block_m", ctypes.c_int32)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          f"'python -m combine_ep_layout_amd.build' (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, U32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_int64
+    st = ctypes.c_int
+    sig = {
+        "ep_handle_create": (st, [ctypes.POINTER(_Config), ctypes.POINTER(P)]),
+        "ep_handle_destroy": (st, [P]),
+        "ep_pool_capacity_rows": (I64, [P]),
+        "ep_max_tiles": (I32, [P]),
+        "ep_num_tokens": (I32, [P]),
+        "ep_layout": (st, [P, P, P, I32, P, ctypes.POINTER(U32)]),
+        "ep_dispatch": (st, [P, P, I32, P, P, U32, P, ctypes.POINTER(U32)]),
+        "ep_combine": (st, [P, U32, P, I32, P, P]),
+        "ep_handle_get_view": (st, [P, P]),
+        "ep_array_bytes": (I64, [P, ctypes.c_int]),
+        "ep_copy_array": (st, [P, ctypes.c_int, P, I64, P]),
+        "ep_counts_to_host": (st, [P, P, P, P]),
+        "ep_handle_sync_status": (st, [P, P]),
+        "ep_tile_consume": (st, [P, U32, P, P, I32, U32, P, I32, U32, P]),
+        "ep_status_string": (ctypes.c_char_p, [st]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def library() -> ctypes.CDLL:
+    return _lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != EP_OK:
+        raise EpError(status, where)
+
+
+def _require(t: torch.Tensor, dtype, name: str, device: torch.device):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+# --------------------------------------------------- functions of the C ABI --
+
+def ep_handle_create(max_tokens: int, top_k: int, num_experts: int, block_m: int) -> ctypes.c_void_p:
+    cfg = _Config(max_tokens, top_k, num_experts, block_m)
+    h = ctypes.c_void_p()
+    _check(_lib.ep_handle_create(ctypes.byref(cfg), ctypes.byref(h)), "ep_handle_create")
+    return h
+
+
+def ep_handle_destroy(h) -> None:
+    _check(_lib.ep_handle_destroy(h), "ep_handle_destroy")
+
+
+def ep_layout(h, topk_idx: torch.Tensor, topk_weights: torch.Tensor, stream=None) -> int:
+    epoch = ctypes.c_uint32()
+    T = topk_idx.shape[0]
+    _check(_lib.ep_layout(h, _ptr(topk_idx), _ptr(topk_weights), T, _stream(stream),
+                          ctypes.byref(epoch)), "ep_layout")
+    return epoch.value
+
+
+def ep_dispatch(h, x: torch.Tensor, pool: torch.Tensor, pool_scales: Optional[torch.Tensor],
+                flags: int, stream=None) -> int:
+    seq = ctypes.c_uint32()
+    _check(_lib.ep_dispatch(h, _ptr(x), x.shape[1], _ptr(pool), _ptr(pool_scales), flags,
+                            _stream(stream), ctypes.byref(seq)), "ep_dispatch")
+    return seq.value
+
+
+def ep_combine(h, epoch: int, expert_out: torch.Tensor, y: torch.Tensor, stream=None) -> None:
+    _check(_lib.ep_combine(h, epoch, _ptr(expert_out), expert_out.shape[1], _ptr(y),
+                           _stream(stream)), "ep_combine")
+
+
+def ep_tile_consume(h, seq: int, pool: torch.Tensor, pool_scales: Optional[torch.Tensor],
+                    hidden: int, flags: int, out: torch.Tensor, workgroups: int,
+                    spin_limit_us: int, stream=None) -> None:
+    _check(_lib.ep_tile_consume(h, seq, _ptr(pool), _ptr(pool_scales), hidden, flags, _ptr(out),
+                                workgroups, spin_limit_us, _stream(stream)), "ep_tile_consume")
+
+
+def ep_handle_sync_status(h, stream=None) -> int:
+    return int(_lib.ep_handle_sync_status(h, _stream(stream)))
+
+
+# ------------------------------------------------------------- convenience --
+
+class EpHandle:
+    """One layout's metadata on the current device (owns an ep_handle)."""
+
+    def __init__(self, max_tokens: int, top_k: int, num_experts: int, block_m: int):
+        self.max_tokens, self.top_k = int(max_tokens), int(top_k)
+        self.num_experts, self.block_m = int(num_experts), int(block_m)
+        self.device = torch.device("cuda", torch.cuda.current_device())
+        self._h = ep_handle_create(max_tokens, top_k, num_experts, block_m)
+        self.capacity_rows = int(_lib.ep_pool_capacity_rows(self._h))
+        self.max_tiles = int(_lib.ep_max_tiles(self._h))
+
+    @property
+    def raw(self):
+        return self._h
+
+    @property
+    def num_tokens(self) -> int:
+        return int(_lib.ep_num_tokens(self._h))
+
+    def close(self):
+        if self._h is not None and self._h.value:
+            ep_handle_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def layout(self, topk_idx: torch.Tensor, topk_weights: torch.Tensor, stream=None) -> int:
+        _require(topk_idx, torch.int32, "topk_idx", self.device)
+        _require(topk_weights, torch.float32, "topk_weights", self.device)
+        if topk_idx.dim() != 2 or topk_idx.shape[1] != self.top_k or topk_weights.shape != topk_idx.shape:
+            raise ValueError("topk_idx / topk_weights must both be [num_tokens, top_k]")
+        return ep_layout(self._h, topk_idx, topk_weights, stream)
+
+    def new_pool(self, hidden: int, fp8: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+        if fp8:
+            return (torch.empty(self.capacity_rows, hidden, dtype=torch.uint8, device=self.device),
+                    torch.empty(self.capacity_rows, hidden // 128, dtype=torch.uint8, device=self.device))
+        return torch.empty(self.capacity_rows, hidden, dtype=torch.bfloat16, device=self.device), None
+
+    def dispatch(self, x: torch.Tensor, pool: torch.Tensor, pool_scales: Optional[torch.Tensor] = None,
+                 fp8: bool = False, tile_ready: bool = False, stream=None) -> int:
+        _require(x, torch.bfloat16, "x", self.device)
+        if x.dim() != 2 or x.shape[0] != self.num_tokens:
+            raise ValueError("x must be [num_tokens of the layout, hidden]")
+        H = x.shape[1]
+        if pool.shape[0] < self.capacity_rows or pool.shape[1] != H:
+            raise ValueError(f"pool must be at least [{self.capacity_rows}, {H}]")
+        _require(pool, torch.uint8 if fp8 else torch.bfloat16, "pool", self.device)
+        if fp8:
+            if pool_scales is None or pool_scales.shape[0] < self.capacity_rows or pool_scales.shape[1] != H // 128:
+                raise ValueError(f"pool_scales must be at least [{self.capacity_rows}, {H // 128}]")
+            _require(pool_scales, torch.uint8, "pool_scales", self.device)
+        flags = (EP_DISPATCH_FP8 if fp8 else 0) | (EP_DISPATCH_TILE_READY if tile_ready else 0)
+        return ep_dispatch(self._h, x, pool, pool_scales if fp8 else None, flags, stream)
+
+    def combine(self, epoch: int, expert_out: torch.Tensor, y: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+        _require(expert_out, torch.bfloat16, "expert_out", self.device)
+        H = expert_out.shape[1]
+        if expert_out.shape[0] < self.capacity_rows:
+            raise ValueError(f"expert_out must have at least {self.capacity_rows} rows")
+        if y is None:
+            y = torch.empty(max(self.num_tokens, 0), H, dtype=torch.bfloat16, device=self.device)
+        _require(y, torch.bfloat16, "y", self.device)
+        if y.shape != (self.num_tokens, H):
+            raise ValueError("y must be [num_tokens of the layout, hidden]")
+        ep_combine(self._h, epoch, expert_out, y, stream)
+        return y
+
+    def tile_consume(self, seq: int, pool: torch.Tensor, pool_scales: Optional[torch.Tensor],
+                     hidden: int, out: torch.Tensor, fp8: bool = False, workgroups: int = 32,
+                     spin_limit_us: int = 2_000_000, stream=None) -> None:
+        _require(out, torch.bfloat16, "out", self.device)
+        if out.shape[0] < self.capacity_rows or out.shape[1] != hidden:
+            raise ValueError("out must be at least [capacity_rows, hidden]")
+        flags = EP_DISPATCH_FP8 if fp8 else 0
+        ep_tile_consume(self._h, seq, pool, pool_scales if fp8 else None, hidden, flags, out,
+                        workgroups, spin_limit_us, stream)
+
+    def array(self, name: str, stream=None) -> torch.Tensor:
+        """Device copy of one metadata array (see ARRAYS)."""
+        which, dtype = ARRAYS[name]
+        nbytes = int(_lib.ep_array_bytes(self._h, which))
+        out = torch.empty(nbytes // 4, dtype=dtype, device=self.device)
+        _check(_lib.ep_copy_array(self._h, which, _ptr(out), nbytes, _stream(stream)), "ep_copy_array")
+        return out
+
+    def counts_to_host(self, stream=None) -> Tuple[np.ndarray, int]:
+        counts = np.empty(self.num_experts, np.int32)
+        nt = np.zeros(1, np.int32)
+        _check(_lib.ep_counts_to_host(self._h, counts.ctypes.data_as(ctypes.c_void_p),
+                                      nt.ctypes.data_as(ctypes.c_void_p), _stream(stream)),
+               "ep_counts_to_host")
+        return counts, int(nt[0])
+
+    def sync_status(self, stream=None) -> int:
+        return ep_handle_sync_status(self._h, stream)

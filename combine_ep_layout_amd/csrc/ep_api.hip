@@ -1,0 +1,374 @@
+// C ABI of the dispatch/combine library: handle management, host-side
+// argument checks and kernel launches.  Declarations and the meaning of every
+// argument are in include/ep_layout.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <new>
+
+#include "ep_layout.h"
+#include "ep_internal.h"
+
+struct ep_handle {
+    ep_config cfg;
+    int64_t cap;              // pool capacity rows
+    int32_t max_tiles;
+    int32_t max_slots;        // max_tokens * top_k
+    int32_t ws_blocks;        // workgroups the layout workspace holds
+    int device;
+    int wall_khz;             // device wall-clock rate (kHz)
+    void* block;              // single device allocation holding every array
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* num_tiles;
+    int32_t* tile_expert;
+    int32_t* tile_target;
+    uint32_t* arrival;
+    uint32_t* tile_ready;
+    int32_t* slot_to_row;
+    int32_t* recv_token;
+    float* weights;
+    uint32_t* error;
+    int32_t* ws;
+    uint32_t* done;
+    // host state of the current layout
+    int32_t T;                // tokens of the current layout, -1 before the first
+    uint32_t epoch;
+    uint32_t seq;
+    uint32_t round;           // TILE_READY dispatches since the layout
+};
+
+namespace {
+
+constexpr int32_t kMaxTopK = 32;
+constexpr int32_t kMaxExperts = 1024;
+constexpr int32_t kMaxBlockM = 4096;
+constexpr int32_t kMaxHidden = 1 << 16;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+ep_status check_config(const ep_config* c) {
+    if (!c) return EP_ERR_INVALID_ARGUMENT;
+    if (c->max_tokens < 0 || c->top_k < 1 || c->top_k > kMaxTopK || c->num_experts < 1 ||
+        c->num_experts > kMaxExperts || c->block_m < 1 || c->block_m > kMaxBlockM)
+        return EP_ERR_INVALID_ARGUMENT;
+    const int64_t slots = (int64_t)c->max_tokens * c->top_k;
+    const int64_t cap = slots + (int64_t)c->num_experts * (c->block_m - 1);
+    if (cap > INT32_MAX / 2) return EP_ERR_INVALID_ARGUMENT;
+    return EP_OK;
+}
+
+ep_status hip_status(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* ep_status_string(ep_status s) {
+    switch (s) {
+        case EP_OK: return "ok";
+        case EP_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case EP_ERR_UNSUPPORTED: return "unsupported";
+        case EP_ERR_OUT_OF_MEMORY: return "out of device memory";
+        case EP_ERR_HANDLE_STATE: return "handle has no layout or the epoch does not match";
+        case EP_ERR_BAD_ROUTING: return "expert id outside [-1, num_experts)";
+        case EP_ERR_TIMEOUT: return "consumer wait timed out";
+        case EP_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+ep_status ep_handle_create(const ep_config* cfg, ep_handle** out) {
+    if (!out) return EP_ERR_INVALID_ARGUMENT;
+    *out = nullptr;
+    ep_status st = check_config(cfg);
+    if (st != EP_OK) return st;
+
+    ep_handle* h = new (std::nothrow) ep_handle();
+    if (!h) return EP_ERR_OUT_OF_MEMORY;
+    h->cfg = *cfg;
+    const int32_t K = cfg->top_k, E = cfg->num_experts, BM = cfg->block_m;
+    h->max_slots = cfg->max_tokens * K;
+    h->cap = (int64_t)h->max_slots + (int64_t)E * (BM - 1);
+    h->max_tiles = (int32_t)(h->cap / BM);
+    h->ws_blocks = epk::layout_blocks(h->max_slots);
+    h->T = -1;
+    h->epoch = 0;
+    h->seq = 0;
+    h->round = 0;
+
+    if (hipGetDevice(&h->device) != hipSuccess ||
+        hipDeviceGetAttribute(&h->wall_khz, hipDeviceAttributeWallClockRate, h->device) != hipSuccess) {
+        delete h;
+        return EP_ERR_HIP;
+    }
+    if (h->wall_khz <= 0) h->wall_khz = 100000;
+
+    // one allocation, every array 256-byte aligned
+    struct Part { void** dst; size_t bytes; };
+    const size_t mt = (size_t)h->max_tiles, ms = (size_t)h->max_slots;
+    Part parts[] = {
+        {(void**)&h->counts, sizeof(int32_t) * E},
+        {(void**)&h->offsets, sizeof(int32_t) * (E + 1)},
+        {(void**)&h->num_tiles, sizeof(int32_t)},
+        {(void**)&h->tile_expert, sizeof(int32_t) * mt},
+        {(void**)&h->tile_target, sizeof(int32_t) * mt},
+        {(void**)&h->arrival, sizeof(uint32_t) * mt},
+        {(void**)&h->tile_ready, sizeof(uint32_t) * mt},
+        {(void**)&h->slot_to_row, sizeof(int32_t) * ms},
+        {(void**)&h->recv_token, sizeof(int32_t) * (size_t)h->cap},
+        {(void**)&h->weights, sizeof(float) * ms},
+        {(void**)&h->error, sizeof(uint32_t)},
+        {(void**)&h->ws, sizeof(int32_t) * (size_t)h->ws_blocks * E},
+        {(void**)&h->done, sizeof(uint32_t)},
+    };
+    size_t total = 0;
+    for (const Part& p : parts) total += round_up(p.bytes ? p.bytes : 1, 256);
+    if (hipMalloc(&h->block, total) != hipSuccess) {
+        (void)hipGetLastError();
+        delete h;
+        return EP_ERR_OUT_OF_MEMORY;
+    }
+    size_t off = 0;
+    for (const Part& p : parts) {
+        *p.dst = (char*)h->block + off;
+        off += round_up(p.bytes ? p.bytes : 1, 256);
+    }
+    if (hipMemset(h->block, 0, total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        (void)hipFree(h->block);
+        delete h;
+        return EP_ERR_HIP;
+    }
+    *out = h;
+    return EP_OK;
+}
+
+ep_status ep_handle_destroy(ep_handle* h) {
+    if (!h) return EP_OK;
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != h->device) e = hipSetDevice(h->device);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    hipError_t f = hipFree(h->block);
+    if (cur != h->device) (void)hipSetDevice(cur);
+    delete h;
+    return (e == hipSuccess && f == hipSuccess) ? EP_OK : EP_ERR_HIP;
+}
+
+int64_t ep_pool_capacity_rows(const ep_handle* h) { return h ? h->cap : -1; }
+
+int32_t ep_max_tiles(const ep_handle* h) { return h ? h->max_tiles : -1; }
+
+int32_t ep_num_tokens(const ep_handle* h) { return h ? h->T : -1; }
+
+ep_status ep_layout(ep_handle* h, const int32_t* topk_idx, const float* topk_weights,
+                    int32_t num_tokens, hipStream_t stream, uint32_t* epoch_out) {
+    if (!h || num_tokens < 0 || num_tokens > h->cfg.max_tokens) return EP_ERR_INVALID_ARGUMENT;
+    if (num_tokens > 0 && (!topk_idx || !topk_weights || !aligned4(topk_idx) ||
+                           !aligned4(topk_weights)))
+        return EP_ERR_INVALID_ARGUMENT;
+    epk::LayoutArgs a;
+    a.topk_idx = topk_idx;
+    a.topk_w = topk_weights;
+    a.S = num_tokens * h->cfg.top_k;
+    a.K = h->cfg.top_k;
+    a.E = h->cfg.num_experts;
+    a.BM = h->cfg.block_m;
+    a.cap = (int32_t)h->cap;
+    a.max_tiles = h->max_tiles;
+    a.counts = h->counts;
+    a.offsets = h->offsets;
+    a.num_tiles = h->num_tiles;
+    a.tile_expert = h->tile_expert;
+    a.tile_target = h->tile_target;
+    a.arrival = h->arrival;
+    a.slot_to_row = h->slot_to_row;
+    a.recv_token = h->recv_token;
+    a.weights = h->weights;
+    a.error = h->error;
+    a.ws = h->ws;
+    a.done = h->done;
+    ep_status st = hip_status(epk::launch_layout(a, stream));
+    if (st != EP_OK) return st;
+    h->T = num_tokens;
+    h->epoch += 1;
+    h->round = 0;
+    if (epoch_out) *epoch_out = h->epoch;
+    return EP_OK;
+}
+
+ep_status ep_dispatch(ep_handle* h, const void* x, int32_t hidden, void* pool,
+                      uint8_t* pool_scales, uint32_t flags, hipStream_t stream,
+                      uint32_t* seq_out) {
+    if (!h) return EP_ERR_INVALID_ARGUMENT;
+    if (flags & ~(EP_DISPATCH_FP8 | EP_DISPATCH_TILE_READY)) return EP_ERR_INVALID_ARGUMENT;
+    const bool fp8 = (flags & EP_DISPATCH_FP8) != 0;
+    const bool ready = (flags & EP_DISPATCH_TILE_READY) != 0;
+    if (hidden <= 0 || hidden % 8 != 0) return EP_ERR_INVALID_ARGUMENT;
+    if (hidden > kMaxHidden) return EP_ERR_UNSUPPORTED;
+    if (fp8 && (hidden % 128 != 0 || !pool_scales)) return EP_ERR_INVALID_ARGUMENT;
+    if (!fp8 && pool_scales) return EP_ERR_INVALID_ARGUMENT;
+    if (h->T < 0) return EP_ERR_HANDLE_STATE;
+    if (h->T > 0 && (!x || !pool || !aligned16(x) || !aligned16(pool)))
+        return EP_ERR_INVALID_ARGUMENT;
+    epk::DispatchArgs a;
+    a.x = x;
+    a.T = h->T;
+    a.K = h->cfg.top_k;
+    a.H = hidden;
+    a.BM = h->cfg.block_m;
+    a.E = h->cfg.num_experts;
+    a.slot_to_row = h->slot_to_row;
+    a.tile_expert = h->tile_expert;
+    a.tile_target = h->tile_target;
+    a.pool = pool;
+    a.scales = pool_scales;
+    a.arrival = h->arrival;
+    a.tile_ready = h->tile_ready;
+    a.seq = h->seq + 1;
+    a.round = h->round + (ready ? 1u : 0u);
+    ep_status st = hip_status(epk::launch_dispatch(a, fp8, ready, stream));
+    if (st != EP_OK) return st;
+    h->seq = a.seq;
+    h->round = a.round;
+    if (seq_out) *seq_out = a.seq;
+    return EP_OK;
+}
+
+ep_status ep_combine(const ep_handle* h, uint32_t epoch, const void* expert_out, int32_t hidden,
+                     void* y, hipStream_t stream) {
+    if (!h) return EP_ERR_INVALID_ARGUMENT;
+    if (hidden <= 0 || hidden % 8 != 0) return EP_ERR_INVALID_ARGUMENT;
+    if (hidden > kMaxHidden) return EP_ERR_UNSUPPORTED;
+    if (h->T < 0 || epoch != h->epoch) return EP_ERR_HANDLE_STATE;
+    if (h->T > 0 && (!expert_out || !y || !aligned16(expert_out) || !aligned16(y)))
+        return EP_ERR_INVALID_ARGUMENT;
+    epk::CombineArgs a;
+    a.expert_out = expert_out;
+    a.T = h->T;
+    a.K = h->cfg.top_k;
+    a.H = hidden;
+    a.slot_to_row = h->slot_to_row;
+    a.weights = h->weights;
+    a.y = y;
+    return hip_status(epk::launch_combine(a, stream));
+}
+
+ep_status ep_handle_get_view(const ep_handle* h, ep_handle_view* out) {
+    if (!h || !out) return EP_ERR_INVALID_ARGUMENT;
+    out->expert_counts = h->counts;
+    out->expert_pool_block_offset = h->offsets;
+    out->num_tiles = h->num_tiles;
+    out->tile_expert = h->tile_expert;
+    out->pool_arrival_target = h->tile_target;
+    out->pool_arrival_count = h->arrival;
+    out->tile_ready = h->tile_ready;
+    out->slot_to_pool_row = h->slot_to_row;
+    out->pool_recv_token = h->recv_token;
+    out->topk_weights = h->weights;
+    return EP_OK;
+}
+
+int64_t ep_array_bytes(const ep_handle* h, ep_array which) {
+    if (!h) return -1;
+    const int64_t E = h->cfg.num_experts, mt = h->max_tiles;
+    const int64_t slots = (int64_t)(h->T < 0 ? 0 : h->T) * h->cfg.top_k;
+    switch (which) {
+        case EP_ARRAY_EXPERT_COUNTS: return 4 * E;
+        case EP_ARRAY_BLOCK_OFFSET: return 4 * (E + 1);
+        case EP_ARRAY_NUM_TILES: return 4;
+        case EP_ARRAY_TILE_EXPERT:
+        case EP_ARRAY_ARRIVAL_TARGET:
+        case EP_ARRAY_ARRIVAL_COUNT:
+        case EP_ARRAY_TILE_READY: return 4 * mt;
+        case EP_ARRAY_SLOT_TO_POOL_ROW:
+        case EP_ARRAY_TOPK_WEIGHTS: return 4 * slots;
+        case EP_ARRAY_POOL_RECV_TOKEN: return 4 * h->cap;
+    }
+    return -1;
+}
+
+ep_status ep_copy_array(const ep_handle* h, ep_array which, void* dst, int64_t dst_bytes,
+                        hipStream_t stream) {
+    const int64_t n = ep_array_bytes(h, which);
+    if (n < 0 || dst_bytes < n) return EP_ERR_INVALID_ARGUMENT;
+    if (n == 0) return EP_OK;
+    if (!dst) return EP_ERR_INVALID_ARGUMENT;
+    const void* src = nullptr;
+    switch (which) {
+        case EP_ARRAY_EXPERT_COUNTS: src = h->counts; break;
+        case EP_ARRAY_BLOCK_OFFSET: src = h->offsets; break;
+        case EP_ARRAY_NUM_TILES: src = h->num_tiles; break;
+        case EP_ARRAY_TILE_EXPERT: src = h->tile_expert; break;
+        case EP_ARRAY_ARRIVAL_TARGET: src = h->tile_target; break;
+        case EP_ARRAY_ARRIVAL_COUNT: src = h->arrival; break;
+        case EP_ARRAY_TILE_READY: src = h->tile_ready; break;
+        case EP_ARRAY_SLOT_TO_POOL_ROW: src = h->slot_to_row; break;
+        case EP_ARRAY_POOL_RECV_TOKEN: src = h->recv_token; break;
+        case EP_ARRAY_TOPK_WEIGHTS: src = h->weights; break;
+    }
+    return hip_status(hipMemcpyAsync(dst, src, (size_t)n, hipMemcpyDeviceToDevice, stream));
+}
+
+ep_status ep_counts_to_host(ep_handle* h, int32_t* counts_host, int32_t* num_tiles_host,
+                            hipStream_t stream) {
+    if (!h || !counts_host || !num_tiles_host) return EP_ERR_INVALID_ARGUMENT;
+    if (h->T < 0) return EP_ERR_HANDLE_STATE;
+    if (hipStreamSynchronize(stream) != hipSuccess) return EP_ERR_HIP;
+    if (hipMemcpy(counts_host, h->counts, sizeof(int32_t) * h->cfg.num_experts,
+                  hipMemcpyDeviceToHost) != hipSuccess ||
+        hipMemcpy(num_tiles_host, h->num_tiles, sizeof(int32_t), hipMemcpyDeviceToHost) !=
+            hipSuccess)
+        return EP_ERR_HIP;
+    return EP_OK;
+}
+
+ep_status ep_handle_sync_status(ep_handle* h, hipStream_t stream) {
+    if (!h) return EP_ERR_INVALID_ARGUMENT;
+    if (hipStreamSynchronize(stream) != hipSuccess) return EP_ERR_HIP;
+    uint32_t word = 0;
+    if (hipMemcpy(&word, h->error, sizeof word, hipMemcpyDeviceToHost) != hipSuccess)
+        return EP_ERR_HIP;
+    if (word) {
+        const uint32_t zero = 0;
+        if (hipMemcpy(h->error, &zero, sizeof zero, hipMemcpyHostToDevice) != hipSuccess)
+            return EP_ERR_HIP;
+    }
+    if (word & 1u) return EP_ERR_BAD_ROUTING;
+    if (word & 2u) return EP_ERR_TIMEOUT;
+    return EP_OK;
+}
+
+ep_status ep_tile_consume(const ep_handle* h, uint32_t seq, const void* pool,
+                          const uint8_t* pool_scales, int32_t hidden, uint32_t flags, void* out,
+                          int32_t workgroups, uint32_t spin_limit_us, hipStream_t stream) {
+    if (!h) return EP_ERR_INVALID_ARGUMENT;
+    if (flags & ~(EP_DISPATCH_FP8 | EP_DISPATCH_TILE_READY)) return EP_ERR_INVALID_ARGUMENT;
+    const bool fp8 = (flags & EP_DISPATCH_FP8) != 0;
+    if (hidden <= 0 || hidden % 8 != 0 || (fp8 && (hidden % 128 != 0 || !pool_scales)))
+        return EP_ERR_INVALID_ARGUMENT;
+    if (hidden > kMaxHidden) return EP_ERR_UNSUPPORTED;
+    if (workgroups < 1 || workgroups > 1024) return EP_ERR_INVALID_ARGUMENT;
+    if (h->T < 0) return EP_ERR_HANDLE_STATE;
+    if (!pool || !out || !aligned16(pool) || !aligned16(out)) return EP_ERR_INVALID_ARGUMENT;
+    epk::ConsumeArgs a;
+    a.pool = pool;
+    a.scales = pool_scales;
+    a.H = hidden;
+    a.BM = h->cfg.block_m;
+    a.fp8 = fp8 ? 1 : 0;
+    a.num_tiles = h->num_tiles;
+    a.recv_token = h->recv_token;
+    a.tile_ready = h->tile_ready;
+    a.seq = seq;
+    a.limit_ticks = (uint64_t)spin_limit_us * (uint64_t)h->wall_khz / 1000u;
+    a.out = out;
+    a.error = h->error;
+    return hip_status(epk::launch_consume(a, workgroups, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// Internal interface between the C ABI (ep_api.hip) and the gfx950 kernels
+// (ep_kernels.hip).  Not installed; callers use include/ep_layout.h.
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+namespace epk {
+
+// Slots handled by one workgroup of the multi-workgroup layout path.
+constexpr int kLayoutSlotsPerBlock = 4096;
+// The single-workgroup layout path is used up to this many slots and experts.
+constexpr int kFusedMaxSlots = 16384;
+constexpr int kFusedMaxExperts = 256;
+
+struct LayoutArgs {
+    const int32_t* topk_idx;    // [S]
+    const float* topk_w;        // [S]
+    int32_t S;                  // num_tokens * top_k
+    int32_t K;
+    int32_t E;
+    int32_t BM;
+    int32_t cap;                // pool capacity rows
+    int32_t max_tiles;
+    int32_t* counts;            // [E]
+    int32_t* offsets;           // [E+1]
+    int32_t* num_tiles;         // [1]
+    int32_t* tile_expert;       // [max_tiles]
+    int32_t* tile_target;       // [max_tiles]
+    uint32_t* arrival;          // [max_tiles]
+    int32_t* slot_to_row;       // [S]
+    int32_t* recv_token;        // [cap]
+    float* weights;             // [S]
+    uint32_t* error;            // [1]
+    int32_t* ws;                // [blocks * E] per-workgroup counts, then bases
+    uint32_t* done;             // [1] last-workgroup counter (self-resetting)
+};
+
+struct DispatchArgs {
+    const void* x;
+    int32_t T;
+    int32_t K;
+    int32_t H;
+    int32_t BM;
+    int32_t E;
+    const int32_t* slot_to_row;
+    const int32_t* tile_expert;
+    const int32_t* tile_target;
+    void* pool;
+    uint8_t* scales;
+    // streaming release
+    uint32_t* arrival;
+    uint32_t* tile_ready;
+    uint32_t seq;
+    uint32_t round;             // TILE_READY dispatches since the layout (1, 2, ...)
+};
+
+struct CombineArgs {
+    const void* expert_out;
+    int32_t T;
+    int32_t K;
+    int32_t H;
+    const int32_t* slot_to_row;
+    const float* weights;
+    void* y;
+};
+
+struct ConsumeArgs {
+    const void* pool;
+    const uint8_t* scales;
+    int32_t H;
+    int32_t BM;
+    int32_t fp8;
+    const int32_t* num_tiles;
+    const int32_t* recv_token;
+    const uint32_t* tile_ready;
+    uint32_t seq;
+    uint64_t limit_ticks;
+    void* out;
+    uint32_t* error;
+};
+
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
+hipError_t launch_dispatch(const DispatchArgs& a, bool fp8, bool tile_ready, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+hipError_t launch_consume(const ConsumeArgs& a, int workgroups, hipStream_t stream);
+
+// Workgroups the multi-workgroup layout path needs for S slots.
+inline int layout_blocks(int64_t S) {
+    int64_t nb = (S + kLayoutSlotsPerBlock - 1) / kLayoutSlotsPerBlock;
+    return nb < 1 ? 1 : (int)nb;
+}
+
+}  // namespace epk

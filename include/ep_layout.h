@@ -1,0 +1,218 @@
+/*
+ * ep_layout.h -- C ABI of an MI355X (gfx950) library for one GPU's share of
+ * Mixture-of-Experts expert-parallel dispatch and combine.
+ *
+ * The operations follow the pages this library is built from:
+ *   [SEP]  StreamEP README, "Streaming dispatch in one paragraph": the
+ *          expert-major, BLOCK_M-padded pool, expert_pool_block_offset (in
+ *          tiles), pool_recv_token (-1 on padding rows), pool_arrival_count /
+ *          pool_arrival_target per tile, and tile_ready[tile] release-stamped
+ *          with the dispatch sequence number for a consumer on another stream.
+ *   [ROUND] blog "DeepEP MoE dispatch/combine", section on one DeepEP round:
+ *          dispatch takes x[num_tokens, hidden], topk_idx and topk_weights,
+ *          counts assignments per expert, lays them out, returns tokens grouped
+ *          per local expert plus a handle; combine takes the same handle and
+ *          returns the weighted reduction in original token order.
+ *   [HANDLE] same blog, EPHandle section: the handle carries the layout, the
+ *          source mapping, per-expert counts and the top-k index/weight
+ *          association; it is valid only for the routing that produced it.
+ *   [CONTRACT] same blog, integration data-contract section: a per-execution
+ *          epoch guards against reusing a stale handle.
+ *   [WEIGHTS] same blog, router-weight section: y_t = sum_j p_{t,j} o_{t,j}.
+ *   [FP8]  instagit DeepEP low-latency page, "FP8 and Quantization Support":
+ *          float8_e4m3fn payload with UE8M0 scales.
+ *
+ * Conventions for every call:
+ *   - Pointers marked "device" are device memory on the handle's GPU, 16-byte
+ *     aligned; pointers marked "host" are ordinary host memory.
+ *   - Calls are stream-ordered and return once work is enqueued on `stream`,
+ *     except those marked BLOCKING.  A NULL stream is the device's null stream.
+ *   - Argument errors are detected on the host before anything is enqueued and
+ *     return EP_ERR_INVALID_ARGUMENT / EP_ERR_UNSUPPORTED / EP_ERR_HANDLE_STATE
+ *     with no side effect.  Data-dependent errors seen on the device (expert ids
+ *     outside [-1, num_experts), a consumer wait that timed out) set a sticky
+ *     error word that ep_handle_sync_status() reports and clears.
+ *   - A handle is used from one host thread and one stream at a time.  The
+ *     caller keeps every buffer it passes alive until the stream work that uses
+ *     it has completed.
+ *   - Arrays: x, pool, expert_out and y are row-major; bf16 values are passed
+ *     as their 16-bit patterns.
+ */
+#ifndef EP_LAYOUT_H
+#define EP_LAYOUT_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ep_status {
+    EP_OK = 0,
+    EP_ERR_INVALID_ARGUMENT = 1, /* bad pointer, size or flag                      */
+    EP_ERR_UNSUPPORTED = 2,      /* valid request outside what this build handles  */
+    EP_ERR_OUT_OF_MEMORY = 3,    /* device allocation failed in ep_handle_create   */
+    EP_ERR_HANDLE_STATE = 4,     /* no layout yet, or epoch does not match         */
+    EP_ERR_BAD_ROUTING = 5,      /* device saw expert ids outside [-1, E)          */
+    EP_ERR_TIMEOUT = 6,          /* a bounded consumer wait expired                */
+    EP_ERR_HIP = 7               /* a HIP runtime call failed                      */
+} ep_status;
+
+/* Opaque; owns every metadata array of one layout ([HANDLE]). */
+typedef struct ep_handle ep_handle;
+
+/* Capacities fixed at creation ([ROUND]; the blog's buffer section: the
+ * buffer is sized once from max tokens, hidden size and top-k).
+ *   max_tokens  >= 0   largest num_tokens ep_layout will accept
+ *   top_k       1..32  slots per token
+ *   num_experts 1..1024 experts handled by this GPU (local experts)
+ *   block_m     1..4096 rows per pool tile (BLOCK_M) */
+typedef struct ep_config {
+    int32_t max_tokens;
+    int32_t top_k;
+    int32_t num_experts;
+    int32_t block_m;
+} ep_config;
+
+/* ep_dispatch flags. */
+#define EP_DISPATCH_FP8        (1u << 0) /* e4m3fn payload + UE8M0 scales ([FP8])    */
+#define EP_DISPATCH_TILE_READY (1u << 1) /* per-tile arrival counts release tile_ready ([SEP]) */
+
+/* Allocate a handle and all its device metadata on the current device.
+ * Returns EP_ERR_INVALID_ARGUMENT for out-of-range fields or when the pool
+ * capacity does not fit int32 rows; EP_ERR_OUT_OF_MEMORY when allocation
+ * fails.  *out receives the handle (host pointer, owned by the library). */
+ep_status ep_handle_create(const ep_config* cfg, ep_handle** out);
+
+/* Free the handle (synchronises the device first).  NULL is a no-op. */
+ep_status ep_handle_destroy(ep_handle* h);
+
+/* Worst-case pool rows: max_tokens * top_k + num_experts * (block_m - 1).
+ * Every pool / expert_out buffer must have at least this many rows. */
+int64_t ep_pool_capacity_rows(const ep_handle* h);
+
+/* Tile slots: ep_pool_capacity_rows(h) / block_m (never fewer than needed). */
+int32_t ep_max_tiles(const ep_handle* h);
+
+/* Tokens of the current layout, or -1 when there is none. */
+int32_t ep_num_tokens(const ep_handle* h);
+
+/* Build the expert-major layout of one routing ([SEP], [ROUND]).
+ *   topk_idx      device int32 [num_tokens, top_k]; -1 marks a masked slot.
+ *   topk_weights  device fp32  [num_tokens, top_k]; copied into the handle.
+ *   num_tokens    0..max_tokens.
+ *   epoch_out     host; receives the new epoch that ep_combine must quote.
+ * Device results (read them with ep_handle_get_view / ep_copy_array):
+ *   expert_counts[e]             rows of expert e
+ *   expert_pool_block_offset[e]  first tile of expert e (E+1 entries, last = num_tiles)
+ *   tile_expert[j], pool_arrival_target[j]  expert and real rows of tile j
+ *                                           (-1 and 0 for j >= num_tiles)
+ *   slot_to_pool_row[t*K+k]      pool row of slot (t,k), -1 if masked
+ *   pool_recv_token[r]           source token of pool row r, -1 for padding
+ * Rows of one expert are in ascending slot order t*K+k.  pool_arrival_count is
+ * zeroed for the layout's tiles.  Ids outside [-1, E) are treated as masked and
+ * set EP_ERR_BAD_ROUTING in the error word.  Invalidates earlier epochs. */
+ep_status ep_layout(ep_handle* h, const int32_t* topk_idx, const float* topk_weights,
+                    int32_t num_tokens, hipStream_t stream, uint32_t* epoch_out);
+
+/* Copy activations into the pool of the current layout ([SEP], [ROUND]).
+ *   x            device bf16 [num_tokens, hidden], hidden % 8 == 0.
+ *   pool         device; bf16 [capacity_rows, hidden], or with EP_DISPATCH_FP8
+ *                e4m3fn bytes [capacity_rows, hidden] (hidden % 128 == 0).
+ *   pool_scales  device u8 [capacity_rows, hidden/128] UE8M0 bytes (scale =
+ *                2^(byte-127)) with EP_DISPATCH_FP8, else must be NULL.
+ *   flags        EP_DISPATCH_FP8 | EP_DISPATCH_TILE_READY.
+ *   seq_out      host, may be NULL; receives this dispatch's sequence number
+ *                (1, 2, ... per handle, wraps; compare wrap-safe).
+ * Only real rows are written; padding rows and rows past the layout keep
+ * their contents.  FP8: per token and 128-channel group, e = smallest integer
+ * in [-127,127] with amax <= 448*2^e; codes are x*2^-e rounded to nearest-even
+ * e4m3fn.  With EP_DISPATCH_TILE_READY each tile's arrival count is raised as
+ * its rows land and the dispatch that completes the tile release-stores the
+ * sequence number into tile_ready[tile] (device scope), so a consumer on
+ * another stream may acquire-load it and read the tile's rows. */
+ep_status ep_dispatch(ep_handle* h, const void* x, int32_t hidden, void* pool,
+                      uint8_t* pool_scales, uint32_t flags, hipStream_t stream,
+                      uint32_t* seq_out);
+
+/* Weighted sum back in original token order ([WEIGHTS], [ROUND]).
+ *   epoch       the value ep_layout returned; else EP_ERR_HANDLE_STATE.
+ *   expert_out  device bf16 [capacity_rows, hidden]; only real rows are read.
+ *   y           device bf16 [num_tokens, hidden], fully written.
+ * y[t,c] = bf16_rne( fp32 fma chain over k ascending of w[t,k] * o[row(t,k),c] )
+ * starting from +0 and skipping masked slots; a token with no slot gets +0. */
+ep_status ep_combine(const ep_handle* h, uint32_t epoch, const void* expert_out,
+                     int32_t hidden, void* y, hipStream_t stream);
+
+/* Device pointers into the handle's metadata; valid until the next ep_layout
+ * or ep_handle_destroy.  Lengths: counts E, offsets E+1, tile arrays
+ * max_tiles, pool_recv_token capacity_rows, slot arrays num_tokens*top_k. */
+typedef struct ep_handle_view {
+    const int32_t* expert_counts;
+    const int32_t* expert_pool_block_offset;
+    const int32_t* num_tiles;
+    const int32_t* tile_expert;
+    const int32_t* pool_arrival_target;
+    const uint32_t* pool_arrival_count;
+    const uint32_t* tile_ready;
+    const int32_t* slot_to_pool_row;
+    const int32_t* pool_recv_token;
+    const float* topk_weights;
+} ep_handle_view;
+
+ep_status ep_handle_get_view(const ep_handle* h, ep_handle_view* out);
+
+/* Which metadata array ep_copy_array copies. */
+typedef enum ep_array {
+    EP_ARRAY_EXPERT_COUNTS = 0,
+    EP_ARRAY_BLOCK_OFFSET = 1,
+    EP_ARRAY_NUM_TILES = 2,
+    EP_ARRAY_TILE_EXPERT = 3,
+    EP_ARRAY_ARRIVAL_TARGET = 4,
+    EP_ARRAY_ARRIVAL_COUNT = 5,
+    EP_ARRAY_TILE_READY = 6,
+    EP_ARRAY_SLOT_TO_POOL_ROW = 7,
+    EP_ARRAY_POOL_RECV_TOKEN = 8,
+    EP_ARRAY_TOPK_WEIGHTS = 9
+} ep_array;
+
+/* Byte size of a metadata array for the current layout. */
+int64_t ep_array_bytes(const ep_handle* h, ep_array which);
+
+/* Stream-ordered device-to-device copy of one metadata array into dst
+ * (device, dst_bytes >= ep_array_bytes). */
+ep_status ep_copy_array(const ep_handle* h, ep_array which, void* dst, int64_t dst_bytes,
+                        hipStream_t stream);
+
+/* BLOCKING: copy expert_counts (E ints) and num_tiles into host memory
+ * ("CPU counts" in DeepEP PR #769's wording). */
+ep_status ep_counts_to_host(ep_handle* h, int32_t* counts_host, int32_t* num_tiles_host,
+                            hipStream_t stream);
+
+/* BLOCKING: wait for `stream`, read and clear the device error word.
+ * Returns EP_ERR_BAD_ROUTING, EP_ERR_TIMEOUT or EP_OK. */
+ep_status ep_handle_sync_status(ep_handle* h, hipStream_t stream);
+
+/* Stand-in for the consumer of the streaming release ([SEP]: a consumer
+ * kernel spins on an acquire-load of tile_ready[tile] >= dispatch_seq from a
+ * different stream).  A bounded grid of `workgroups` walks tiles in order,
+ * waits until tile_ready[tile] has reached `seq` (wrap-safe), then writes
+ * every real row of the tile to `out` (device bf16 [capacity_rows, hidden]):
+ * a copy of a bf16 pool, or with EP_DISPATCH_FP8 the dequantised value
+ * bf16(e4m3(q) * 2^(scale-127)).  A wait longer than spin_limit_us gives up
+ * on that tile and sets EP_ERR_TIMEOUT in the error word, so it always ends.
+ * The caller orders it after ep_layout (e.g. with an event). */
+ep_status ep_tile_consume(const ep_handle* h, uint32_t seq, const void* pool,
+                          const uint8_t* pool_scales, int32_t hidden, uint32_t flags,
+                          void* out, int32_t workgroups, uint32_t spin_limit_us,
+                          hipStream_t stream);
+
+/* Static description of a status code. */
+const char* ep_status_string(ep_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_LAYOUT_H */

@@ -1,0 +1,73 @@
+"""The C-ABI library loads and exports every function include/ep_layout.h
+declares; host-side argument checks reject bad configurations before any HIP
+call (CPU only: nothing here launches GPU work)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ep_layout.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s+(ep_[a-z0-9_]+)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("ep_handle_create", "ep_handle_destroy", "ep_layout", "ep_dispatch",
+                     "ep_combine", "ep_handle_get_view", "ep_counts_to_host",
+                     "ep_handle_sync_status", "ep_status_string"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    import combine_ep_layout_amd as ep
+    lib = ep.library()
+    names = _declared_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(ep.EXPORTS) == names
+
+
+def test_status_strings():
+    import combine_ep_layout_amd as ep
+    lib = ep.library()
+    for s in range(8):
+        assert lib.ep_status_string(s)
+    assert lib.ep_status_string(0) == b"ok"
+
+
+@pytest.mark.parametrize("cfg", [
+    (-1, 2, 8, 16),        # negative max_tokens
+    (16, 0, 8, 16),        # top_k 0
+    (16, 33, 8, 16),       # top_k above 32
+    (16, 2, 0, 16),        # no experts
+    (16, 2, 1025, 16),     # too many experts
+    (16, 2, 8, 0),         # block_m 0
+    (16, 2, 8, 4097),      # block_m above 4096
+    (1 << 30, 8, 8, 16),   # capacity beyond int32 rows
+])
+def test_create_rejects_bad_config_without_gpu(cfg):
+    import combine_ep_layout_amd as ep
+    with pytest.raises(ep.EpError) as ei:
+        ep.ep_handle_create(*cfg)
+    assert ei.value.status == ep.EP_ERR_INVALID_ARGUMENT
+
+
+def test_null_handle_calls_are_rejected():
+    import combine_ep_layout_amd as ep
+    lib = ep.library()
+    assert lib.ep_layout(None, None, None, 0, None, None) == ep.EP_ERR_INVALID_ARGUMENT
+    assert lib.ep_dispatch(None, None, 128, None, None, 0, None, None) == ep.EP_ERR_INVALID_ARGUMENT
+    assert lib.ep_combine(None, 1, None, 128, None, None) == ep.EP_ERR_INVALID_ARGUMENT
+    assert lib.ep_handle_destroy(None) == ep.EP_OK
+    assert lib.ep_pool_capacity_rows(None) == -1 and lib.ep_max_tiles(None) == -1
+    assert lib.ep_handle_create(None, None) == ep.EP_ERR_INVALID_ARGUMENT

@@ -1,0 +1,125 @@
+"""GPU parity of dispatch (bf16 copy and FP8 e4m3fn + UE8M0) against the
+oracle: pool and scale bytes bit-exact, padding rows never written."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import CONFIGS, Config, generate
+from gpu_helpers import (say, inputs, oracle_layout, new_handle, device_routing, to_dev_bf16,
+                         bits_of, full_path_check, dev, POISON_BF16, POISON_U8)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name,tokens", [("tiny", -1), ("share", -1), ("prefill", 700),
+                                         ("decode", 64)])
+def test_bf16_full_compare(name, tokens):
+    say(f"[dispatch bf16] {name} tokens={tokens}")
+    cfg, d = inputs(name, tokens)
+    cfg = cfg.replace(fp8=False)
+    full_path_check(cfg, d)
+
+
+@pytest.mark.parametrize("name,tokens", [("decode", -1), ("stream", 2048)])
+def test_fp8_full_compare(name, tokens):
+    say(f"[dispatch fp8] {name} tokens={tokens}")
+    cfg, d = inputs(name, tokens)
+    full_path_check(cfg, d, fp8=True)
+
+
+def _sampled_dispatch(name, fp8):
+    cfg, d = inputs(name)
+    L = oracle_layout(name)
+    h = new_handle(cfg)
+    h.layout(*device_routing(d))
+    x = to_dev_bf16(d["x"])
+    cap, H = h.capacity_rows, cfg.hidden
+    recv = L["pool_recv_token"]
+    real = np.flatnonzero(recv >= 0)
+    pad = np.flatnonzero(recv < 0)
+    rng = np.random.default_rng(11)
+    sample = np.sort(rng.choice(real, size=min(2048, len(real)), replace=False))
+    if fp8:
+        pool = torch.full((cap, H), POISON_U8, dtype=torch.uint8, device=dev())
+        scales = torch.full((cap, H // 128), POISON_U8, dtype=torch.uint8, device=dev())
+        h.dispatch(x, pool, scales, fp8=True)
+        got_q = pool[torch.from_numpy(sample).to(dev())].cpu().numpy()
+        got_s = scales[torch.from_numpy(sample).to(dev())].cpu().numpy()
+        for i, r in enumerate(sample):
+            q, s = oracle.quantize_row(d["x"][recv[r]])
+            assert np.array_equal(got_q[i], q), r
+            assert np.array_equal(got_s[i], s), r
+        padt = torch.from_numpy(pad).to(dev())
+        assert bool((pool[padt] == POISON_U8).all()) and bool((scales[padt] == POISON_U8).all())
+    else:
+        pool = torch.full((cap, H), POISON_BF16 - 0x10000, dtype=torch.int16,
+                          device=dev()).view(torch.bfloat16)
+        h.dispatch(x, pool)
+        got = bits_of(pool[torch.from_numpy(sample).to(dev())])
+        assert np.array_equal(got, d["x"][recv[sample]])
+        padt = torch.from_numpy(pad).to(dev())
+        assert bool((pool.view(torch.int16)[padt] == POISON_BF16 - 0x10000).all())
+        # every real row, compared on the device against the row of x it came from
+        realt = torch.from_numpy(real).to(dev())
+        srct = torch.from_numpy(recv[real].astype(np.int64)).to(dev())
+        assert torch.equal(pool.view(torch.int16)[realt], x.view(torch.int16)[srct])
+    h.close()
+
+
+def test_bf16_prefill_full_size_sampled():
+    say("[dispatch bf16] prefill full size")
+    _sampled_dispatch("prefill", fp8=False)
+
+
+def test_fp8_stream_full_size_sampled():
+    say("[dispatch fp8] stream full size")
+    _sampled_dispatch("stream", fp8=True)
+
+
+def _one_row_per_token(x_bits: np.ndarray) -> Config:
+    T, H = x_bits.shape
+    return Config("rows", T, H, 1, 1, 1, 1)
+
+
+def test_fp8_every_bf16_pattern():
+    """All 65536 bf16 bit patterns (NaN and infinities included) through the
+    quantiser, in natural order, shuffled, and next to amax values that pin
+    the scale exponent at the ends of its range."""
+    say("[dispatch fp8] all bf16 patterns")
+    H = 4096
+    allp = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    rng = np.random.default_rng(7)
+    rows = [allp.reshape(-1, H), rng.permutation(allp).reshape(-1, H)]
+    # groups of 127 probes + one amax setter 448 * 2^e for e in a spread of exponents
+    finite = allp[(allp & 0x7F80) != 0x7F80]
+    for e in (-127, -126, -120, -9, -1, 0, 1, 60, 119):
+        setter = np.array([0x43E0 + (e << 7)], np.uint16)   # bf16 pattern of 448 * 2^e
+        mag = finite & 0x7FFF
+        probes = finite[(mag <= setter[0]) & (mag > 0)]
+        probes = rng.permutation(probes)[: 127 * 64]
+        probes = np.resize(probes, 127 * 64).reshape(64, 127)
+        groups = np.concatenate([np.repeat(setter[None, :], 64, 0), probes], axis=1)
+        rows.append(groups.reshape(-1, H))
+    x_bits = np.ascontiguousarray(np.concatenate(rows, axis=0))
+    T = x_bits.shape[0]
+    cfg = _one_row_per_token(x_bits)
+    d = {"x": x_bits, "topk_idx": np.zeros((T, 1), np.int32),
+         "topk_weights": np.ones((T, 1), np.float32)}
+    full_path_check(cfg, d, fp8=True)
+
+
+def test_fp8_nonfinite_inputs():
+    say("[dispatch fp8] NaN / inf rows")
+    H = 256
+    rng = np.random.default_rng(2)
+    x = rng.integers(0x3000, 0x4000, size=(6, H), dtype=np.uint16)
+    x[0, 3] = 0x7FC0          # NaN: ignored by amax, code 0x7F
+    x[1, 5] = 0xFFC1          # negative NaN
+    x[2, 7] = 0x7F80          # +inf: scale 254, saturates to 0x7E
+    x[3, 130] = 0xFF80        # -inf in the second group
+    x[4, :128] = 0x0000       # all-zero group: scale byte 0
+    x[5, :] = 0x8000          # negative zeros
+    cfg = _one_row_per_token(x)
+    d = {"x": x, "topk_idx": np.zeros((6, 1), np.int32), "topk_weights": np.ones((6, 1), np.float32)}
+    full_path_check(cfg, d, fp8=True)

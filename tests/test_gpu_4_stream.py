@@ -1,0 +1,104 @@
+"""Streaming release: per-tile arrival counts and tile_ready stamps acquired by
+a consumer on another stream (StreamEP README, "Streaming dispatch in one
+paragraph": dispatch release-stores dispatch_seq into tile_ready[tile] once a
+tile's pool_arrival_count reaches pool_arrival_target; a consumer on a
+different stream acquire-loads tile_ready[tile] >= dispatch_seq and reads the
+tile's real rows).
+
+Every consumer wait is bounded (spin_limit_us); a wait that expires shows up
+as EP_ERR_TIMEOUT, never as a hang."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import (say, inputs, oracle_layout, new_handle, device_routing, to_dev_bf16,
+                         bits_of, dev)
+
+pytestmark = pytest.mark.gpu
+
+SPIN_US = 3_000_000
+
+
+def _expected_consumer_rows(d, L, fp8, rows):
+    recv = L["pool_recv_token"]
+    if fp8:
+        out = []
+        for r in rows:
+            q, s = oracle.quantize_row(d["x"][recv[r]])
+            out.append(oracle.dequant_rows(q[None, :], s[None, :])[0])
+        return np.stack(out)
+    return d["x"][recv[rows]]
+
+
+def _check_end_state(h, L, seq, rounds):
+    nt = L["num_tiles"]
+    cnt = h.array("pool_arrival_count").cpu().numpy().view(np.uint32)[:nt]
+    tgt = L["pool_arrival_target"][:nt].astype(np.uint32)
+    assert np.array_equal(cnt, rounds * tgt)
+    ready = h.array("tile_ready").cpu().numpy().view(np.uint32)
+    assert (ready[:nt] == seq).all()
+
+
+def _run(name, tokens, fp8, consumer_first, replays=1, sample=None):
+    import combine_ep_layout_amd as ep
+    cfg, d = inputs(name, tokens)
+    L = oracle.layout(d["topk_idx"], cfg.num_experts, cfg.block_m)
+    h = new_handle(cfg)
+    H = cfg.hidden
+    sa = torch.cuda.current_stream()
+    sb = torch.cuda.Stream()                       # default priority
+    h.layout(*device_routing(d))
+    x = to_dev_bf16(d["x"])
+    pool, scales = h.new_pool(H, fp8=fp8)
+    for rep in range(1, replays + 1):
+        out = torch.zeros(h.capacity_rows, H, dtype=torch.bfloat16, device=dev())
+        ev = torch.cuda.Event()
+        ev.record(sa)                              # layout (and out's zero fill) done
+        sb.wait_event(ev)
+        seq_next = rep                             # one dispatch per replay, from seq 1
+        if consumer_first:
+            h.tile_consume(seq_next, pool, scales, H, out, fp8=fp8, workgroups=16,
+                           spin_limit_us=SPIN_US, stream=sb)
+            seq = h.dispatch(x, pool, scales, fp8=fp8, tile_ready=True, stream=sa)
+        else:
+            seq = h.dispatch(x, pool, scales, fp8=fp8, tile_ready=True, stream=sa)
+            h.tile_consume(seq_next, pool, scales, H, out, fp8=fp8, workgroups=16,
+                           spin_limit_us=SPIN_US, stream=sb)
+        assert seq == seq_next
+        sb.synchronize()
+        sa.synchronize()
+        assert h.sync_status() == ep.EP_OK, "a consumer wait timed out"
+        _check_end_state(h, L, seq, rep)
+        real = np.flatnonzero(L["pool_recv_token"] >= 0)
+        if sample is not None:
+            real = np.sort(np.random.default_rng(rep).choice(real, size=sample, replace=False))
+        got = bits_of(out[torch.from_numpy(real).to(dev())])
+        assert np.array_equal(got, _expected_consumer_rows(d, L, fp8, real))
+    h.close()
+
+
+@pytest.mark.parametrize("fp8", [True, False])
+def test_consumer_first_small(fp8):
+    say(f"[stream] consumer first, stream tokens=3000 fp8={fp8}")
+    _run("stream", 3000, fp8, consumer_first=True)
+
+
+def test_consumer_after_dispatch():
+    say("[stream] consumer after dispatch")
+    _run("stream", 3000, True, consumer_first=False)
+
+
+def test_replays_without_reset():
+    say("[stream] three dispatches on one layout, tile_ready never reset")
+    _run("stream", 2500, True, consumer_first=True, replays=3)
+
+
+def test_stream_full_size():
+    say("[stream] full size, consumer first, sampled rows")
+    _run("stream", -1, True, consumer_first=True, sample=1024)
+
+
+def test_bf16_prefill_shape_streaming():
+    say("[stream] bf16 prefill shape tokens=1500")
+    _run("prefill", 1500, False, consumer_first=True)
