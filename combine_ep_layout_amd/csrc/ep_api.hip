@@ -229,6 +229,9 @@ ep_status ep_dispatch(ep_handle* h, const void* x, int32_t hidden, void* pool,
     a.scales = pool_scales;
     a.arrival = h->arrival;
     a.tile_ready = h->tile_ready;
+    a.max_tiles = h->max_tiles;
+    a.tile_bits = 1;
+    while ((1 << a.tile_bits) <= h->max_tiles) ++a.tile_bits;
     a.seq = h->seq + 1;
     a.round = h->round + (ready ? 1u : 0u);
     ep_status st = hip_status(epk::launch_dispatch(a, fp8, ready, stream));

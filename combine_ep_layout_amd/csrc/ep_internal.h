@@ -7,11 +7,13 @@
 
 namespace epk {
 
-// Slots handled by one workgroup of the multi-workgroup layout path.
-constexpr int kLayoutSlotsPerBlock = 4096;
-// The single-workgroup layout path is used up to this many slots and experts.
-constexpr int kFusedMaxSlots = 16384;
-constexpr int kFusedMaxExperts = 256;
+#ifndef EP_LAYOUT_SLOTS_PER_LANE
+#define EP_LAYOUT_SLOTS_PER_LANE 2
+#endif
+
+// Slots ranked by one layout workgroup (1024 threads x EP_LAYOUT_SLOTS_PER_LANE).
+// Up to this many slots the whole layout runs in a single workgroup and launch.
+constexpr int kLayoutSlotsPerBlock = 1024 * EP_LAYOUT_SLOTS_PER_LANE;
 
 struct LayoutArgs {
     const int32_t* topk_idx;    // [S]
@@ -53,6 +55,8 @@ struct DispatchArgs {
     uint32_t* tile_ready;
     uint32_t seq;
     uint32_t round;             // TILE_READY dispatches since the layout (1, 2, ...)
+    int32_t max_tiles;
+    int32_t tile_bits;          // bits of a tile id, max_tiles included
 };
 
 struct CombineArgs {

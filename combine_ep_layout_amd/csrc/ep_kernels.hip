@@ -7,44 +7,57 @@
 // every (token, k) slot inside its expert.  Stable ranks come from wave64
 // match-any masks built out of one ballot per key bit, so a slot's row
 // depends only on how many earlier slots share its expert, never on timing.
+// The layout is latency-bound (a few hundred KB), so every workgroup issues
+// all of its loads before it waits on any of them, and the cross-workgroup
+// scan is recomputed redundantly by each workgroup instead of being
+// serialised through one of them.
 //
-// Dispatch is token-major: one wave reads a token's row of x once and writes
-// it, as 16-byte vectors, to each of the token's pool rows (bf16), or
-// quantises it once to e4m3fn with UE8M0 scales per 128 channels and writes
-// the codes (FP8).  With the streaming release, each workgroup makes its rows
-// visible at device scope and then raises the arrival count of every tile it
-// wrote; the workgroup that completes a tile release-stores the sequence
-// number into tile_ready[tile].
+// Dispatch is token-major: a wave reads one segment of a token's row of x
+// once and writes it, as 16-byte vectors, to each of the token's pool rows
+// (bf16), or quantises it once to e4m3fn with UE8M0 scales per 128 channels
+// and writes the codes (FP8).  With the streaming release, each workgroup
+// covers whole tokens, makes its rows visible at device scope and then raises
+// the arrival count of every tile it wrote; the workgroup that completes a
+// tile release-stores the sequence number into tile_ready[tile].
 //
-// Combine is token-major too: one wave gathers the token's k expert rows,
-// accumulates w * o in fp32 with one fused multiply-add per slot in slot
-// order, and rounds once to bf16 (blog, router-weight section).
+// Combine is token-major too: a wave gathers one segment of the token's k
+// expert rows, accumulates w * o in fp32 with one fused multiply-add per slot
+// in slot order, and rounds once to bf16 (blog, router-weight section).
 //
 // Nothing here is a dense contraction, so no matrix-core instructions are
-// used; the dispatch and combine kernels are HBM-bound streaming kernels.
+// used; dispatch and combine are HBM-bound streaming kernels.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <limits.h>
 
 #include "ep_internal.h"
 
-#ifndef EP_DISPATCH_TPW
-#define EP_DISPATCH_TPW 2      // tokens per wave in dispatch
-#endif
-#ifndef EP_COMBINE_TPW
-#define EP_COMBINE_TPW 2       // tokens per wave in combine
-#endif
 #ifndef EP_DISPATCH_UNROLL
-#define EP_DISPATCH_UNROLL 4   // 16-byte chunks in flight per lane (bf16 dispatch)
-#endif
-#ifndef EP_COMBINE_UNROLL
-#define EP_COMBINE_UNROLL 2    // 16-byte chunks per lane per slot in combine
+#define EP_DISPATCH_UNROLL 7   // 16-byte chunks per lane per bf16 dispatch work item
 #endif
 #ifndef EP_FP8_UNROLL
-#define EP_FP8_UNROLL 2        // 16-channel units per lane in FP8 dispatch
+#define EP_FP8_UNROLL 2        // 16-channel units per lane per FP8 dispatch work item
 #endif
-#ifndef EP_NT_STORES
-#define EP_NT_STORES 1         // non-temporal stores for pool rows and y
+#ifndef EP_COMBINE_UNROLL
+#define EP_COMBINE_UNROLL 2    // 16-byte chunks per lane per combine work item
+#endif
+#ifndef EP_ITEMS_PER_WAVE
+#define EP_ITEMS_PER_WAVE 1    // work items per wave outside streaming mode
+#endif
+#ifndef EP_STREAM_TOKENS
+#define EP_STREAM_TOKENS 64    // whole tokens per 1024-thread workgroup in streaming mode
+#endif
+#ifndef EP_DISPATCH_NT
+#define EP_DISPATCH_NT 1       // non-temporal stores for pool rows
+#endif
+#ifndef EP_COMBINE_NT
+#define EP_COMBINE_NT 1        // non-temporal stores for y
+#endif
+#ifndef EP_COMBINE_NT_LOADS
+#define EP_COMBINE_NT_LOADS 1  // non-temporal loads of expert rows
+#endif
+#ifndef EP_STREAM_STORE
+#define EP_STREAM_STORE 2      // streaming pool stores: 0 plain, 1 device-coherent 64-bit, 2 buffer sc1
 #endif
 
 namespace epk {
@@ -53,6 +66,10 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
+constexpr int kLayoutThreads = 1024;                          // 16 waves
+constexpr int kLayoutWaves = kLayoutThreads / kWave;
+constexpr int kSlotsPerLane = kLayoutSlotsPerBlock / kLayoutThreads;   // 8
+constexpr int kWaveSlots = kLayoutSlotsPerBlock / kLayoutWaves;       // 512
 
 __device__ __forceinline__ int uniform_i(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -72,67 +89,24 @@ __device__ __forceinline__ uint64_t match_any(int key, int nbits) {
     return m;
 }
 
-template <typename T>
-__device__ __forceinline__ void store_stream(T* p, const T& v) {
-#if EP_NT_STORES
-    __builtin_nontemporal_store(v, p);
-#else
-    *p = v;
-#endif
+template <bool NT, typename T>
+__device__ __forceinline__ void store_v(T* p, const T& v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+template <bool NT, typename T>
+__device__ __forceinline__ T load_v(const T* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
 }
 
 // ---------------------------------------------------------------- layout ---
 
-// Key of a slot: its expert, or E for masked / invalid / past-the-end slots.
-__device__ __forceinline__ int slot_key(const int32_t* idx, int s, int hi, int E, bool& bad) {
-    if (s >= hi) return E;
-    const int e = idx[s];
-    if (e >= 0 && e < E) return e;
-    if (e != -1) bad = true;
-    return E;
-}
+__device__ __forceinline__ int key_bits(int E) { return 32 - __clz(E); }
 
-// Count slots [lo, hi) per expert into hist (LDS), one wave.
-__device__ void count_walk(const int32_t* idx, int lo, int hi, int E, int nbits, int* hist,
-                           bool& bad) {
-    const int lane = threadIdx.x & (kWave - 1);
-    for (int base = lo; base < hi; base += kWave) {
-        const int key = slot_key(idx, base + lane, hi, E, bad);
-        const uint64_t m = match_any(key, nbits);
-        const int leader = __ffsll((unsigned long long)m) - 1;
-        if (key < E && lane == leader) atomicAdd(&hist[key], __popcll(m));
-    }
-}
-
-// Give slots [lo, hi) their pool rows, one wave; run[e] is this wave's next
-// free row of expert e (LDS).
-__device__ void rank_walk(const int32_t* idx, int lo, int hi, int K, int E, int nbits, int* run,
-                          int32_t* slot_to_row, int32_t* recv_token) {
-    const int lane = threadIdx.x & (kWave - 1);
-    bool bad = false;
-    for (int base = lo; base < hi; base += kWave) {
-        const int s = base + lane;
-        const int key = slot_key(idx, s, hi, E, bad);
-        const uint64_t m = match_any(key, nbits);
-        const int leader = __ffsll((unsigned long long)m) - 1;
-        const int rank = __popcll(m & lanemask_lt());
-        int first = 0;
-        if (key < E && lane == leader) first = atomicAdd(&run[key], __popcll(m));
-        first = __shfl(first, leader, kWave);
-        if (s < hi) {
-            if (key < E) {
-                const int row = first + rank;
-                slot_to_row[s] = row;
-                recv_token[row] = s / K;
-            } else {
-                slot_to_row[s] = -1;
-            }
-        }
-    }
-}
-
-// Exclusive scan over the workgroup (NT threads); returns this thread's
-// prefix and the total.  Every thread must call it.
+// Exclusive scan over a workgroup of NT threads; returns this thread's prefix
+// and the total.  Every thread must call it.
 template <int NT>
 __device__ int block_exclusive_scan(int v, int* s_tmp, int& total) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -157,228 +131,249 @@ __device__ int block_exclusive_scan(int v, int* s_tmp, int& total) {
     return before + x - v;
 }
 
-// Tile metadata from LDS offsets (E+1, tiles) and counts (E).
-__device__ void fill_tiles(int tid, int nthreads, const LayoutArgs& a, const int* s_off,
-                           const int* s_cnt) {
-    const int nt = s_off[a.E];
-    for (int j = tid; j < a.max_tiles; j += nthreads) {
-        if (j < nt) {
-            int lo = 0, hi = a.E - 1;           // last expert whose first tile is <= j
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (s_off[mid] <= j) lo = mid; else hi = mid - 1;
+// Expert owning tile j: the last e whose first tile is <= j (s_off has E+1
+// non-decreasing entries; requires j < s_off[E]).
+__device__ __forceinline__ int expert_of_tile(const int* s_off, int E, int j) {
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_off[mid] <= j) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Keys of this wave's 512 slots, slot = base + i*64 + lane: the expert id, or
+// E for masked, invalid and past-the-end slots.  All loads are issued first.
+__device__ __forceinline__ void load_keys(const int32_t* idx, int base, int S, int E,
+                                          int (&key)[kSlotsPerLane], bool& bad) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int raw[kSlotsPerLane];
+#pragma unroll
+    for (int i = 0; i < kSlotsPerLane; ++i) {
+        const int s = base + i * kWave + lane;
+        raw[i] = (s < S) ? idx[s] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kSlotsPerLane; ++i) {
+        const bool ok = raw[i] >= 0 && raw[i] < E;
+        bad |= !ok && raw[i] != -1;
+        key[i] = ok ? raw[i] : E;
+    }
+}
+
+// Launch 1 of the multi-workgroup layout: per-workgroup expert histograms.
+__global__ __launch_bounds__(kLayoutThreads) void k_layout_count(LayoutArgs a) {
+    extern __shared__ int smem[];
+    int* hist = smem;                                   // [E]
+    const int E = a.E, tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int w = uniform_i(tid / kWave);
+    const int base = (int)blockIdx.x * kLayoutSlotsPerBlock + w * kWaveSlots;
+    int key[kSlotsPerLane];
+    bool bad = false;
+    load_keys(a.topk_idx, base, a.S, E, key, bad);
+    for (int i = tid; i < E; i += kLayoutThreads) hist[i] = 0;
+    __syncthreads();
+    const int nbits = key_bits(E);
+#pragma unroll
+    for (int i = 0; i < kSlotsPerLane; ++i) {
+        if (base + i * kWave >= a.S) break;             // uniform per wave
+        const uint64_t m = match_any(key[i], nbits);
+        if (key[i] < E && lane == __ffsll((unsigned long long)m) - 1)
+            atomicAdd(&hist[key[i]], __popcll(m));
+    }
+    if (__ballot(bad) && lane == 0) atomicOr(a.error, 1u);
+    __syncthreads();
+    for (int e = tid; e < E; e += kLayoutThreads)
+        a.ws[(int64_t)blockIdx.x * E + e] = hist[e];
+}
+
+// Layout ranks.  FUSED: the whole layout in this one workgroup (nb == 1, no
+// histogram launch).  Otherwise launch 2 of the multi-workgroup layout: the
+// workgroup sums the histograms of the workgroups before it and of all of
+// them, scans tiles over experts, and ranks its own 8192 slots.  Every
+// workgroup writes its share of the tile metadata and of the padding rows.
+template <bool FUSED>
+__global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, int nb, int lg_tpe) {
+    extern __shared__ int smem[];
+    const int E = a.E, BM = a.BM;
+    int* s_base = smem;                                 // [E]   first row of e for this workgroup
+    int* s_cnt = s_base + E;                            // [E]   rows of expert e
+    int* s_off = s_cnt + E;                             // [E+1] first tile of expert e
+    int* s_tmp = s_off + E + 1;                         // [16]
+    int* s_tt = s_tmp + kLayoutWaves;                   // [1024] real rows of a chunk of tiles
+    uint16_t* wc = (uint16_t*)(s_tt + kLayoutThreads);  // [16][E] per-wave counts, then next ranks
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int w = uniform_i(tid / kWave);
+    const int b = (int)blockIdx.x;
+    const int nbits = key_bits(E);
+    const int base = b * kLayoutSlotsPerBlock + w * kWaveSlots;
+
+    int key[kSlotsPerLane];
+    bool bad = false;
+    load_keys(a.topk_idx, base, a.S, E, key, bad);
+    for (int i = tid; i < kLayoutWaves * E; i += kLayoutThreads) wc[i] = 0;
+
+    int total = 0;
+    if constexpr (!FUSED) {
+        // rows of expert e in earlier workgroups (pre) and in all (tot); 2^lg_tpe threads per expert
+        const int tpe = 1 << lg_tpe;
+        const int e = tid >> lg_tpe, part = tid & (tpe - 1);
+        int pre = 0, tot = 0;
+        if (e < E) {
+            for (int bb = part; bb < nb; bb += tpe) {
+                const int c = a.ws[(int64_t)bb * E + e];
+                tot += c;
+                pre += (bb < b) ? c : 0;
             }
-            const int left = s_cnt[lo] - (j - s_off[lo]) * a.BM;
-            a.tile_expert[j] = lo;
-            a.tile_target[j] = left < a.BM ? left : a.BM;
+        }
+        for (int d = 1; d < tpe; d <<= 1) {
+            pre += __shfl_xor(pre, d, kWave);
+            tot += __shfl_xor(tot, d, kWave);
+        }
+        const bool owner = e < E && part == 0;
+        const int tiles = owner ? (tot + BM - 1) / BM : 0;
+        const int off = block_exclusive_scan<kLayoutThreads>(tiles, s_tmp, total);
+        if (owner) {
+            s_cnt[e] = tot;
+            s_off[e] = off;
+            s_base[e] = off * BM + pre;
+            if (b == 0) {
+                a.counts[e] = tot;
+                a.offsets[e] = off;
+            }
+        }
+    }
+    __syncthreads();
+
+    // per-wave counts; each iteration's match mask is kept for the ranking pass
+    uint64_t m[kSlotsPerLane];
+#pragma unroll
+    for (int i = 0; i < kSlotsPerLane; ++i) {
+        m[i] = 0;
+        if (base + i * kWave >= a.S) continue;          // uniform per wave
+        m[i] = match_any(key[i], nbits);
+        if (key[i] < E && lane == __ffsll((unsigned long long)m[i]) - 1)
+            wc[w * E + key[i]] += (uint16_t)__popcll(m[i]);
+    }
+    __syncthreads();
+
+    if constexpr (FUSED) {
+        if (__ballot(bad) && lane == 0) atomicOr(a.error, 1u);
+        int tot = 0;
+        if (tid < E)
+            for (int v = 0; v < kLayoutWaves; ++v) tot += wc[v * E + tid];
+        const int tiles = (tid < E) ? (tot + BM - 1) / BM : 0;
+        const int off = block_exclusive_scan<kLayoutThreads>(tiles, s_tmp, total);
+        if (tid < E) {
+            s_cnt[tid] = tot;
+            s_off[tid] = off;
+            s_base[tid] = off * BM;
+            a.counts[tid] = tot;
+            a.offsets[tid] = off;
+        }
+    }
+    // exclusive prefix of the per-wave counts over waves
+    for (int e = tid; e < E; e += kLayoutThreads) {
+        int run = 0;
+        for (int v = 0; v < kLayoutWaves; ++v) {
+            const int c = wc[v * E + e];
+            wc[v * E + e] = (uint16_t)run;
+            run += c;
+        }
+    }
+    if (tid == 0) {
+        s_off[E] = total;
+        if (b == 0) {
+            a.offsets[E] = total;
+            *a.num_tiles = total;
+        }
+    }
+    __syncthreads();
+
+    // pool row of every slot of this wave
+#pragma unroll
+    for (int i = 0; i < kSlotsPerLane; ++i) {
+        if (base + i * kWave >= a.S) continue;          // uniform per wave
+        const int s = base + i * kWave + lane;
+        const int k = key[i];
+        const int leader = __ffsll((unsigned long long)m[i]) - 1;
+        int cur = 0;
+        if (k < E && lane == leader) {
+            cur = wc[w * E + k];
+            wc[w * E + k] = (uint16_t)(cur + __popcll(m[i]));
+        }
+        cur = __shfl(cur, leader, kWave);
+        if (s < a.S) {
+            if (k < E) {
+                const int row = s_base[k] + cur + __popcll(m[i] & lanemask_lt());
+                a.slot_to_row[s] = row;
+                a.recv_token[row] = s / a.K;
+            } else {
+                a.slot_to_row[s] = -1;
+            }
+        }
+    }
+
+    // this workgroup's share of the tile metadata
+    const int tpb = (a.max_tiles + nb - 1) / nb;
+    const int j1 = min(a.max_tiles, (b + 1) * tpb);
+    for (int j = b * tpb + tid; j < j1; j += kLayoutThreads) {
+        if (j < total) {
+            const int e = expert_of_tile(s_off, E, j);
+            const int left = s_cnt[e] - (j - s_off[e]) * BM;
+            a.tile_expert[j] = e;
+            a.tile_target[j] = left < BM ? left : BM;
             a.arrival[j] = 0u;
         } else {
             a.tile_expert[j] = -1;
             a.tile_target[j] = 0;
         }
     }
-}
-
-__device__ __forceinline__ int key_bits(int E) { return 32 - __clz(E); }
-
-// Whole layout in one workgroup of 1024 threads (small S, E <= 256).
-__global__ __launch_bounds__(1024) void k_layout_fused(LayoutArgs a) {
-    extern __shared__ int smem[];
-    const int E = a.E;
-    int* hist = smem;                 // [16][E]: counts, then per-wave next rows
-    int* s_cnt = hist + 16 * E;       // [E]
-    int* s_off = s_cnt + E;           // [E+1]
-    int* s_tmp = s_off + E + 1;       // [16]
-    const int tid = threadIdx.x;
-    const int w = uniform_i(tid / kWave);
-    const int nbits = key_bits(E);
-    for (int i = tid; i < 16 * E; i += 1024) hist[i] = 0;
-    __syncthreads();
-
-    int sub = (a.S + 15) / 16;
-    sub = (sub + kWave - 1) / kWave * kWave;
-    const int lo = min(a.S, w * sub), hi = min(a.S, lo + sub);
-    bool bad = false;
-    count_walk(a.topk_idx, lo, hi, E, nbits, hist + w * E, bad);
-    if (__ballot(bad) && (tid & (kWave - 1)) == 0) atomicOr(a.error, 1u);
-    __syncthreads();
-
-    int n = 0;
-    if (tid < E)
-        for (int v = 0; v < 16; ++v) n += hist[v * E + tid];
-    const int tiles = (tid < E) ? (n + a.BM - 1) / a.BM : 0;
-    int total;
-    const int off = block_exclusive_scan<1024>(tiles, s_tmp, total);
-    if (tid < E) {
-        s_cnt[tid] = n;
-        s_off[tid] = off;
-        a.counts[tid] = n;
-        a.offsets[tid] = off;
-        int next = off * a.BM;
-        for (int v = 0; v < 16; ++v) {
-            const int c = hist[v * E + tid];
-            hist[v * E + tid] = next;
-            next += c;
-        }
-    }
-    if (tid == 0) {
-        s_off[E] = total;
-        a.offsets[E] = total;
-        *a.num_tiles = total;
-    }
-    __syncthreads();
-
-    fill_tiles(tid, 1024, a, s_off, s_cnt);
-    rank_walk(a.topk_idx, lo, hi, a.K, E, nbits, hist + w * E, a.slot_to_row, a.recv_token);
-    for (int s = tid; s < a.S; s += 1024) a.weights[s] = a.topk_w[s];
-    // rows that receive no slot: padding inside tiles and everything past them
-    for (int r = tid; r < a.cap; r += 1024) {
-        const int j = r / a.BM;
-        bool real = false;
-        if (j < total) {
-            int l = 0, h = E - 1;
-            while (l < h) {
-                const int mid = (l + h + 1) >> 1;
-                if (s_off[mid] <= j) l = mid; else h = mid - 1;
+    // ... of the rows that receive no slot (padding, and everything past the
+    // tiles), with the real-row count of each tile looked up once per tile
+    const int rpb = (a.cap + nb - 1) / nb;
+    const int r0 = min(a.cap, b * rpb), r1 = min(a.cap, (b + 1) * rpb);
+    const int jt0 = r0 / BM, jt1 = (r1 + BM - 1) / BM;
+    for (int jc = jt0; jc < jt1; jc += kLayoutThreads) {
+        const int jn = min(jt1, jc + kLayoutThreads);
+        __syncthreads();
+        if (jc + tid < jn) {
+            const int j = jc + tid;
+            int real = 0;
+            if (j < total) {
+                const int e = expert_of_tile(s_off, E, j);
+                const int left = s_cnt[e] - (j - s_off[e]) * BM;
+                real = left < BM ? left : BM;
             }
-            real = (r - s_off[l] * a.BM) < s_cnt[l];
+            s_tt[tid] = real;
         }
-        if (!real) a.recv_token[r] = -1;
-    }
-}
-
-// Multi-workgroup path, launch 1: per-workgroup histograms; the last
-// workgroup to finish scans them (per expert over workgroups, then over
-// experts) and writes counts, offsets and tile metadata.
-__global__ __launch_bounds__(256) void k_layout_count(LayoutArgs a, int nb) {
-    extern __shared__ int smem[];
-    const int E = a.E;
-    int* hist = smem;                 // [E]
-    int* s_cnt = hist + E;            // [E]
-    int* s_off = s_cnt + E;           // [E+1]
-    int* s_tmp = s_off + E + 1;       // [4]
-    __shared__ int s_last;
-    const int tid = threadIdx.x;
-    const int w = uniform_i(tid / kWave);
-    const int nbits = key_bits(E);
-    for (int i = tid; i < E; i += 256) hist[i] = 0;
-    __syncthreads();
-
-    const int sub = kLayoutSlotsPerBlock / 4;
-    const int lo = min(a.S, (int)blockIdx.x * kLayoutSlotsPerBlock + w * sub);
-    const int hi = min(a.S, lo + sub);
-    bool bad = false;
-    count_walk(a.topk_idx, lo, hi, E, nbits, hist, bad);
-    if (__ballot(bad) && (tid & (kWave - 1)) == 0) atomicOr(a.error, 1u);
-    __syncthreads();
-    for (int e = tid; e < E; e += 256) a.ws[(int64_t)blockIdx.x * E + e] = hist[e];
-
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(a.done, 1u) == (unsigned)(nb - 1));
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-
-    // per expert: exclusive prefix over workgroups (in place) and total
-    int carry = 0;
-    for (int e0 = 0; e0 < E; e0 += 256) {
-        const int e = e0 + tid;
-        int n = 0;
-        if (e < E) {
-            int b = 0;
-            for (; b + 8 <= nb; b += 8) {
-                int c[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) c[i] = a.ws[(int64_t)(b + i) * E + e];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    a.ws[(int64_t)(b + i) * E + e] = n;
-                    n += c[i];
-                }
-            }
-            for (; b < nb; ++b) {
-                const int c = a.ws[(int64_t)b * E + e];
-                a.ws[(int64_t)b * E + e] = n;
-                n += c;
-            }
-        }
-        const int tiles = (e < E) ? (n + a.BM - 1) / a.BM : 0;
-        int total;
-        const int off = carry + block_exclusive_scan<256>(tiles, s_tmp, total);
-        carry += total;
-        if (e < E) {
-            s_cnt[e] = n;
-            s_off[e] = off;
-            a.counts[e] = n;
-            a.offsets[e] = off;
+        __syncthreads();
+        const int ra = max(r0, jc * BM), rb = min(r1, jn * BM);
+        for (int r = ra + tid; r < rb; r += kLayoutThreads) {
+            const int j = r / BM;
+            if (r - j * BM >= s_tt[j - jc]) a.recv_token[r] = -1;
         }
     }
-    if (tid == 0) {
-        s_off[E] = carry;
-        a.offsets[E] = carry;
-        *a.num_tiles = carry;
-    }
-    __syncthreads();
-    fill_tiles(tid, 256, a, s_off, s_cnt);
-    if (tid == 0) *a.done = 0u;
-}
-
-// Multi-workgroup path, launch 2: re-count per wave, turn the scanned
-// workgroup bases into per-wave next rows, and rank every slot.
-__global__ __launch_bounds__(256) void k_layout_rank(LayoutArgs a) {
-    extern __shared__ int smem[];
-    const int E = a.E;
-    int* run = smem;                  // [4][E]
-    const int tid = threadIdx.x;
-    const int w = uniform_i(tid / kWave);
-    const int nbits = key_bits(E);
-    for (int i = tid; i < 4 * E; i += 256) run[i] = 0;
-    __syncthreads();
-
-    const int sub = kLayoutSlotsPerBlock / 4;
-    const int blo = (int)blockIdx.x * kLayoutSlotsPerBlock;
-    const int lo = min(a.S, blo + w * sub);
-    const int hi = min(a.S, lo + sub);
-    bool bad = false;
-    count_walk(a.topk_idx, lo, hi, E, nbits, run + w * E, bad);
-    __syncthreads();
-    for (int e = tid; e < E; e += 256) {
-        int next = a.ws[(int64_t)blockIdx.x * E + e] + a.offsets[e] * a.BM;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int c = run[v * E + e];
-            run[v * E + e] = next;
-            next += c;
-        }
-    }
-    __syncthreads();
-    rank_walk(a.topk_idx, lo, hi, a.K, E, nbits, run + w * E, a.slot_to_row, a.recv_token);
-    const int bhi = min(a.S, blo + kLayoutSlotsPerBlock);
-    for (int s = blo + tid; s < bhi; s += 256) a.weights[s] = a.topk_w[s];
-
-    const int nt = *a.num_tiles;
-    for (int r = (int)blockIdx.x * 256 + tid; r < a.cap; r += (int)gridDim.x * 256) {
-        const int j = r / a.BM;
-        const bool real = j < nt && (r - j * a.BM) < a.tile_target[j];
-        if (!real) a.recv_token[r] = -1;
-    }
+    // ... and of the weights
+    const int s1 = min(a.S, (b + 1) * kLayoutSlotsPerBlock);
+    for (int s = b * kLayoutSlotsPerBlock + tid; s < s1; s += kLayoutThreads)
+        a.weights[s] = a.topk_w[s];
 }
 
 // ------------------------------------------------------------- dispatch ---
 
-// After a workgroup's rows are stored: publish them at device scope, then
-// raise the arrival count of each tile written.  Rows of one expert written
-// by a contiguous token range are contiguous, so one add per (expert, tile).
-__device__ void release_tiles(const DispatchArgs& a, int t0, int t1, int* s_lo, int* s_hi) {
-    __threadfence();
-    __syncthreads();
+// Streaming release of the rows a workgroup has just stored for its tokens
+// [t0, t1).  Every wave waits until its own stores have reached the cache,
+// the workgroup meets at a barrier, and one wave then publishes them all at
+// device scope with a single release fence and makes the arrival adds: rows
+// of one expert written for a contiguous token range are contiguous, so it
+// adds once per (expert, tile) touched.  The add that brings a tile to its
+// target acquires the other workgroups' releases and release-stores the
+// sequence number into tile_ready[tile]; a consumer that acquire-loads
+// tile_ready then sees every row of the tile.
+__device__ void release_block(const DispatchArgs& a, int t0, int t1, int* s_lo, int* s_hi) {
+    __builtin_amdgcn_s_waitcnt(0);
     const int tid = threadIdx.x;
-    for (int e = tid; e < a.E; e += blockDim.x) {
-        s_lo[e] = INT_MAX;
-        s_hi[e] = -1;
-    }
-    __syncthreads();
     const int s0 = t0 * a.K, s1 = t1 * a.K;
     for (int s = s0 + tid; s < s1; s += blockDim.x) {
         const int r = a.slot_to_row[s];
@@ -389,7 +384,9 @@ __device__ void release_tiles(const DispatchArgs& a, int t0, int t1, int* s_lo, 
         }
     }
     __syncthreads();
-    for (int e = tid; e < a.E; e += blockDim.x) {
+    if (tid >= kWave) return;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    for (int e = tid; e < a.E; e += kWave) {
         const int hi = s_hi[e];
         if (hi < 0) continue;
         const int lo = s_lo[e];
@@ -397,12 +394,40 @@ __device__ void release_tiles(const DispatchArgs& a, int t0, int t1, int* s_lo, 
             const int first = max(lo, j * a.BM);
             const int last = min(hi, j * a.BM + a.BM - 1);
             const uint32_t n = (uint32_t)(last - first + 1);
-            const uint32_t old = __hip_atomic_fetch_add(&a.arrival[j], n, __ATOMIC_ACQ_REL,
+            const uint32_t old = __hip_atomic_fetch_add(&a.arrival[j], n, __ATOMIC_RELAXED,
                                                          __HIP_MEMORY_SCOPE_AGENT);
-            if (old + n == a.round * (uint32_t)a.tile_target[j])
+            if (old + n == a.round * (uint32_t)a.tile_target[j]) {
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
                 __hip_atomic_store(&a.tile_ready[j], a.seq, __ATOMIC_RELEASE,
                                    __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
+    }
+}
+
+// Clears the LDS per-expert row ranges of a streaming workgroup.
+__device__ __forceinline__ void clear_ranges(int E, int* s_lo, int* s_hi) {
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        s_lo[e] = INT_MAX;
+        s_hi[e] = -1;
+    }
+}
+
+// Pool store of chunk c of a row.  Streaming stores may be device-coherent so
+// that the release has no dirty cache lines of this workgroup to write back.
+template <bool STREAM>
+__device__ __forceinline__ void store_pool(u32x4* row, int row_bytes, int c, const u32x4& v) {
+    if constexpr (STREAM && EP_STREAM_STORE == 1) {
+        uint64_t* q = (uint64_t*)(row + c);
+        __hip_atomic_store(q, (uint64_t)v[0] | ((uint64_t)v[1] << 32), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(q + 1, (uint64_t)v[2] | ((uint64_t)v[3] << 32), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    } else if constexpr (STREAM && EP_STREAM_STORE == 2) {
+        __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(row, (short)0, row_bytes, 0x00020000);
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, c * 16, 0, 16);
+    } else {
+        store_v<EP_DISPATCH_NT>(row + c, v);
     }
 }
 
@@ -417,42 +442,50 @@ __device__ __forceinline__ bool load_rows(const int32_t* s2r, int t, int K, int 
     return any;
 }
 
+// Work items are (token, segment) pairs, item = t * nseg + seg, handed out in
+// order: workgroup b owns items [b * ipb, (b+1) * ipb) and its waves take them
+// round-robin.  In streaming mode ipb is a whole number of tokens.
 template <int KT, bool STREAM>
-__global__ __launch_bounds__(256) void k_dispatch_bf16(DispatchArgs a) {
+__global__ __launch_bounds__(1024) void k_dispatch_bf16(DispatchArgs a, int nseg, int ipb) {
     extern __shared__ int smem[];
     constexpr int U = EP_DISPATCH_UNROLL;
     const int lane = threadIdx.x & (kWave - 1);
     const int w = uniform_i(threadIdx.x / kWave);
-    const int tpb = 4 * EP_DISPATCH_TPW;
-    const int t0 = (int)blockIdx.x * tpb;
-    const int t1 = min(a.T, t0 + tpb);
     const int n16 = a.H / 8;
+    const int i0 = (int)blockIdx.x * ipb;
+    const int i1 = min(a.T * nseg, i0 + ipb);
     const u32x4* x = (const u32x4*)a.x;
     u32x4* pool = (u32x4*)a.pool;
-    for (int t = t0 + w; t < t1; t += 4) {
+    const int nw = (int)blockDim.x / kWave;
+    if constexpr (STREAM) {
+        clear_ranges(a.E, smem, smem + a.E);
+        __syncthreads();
+    }
+    for (int it = i0 + w; it < i1; it += nw) {
+        const int t = it / nseg;
+        const int seg = it - t * nseg;
         int rows[KT];
         if (!load_rows<KT>(a.slot_to_row, t, a.K, rows)) continue;
+        const int c0 = seg * (kWave * U) + lane;
         const u32x4* src = x + (int64_t)t * n16;
-        for (int c0 = lane; c0 < n16; c0 += kWave * U) {
-            u32x4 v[U];
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + u * kWave;
+            if (c < n16) v[u] = src[c];
+        }
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+            if (rows[k] < 0) continue;
+            u32x4* dst = pool + (int64_t)rows[k] * n16;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int c = c0 + u * kWave;
-                if (c < n16) v[u] = src[c];
-            }
-#pragma unroll
-            for (int k = 0; k < KT; ++k) {
-                if (rows[k] < 0) continue;
-                u32x4* dst = pool + (int64_t)rows[k] * n16;
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int c = c0 + u * kWave;
-                    if (c < n16) store_stream(dst + c, v[u]);
-                }
+                if (c < n16) store_pool<STREAM>(dst, a.H * 2, c, v[u]);
             }
         }
     }
-    if constexpr (STREAM) release_tiles(a, t0, t1, smem, smem + a.E);
+    if constexpr (STREAM) release_block(a, i0 / nseg, i1 / nseg, smem, smem + a.E);
 }
 
 // --- FP8 e4m3fn with UE8M0 scales, from bf16 bit patterns, integer only ---
@@ -513,72 +546,102 @@ __device__ __forceinline__ uint32_t mag_for_max(uint32_t b) {
 }
 
 template <int KT, bool STREAM>
-__global__ __launch_bounds__(256) void k_dispatch_fp8(DispatchArgs a) {
+__global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg, int ipb) {
     extern __shared__ int smem[];
     constexpr int U = EP_FP8_UNROLL;
     const int lane = threadIdx.x & (kWave - 1);
     const int w = uniform_i(threadIdx.x / kWave);
-    const int tpb = 4 * EP_DISPATCH_TPW;
-    const int t0 = (int)blockIdx.x * tpb;
-    const int t1 = min(a.T, t0 + tpb);
     const int nunit = a.H / 16;          // 16 channels (32 bytes in, 16 bytes out) per unit
     const int ngrp = a.H / 128;
+    const bool pack8 = (ngrp & 7) == 0 && ((uintptr_t)a.scales & 7) == 0;
+    const int i0 = (int)blockIdx.x * ipb;
+    const int i1 = min(a.T * nseg, i0 + ipb);
     const u32x4* x = (const u32x4*)a.x;
     u32x4* pool = (u32x4*)a.pool;
-    for (int t = t0 + w; t < t1; t += 4) {
+    const int nw = (int)blockDim.x / kWave;
+    if constexpr (STREAM) {
+        clear_ranges(a.E, smem, smem + a.E);
+        __syncthreads();
+    }
+    for (int it = i0 + w; it < i1; it += nw) {
+        const int t = it / nseg;
+        const int seg = it - t * nseg;
         int rows[KT];
         if (!load_rows<KT>(a.slot_to_row, t, a.K, rows)) continue;
+        const int u0 = seg * (kWave * U) + lane;
         const u32x4* src = x + (int64_t)t * (a.H / 8);
-        for (int u0 = lane; u0 - lane < nunit; u0 += kWave * U) {
-            u32x4 lo[U], hi[U];
+        u32x4 lo[U], hi[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int c = u0 + u * kWave;
-                if (c < nunit) {
-                    lo[u] = src[2 * c];
-                    hi[u] = src[2 * c + 1];
-                } else {
-                    lo[u] = u32x4{0, 0, 0, 0};
-                    hi[u] = u32x4{0, 0, 0, 0};
+        for (int u = 0; u < U; ++u) {
+            const int c = u0 + u * kWave;
+            if (c < nunit) {
+                lo[u] = src[2 * c];
+                hi[u] = src[2 * c + 1];
+            } else {
+                lo[u] = u32x4{0, 0, 0, 0};
+                hi[u] = u32x4{0, 0, 0, 0};
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = u0 + u * kWave;
+            if (c - lane >= nunit) break;            // whole wave past the row
+            // 8 lanes hold one 128-channel group (groups never straddle lanes 8g..8g+7)
+            uint32_t amax = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                amax = max(amax, max(mag_for_max(lo[u][i]), mag_for_max(lo[u][i] >> 16)));
+                amax = max(amax, max(mag_for_max(hi[u][i]), mag_for_max(hi[u][i] >> 16)));
+            }
+            amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, kWave));
+            amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2, kWave));
+            amax = max(amax, (uint32_t)__shfl_xor((int)amax, 4, kWave));
+            const int e = ue8m0_exp(amax);
+            u32x4 q;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const uint32_t w0 = lo[u][2 * i], w1 = lo[u][2 * i + 1];
+                q[i] = e4m3_code(w0 & 0xFFFFu, e) | (e4m3_code(w0 >> 16, e) << 8) |
+                       (e4m3_code(w1 & 0xFFFFu, e) << 16) | (e4m3_code(w1 >> 16, e) << 24);
+                const uint32_t h0 = hi[u][2 * i], h1 = hi[u][2 * i + 1];
+                q[2 + i] = e4m3_code(h0 & 0xFFFFu, e) | (e4m3_code(h0 >> 16, e) << 8) |
+                           (e4m3_code(h1 & 0xFFFFu, e) << 16) | (e4m3_code(h1 >> 16, e) << 24);
+            }
+            if (c < nunit) {
+#pragma unroll
+                for (int k = 0; k < KT; ++k) {
+                    if (rows[k] < 0) continue;
+                    store_pool<STREAM>(pool + (int64_t)rows[k] * nunit, a.H, c, q);
                 }
             }
+            // scale bytes: the 8 groups of a full 64-lane step go out as one
+            // 64-bit store per row (device-coherent when streaming)
+            const uint32_t sbyte = (uint32_t)(e + 127);
+            if (pack8 && c - lane + kWave <= nunit) {
+                uint64_t word = 0;
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int c = u0 + u * kWave;
-                if (c - lane >= nunit) break;            // whole wave past the row
-                uint32_t amax = 0;
+                for (int g = 0; g < 8; ++g)
+                    word |= (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)sbyte, 8 * g) << (8 * g);
+                const int g0 = (c - lane) >> 3;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    amax = max(amax, max(mag_for_max(lo[u][i]), mag_for_max(lo[u][i] >> 16)));
-                    amax = max(amax, max(mag_for_max(hi[u][i]), mag_for_max(hi[u][i] >> 16)));
+                for (int k = 0; k < KT; ++k) {
+                    if (rows[k] < 0 || lane != k) continue;
+                    uint64_t* dst = (uint64_t*)(a.scales + (int64_t)rows[k] * ngrp + g0);
+                    if constexpr (STREAM)
+                        __hip_atomic_store(dst, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    else
+                        *dst = word;
                 }
-                amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, kWave));
-                amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2, kWave));
-                amax = max(amax, (uint32_t)__shfl_xor((int)amax, 4, kWave));
-                const int e = ue8m0_exp(amax);
-                u32x4 q;
+            } else if (c < nunit && (lane & 7) == 0) {
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const uint32_t w0 = lo[u][2 * i], w1 = lo[u][2 * i + 1];
-                    q[i] = e4m3_code(w0 & 0xFFFFu, e) | (e4m3_code(w0 >> 16, e) << 8) |
-                           (e4m3_code(w1 & 0xFFFFu, e) << 16) | (e4m3_code(w1 >> 16, e) << 24);
-                    const uint32_t h0 = hi[u][2 * i], h1 = hi[u][2 * i + 1];
-                    q[2 + i] = e4m3_code(h0 & 0xFFFFu, e) | (e4m3_code(h0 >> 16, e) << 8) |
-                               (e4m3_code(h1 & 0xFFFFu, e) << 16) | (e4m3_code(h1 >> 16, e) << 24);
-                }
-                if (c < nunit) {
-#pragma unroll
-                    for (int k = 0; k < KT; ++k) {
-                        if (rows[k] < 0) continue;
-                        store_stream(pool + (int64_t)rows[k] * nunit + c, q);
-                        if ((lane & 7) == 0)
-                            a.scales[(int64_t)rows[k] * ngrp + (c >> 3)] = (uint8_t)(e + 127);
-                    }
+                for (int k = 0; k < KT; ++k) {
+                    if (rows[k] < 0) continue;
+                    a.scales[(int64_t)rows[k] * ngrp + (c >> 3)] = (uint8_t)sbyte;
                 }
             }
         }
     }
-    if constexpr (STREAM) release_tiles(a, t0, t1, smem, smem + a.E);
+    if constexpr (STREAM) release_block(a, i0 / nseg, i1 / nseg, smem, smem + a.E);
 }
 
 // -------------------------------------------------------------- combine ---
@@ -590,17 +653,18 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 }
 
 template <int KT>
-__global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
+__global__ __launch_bounds__(256) void k_combine(CombineArgs a, int nseg, int ipb) {
     constexpr int U = EP_COMBINE_UNROLL;
     const int lane = threadIdx.x & (kWave - 1);
     const int w = uniform_i(threadIdx.x / kWave);
-    const int tpb = 4 * EP_COMBINE_TPW;
-    const int t0 = (int)blockIdx.x * tpb;
-    const int t1 = min(a.T, t0 + tpb);
     const int n16 = a.H / 8;
+    const int i0 = (int)blockIdx.x * ipb;
+    const int i1 = min(a.T * nseg, i0 + ipb);
     const u32x4* eo = (const u32x4*)a.expert_out;
     u32x4* y = (u32x4*)a.y;
-    for (int t = t0 + w; t < t1; t += 4) {
+    for (int it = i0 + w; it < i1; it += 4) {
+        const int t = it / nseg;
+        const int seg = it - t * nseg;
         int rows[KT];
         float wt[KT];
 #pragma unroll
@@ -608,42 +672,41 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
             rows[k] = (k < a.K) ? a.slot_to_row[t * a.K + k] : -1;
             wt[k] = (k < a.K) ? a.weights[t * a.K + k] : 0.0f;
         }
+        const int c0 = seg * (kWave * U) + lane;
+        u32x4 v[KT][U];
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+            if (rows[k] < 0) continue;
+            const u32x4* src = eo + (int64_t)rows[k] * n16;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + u * kWave;
+                if (c < n16) v[k][u] = load_v<EP_COMBINE_NT_LOADS>(src + c);
+            }
+        }
         u32x4* dst = y + (int64_t)t * n16;
-        for (int c0 = lane; c0 < n16; c0 += kWave * U) {
-            u32x4 v[KT][U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float acc[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
 #pragma unroll
             for (int k = 0; k < KT; ++k) {
                 if (rows[k] < 0) continue;
-                const u32x4* src = eo + (int64_t)rows[k] * n16;
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int c = c0 + u * kWave;
-                    if (c < n16) v[k][u] = src[c];
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t p = v[k][u][i];
+                    acc[2 * i] = __builtin_fmaf(wt[k], __uint_as_float(p << 16), acc[2 * i]);
+                    acc[2 * i + 1] =
+                        __builtin_fmaf(wt[k], __uint_as_float(p & 0xFFFF0000u), acc[2 * i + 1]);
                 }
             }
+            u32x4 o;
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float acc[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-#pragma unroll
-                for (int k = 0; k < KT; ++k) {
-                    if (rows[k] < 0) continue;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const uint32_t p = v[k][u][i];
-                        acc[2 * i] = __builtin_fmaf(wt[k], __uint_as_float(p << 16), acc[2 * i]);
-                        acc[2 * i + 1] =
-                            __builtin_fmaf(wt[k], __uint_as_float(p & 0xFFFF0000u), acc[2 * i + 1]);
-                    }
-                }
-                u32x4 o;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    o[i] = f32_to_bf16_rne(acc[2 * i]) | (f32_to_bf16_rne(acc[2 * i + 1]) << 16);
-                const int c = c0 + u * kWave;
-                if (c < n16) store_stream(dst + c, o);
-            }
+            for (int i = 0; i < 4; ++i)
+                o[i] = f32_to_bf16_rne(acc[2 * i]) | (f32_to_bf16_rne(acc[2 * i + 1]) << 16);
+            const int c = c0 + u * kWave;
+            if (c < n16) store_v<EP_COMBINE_NT>(dst + c, o);
         }
     }
 }
@@ -685,41 +748,39 @@ __global__ __launch_bounds__(256) void k_tile_consume(ConsumeArgs a) {
         __syncthreads();
         if (!s_go) return;                    // timed out: give up on the remaining tiles too
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        {
-            for (int r = j * a.BM + w; r < (j + 1) * a.BM; r += 4) {
-                if (a.recv_token[r] < 0) continue;
-                if (a.fp8) {
-                    const int nunit = a.H / 16;
-                    const u32x4* src = (const u32x4*)a.pool + (int64_t)r * nunit;
-                    u32x4* dst = (u32x4*)a.out + (int64_t)r * (a.H / 8);
-                    for (int c = lane; c < nunit; c += kWave) {
-                        const int e = (int)a.scales[(int64_t)r * (a.H / 128) + (c >> 3)] - 127;
-                        const u32x4 q = src[c];
-                        u32x4 o0, o1;
+        for (int r = j * a.BM + w; r < (j + 1) * a.BM; r += 4) {
+            if (a.recv_token[r] < 0) continue;
+            if (a.fp8) {
+                const int nunit = a.H / 16;
+                const u32x4* src = (const u32x4*)a.pool + (int64_t)r * nunit;
+                u32x4* dst = (u32x4*)a.out + (int64_t)r * (a.H / 8);
+                for (int c = lane; c < nunit; c += kWave) {
+                    const int e = (int)a.scales[(int64_t)r * (a.H / 128) + (c >> 3)] - 127;
+                    const u32x4 q = src[c];
+                    u32x4 o0, o1;
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const uint32_t word = q[i];
-                            const uint32_t b0 = e4m3_to_bf16(word & 0xFFu, e);
-                            const uint32_t b1 = e4m3_to_bf16((word >> 8) & 0xFFu, e);
-                            const uint32_t b2 = e4m3_to_bf16((word >> 16) & 0xFFu, e);
-                            const uint32_t b3 = e4m3_to_bf16(word >> 24, e);
-                            if (i < 2) {
-                                o0[2 * i] = b0 | (b1 << 16);
-                                o0[2 * i + 1] = b2 | (b3 << 16);
-                            } else {
-                                o1[2 * (i - 2)] = b0 | (b1 << 16);
-                                o1[2 * (i - 2) + 1] = b2 | (b3 << 16);
-                            }
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t word = q[i];
+                        const uint32_t b0 = e4m3_to_bf16(word & 0xFFu, e);
+                        const uint32_t b1 = e4m3_to_bf16((word >> 8) & 0xFFu, e);
+                        const uint32_t b2 = e4m3_to_bf16((word >> 16) & 0xFFu, e);
+                        const uint32_t b3 = e4m3_to_bf16(word >> 24, e);
+                        if (i < 2) {
+                            o0[2 * i] = b0 | (b1 << 16);
+                            o0[2 * i + 1] = b2 | (b3 << 16);
+                        } else {
+                            o1[2 * (i - 2)] = b0 | (b1 << 16);
+                            o1[2 * (i - 2) + 1] = b2 | (b3 << 16);
                         }
-                        dst[2 * c] = o0;
-                        dst[2 * c + 1] = o1;
                     }
-                } else {
-                    const int n16 = a.H / 8;
-                    const u32x4* src = (const u32x4*)a.pool + (int64_t)r * n16;
-                    u32x4* dst = (u32x4*)a.out + (int64_t)r * n16;
-                    for (int c = lane; c < n16; c += kWave) dst[c] = src[c];
+                    dst[2 * c] = o0;
+                    dst[2 * c + 1] = o1;
                 }
+            } else {
+                const int n16 = a.H / 8;
+                const u32x4* src = (const u32x4*)a.pool + (int64_t)r * n16;
+                u32x4* dst = (u32x4*)a.out + (int64_t)r * n16;
+                for (int c = lane; c < n16; c += kWave) dst[c] = src[c];
             }
         }
         __syncthreads();
@@ -728,48 +789,68 @@ __global__ __launch_bounds__(256) void k_tile_consume(ConsumeArgs a) {
 
 // ------------------------------------------------------------- launchers ---
 
+// Items per workgroup: 4 waves x EP_ITEMS_PER_WAVE, or whole tokens when streaming.
+inline int items_per_block(int nseg, bool stream) {
+    return stream ? EP_STREAM_TOKENS * nseg : 4 * EP_ITEMS_PER_WAVE;
+}
+
 template <int KT>
 hipError_t dispatch_kt(const DispatchArgs& a, bool fp8, bool stream, hipStream_t st) {
-    const int tpb = 4 * EP_DISPATCH_TPW;
-    const int grid = (a.T + tpb - 1) / tpb;
+    const int per_seg = fp8 ? kWave * EP_FP8_UNROLL * 16 : kWave * EP_DISPATCH_UNROLL * 8;  // channels
+    const int nseg = (a.H + per_seg - 1) / per_seg;
+    const int ipb = items_per_block(nseg, stream);
+    const int64_t items = (int64_t)a.T * nseg;
+    const int grid = (int)((items + ipb - 1) / ipb);
     const size_t lds = stream ? 2 * sizeof(int) * (size_t)a.E : 0;
+    const dim3 block(stream ? 1024 : 256);
     if (fp8) {
         if (stream)
-            hipLaunchKernelGGL((k_dispatch_fp8<KT, true>), dim3(grid), dim3(256), lds, st, a);
+            hipLaunchKernelGGL((k_dispatch_fp8<KT, true>), dim3(grid), block, lds, st, a, nseg, ipb);
         else
-            hipLaunchKernelGGL((k_dispatch_fp8<KT, false>), dim3(grid), dim3(256), lds, st, a);
+            hipLaunchKernelGGL((k_dispatch_fp8<KT, false>), dim3(grid), block, lds, st, a, nseg, ipb);
     } else {
         if (stream)
-            hipLaunchKernelGGL((k_dispatch_bf16<KT, true>), dim3(grid), dim3(256), lds, st, a);
+            hipLaunchKernelGGL((k_dispatch_bf16<KT, true>), dim3(grid), block, lds, st, a, nseg, ipb);
         else
-            hipLaunchKernelGGL((k_dispatch_bf16<KT, false>), dim3(grid), dim3(256), lds, st, a);
+            hipLaunchKernelGGL((k_dispatch_bf16<KT, false>), dim3(grid), block, lds, st, a, nseg, ipb);
     }
     return hipGetLastError();
 }
 
 template <int KT>
 hipError_t combine_kt(const CombineArgs& a, hipStream_t st) {
-    const int tpb = 4 * EP_COMBINE_TPW;
-    const int grid = (a.T + tpb - 1) / tpb;
-    hipLaunchKernelGGL((k_combine<KT>), dim3(grid), dim3(256), 0, st, a);
+    const int per_seg = kWave * EP_COMBINE_UNROLL * 8;
+    const int nseg = (a.H + per_seg - 1) / per_seg;
+    const int ipb = items_per_block(nseg, false);
+    const int64_t items = (int64_t)a.T * nseg;
+    const int grid = (int)((items + ipb - 1) / ipb);
+    hipLaunchKernelGGL((k_combine<KT>), dim3(grid), dim3(256), 0, st, a, nseg, ipb);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
-    if (a.S <= kFusedMaxSlots && a.E <= kFusedMaxExperts) {
-        const size_t lds = sizeof(int) * (size_t)(16 * a.E + a.E + a.E + 1 + 16);
-        hipLaunchKernelGGL(k_layout_fused, dim3(1), dim3(1024), lds, stream, a);
+    const size_t lds_rank = sizeof(int) * (size_t)(3 * a.E + 1 + kLayoutWaves + kLayoutThreads) +
+                            sizeof(uint16_t) * (size_t)kLayoutWaves * a.E;
+    if (a.S <= kLayoutSlotsPerBlock) {
+        hipLaunchKernelGGL((k_layout_rank<true>), dim3(1), dim3(kLayoutThreads), lds_rank, stream,
+                           a, 1, 0);
         return hipGetLastError();
     }
     const int nb = layout_blocks(a.S);
-    const size_t lds1 = sizeof(int) * (size_t)(3 * a.E + 1 + 4);
-    hipLaunchKernelGGL(k_layout_count, dim3(nb), dim3(256), lds1, stream, a, nb);
+    hipLaunchKernelGGL(k_layout_count, dim3(nb), dim3(kLayoutThreads), sizeof(int) * (size_t)a.E,
+                       stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const size_t lds2 = sizeof(int) * (size_t)(4 * a.E);
-    hipLaunchKernelGGL(k_layout_rank, dim3(nb), dim3(256), lds2, stream, a);
+    int epad = 1;
+    while (epad < a.E) epad <<= 1;
+    int tpe = kLayoutThreads / epad;
+    if (tpe > kWave) tpe = kWave;
+    int lg_tpe = 0;
+    while ((1 << (lg_tpe + 1)) <= tpe) ++lg_tpe;
+    hipLaunchKernelGGL((k_layout_rank<false>), dim3(nb), dim3(kLayoutThreads), lds_rank, stream, a,
+                       nb, lg_tpe);
     return hipGetLastError();
 }
 

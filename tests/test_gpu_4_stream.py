@@ -102,3 +102,14 @@ def test_stream_full_size():
 def test_bf16_prefill_shape_streaming():
     say("[stream] bf16 prefill shape tokens=1500")
     _run("prefill", 1500, False, consumer_first=True)
+
+
+@pytest.mark.parametrize("name,tokens,fp8", [("stream", 2000, True), ("share", 3000, False),
+                                              ("decode", -1, True)])
+def test_streaming_dispatch_pool_bytes(name, tokens, fp8):
+    """With the streaming release on, pool rows and scale bytes are still
+    bit-exact and padding rows untouched (device-coherent stores)."""
+    from gpu_helpers import full_path_check
+    say(f"[stream] pool bytes with tile_ready: {name} tokens={tokens} fp8={fp8}")
+    cfg, d = inputs(name, tokens)
+    full_path_check(cfg, d, fp8=fp8, tile_ready=True)
