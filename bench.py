@@ -92,25 +92,35 @@ def read_traffic(kernel: str, workload: str, per_launch_alg: float):
         return None
 
 
-def cpu_baseline(cfg, d, eo_host: np.ndarray, alg_total: int, reps: int):
-    """Time the oracle (single-threaded C) on the same workload."""
+def cpu_baseline(cfg, d, eo_host: np.ndarray, reps: int, tokens: int):
+    """Time the oracle (single-threaded C) on the first `tokens` tokens of the
+    same workload (all of them when tokens >= T); GB/s uses the same
+    algorithmic byte counts as the GPU figure, for that sample."""
     import oracle
+    n = min(tokens, cfg.tokens)
+    sub = {k: v[:n] for k, v in d.items()}
+    scfg = cfg.replace(tokens=n)
+    L0 = oracle.layout(sub["topk_idx"], cfg.num_experts, cfg.block_m)
+    ab = algorithmic_bytes(scfg, sub["topk_idx"], L0["expert_counts"], cfg.fp8)
+    alg = ab["layout"] + ab["dispatch"] + ab["combine"]
     times = []
     for _ in range(reps):
         t0 = time.perf_counter()
-        L = oracle.layout(d["topk_idx"], cfg.num_experts, cfg.block_m)
+        L = oracle.layout(sub["topk_idx"], cfg.num_experts, cfg.block_m)
         if cfg.fp8:
-            oracle.dispatch_fp8(d["x"], L["pool_recv_token"])
+            oracle.dispatch_fp8(sub["x"], L["pool_recv_token"])
         else:
-            oracle.dispatch_bf16(d["x"], L["pool_recv_token"])
-        oracle.combine(eo_host, L["slot_to_pool_row"], d["topk_weights"])
+            oracle.dispatch_bf16(sub["x"], L["pool_recv_token"])
+        oracle.combine(eo_host, L["slot_to_pool_row"], sub["topk_weights"])
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
-    return {"value": round(alg_total / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    what = (f"the full {cfg.name} workload ({n} tokens)" if n == cfg.tokens else
+            f"the first {n} of {cfg.tokens} tokens of the {cfg.name} workload")
+    return {"value": round(alg / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "seconds_per_pass": round(t, 3),
-            "tokens_per_s": round(cfg.tokens / t, 1),
-            "sample": f"the full {cfg.name} workload ({cfg.tokens} tokens), layout + "
-                      f"dispatch + combine, median of {reps} passes, one host thread"}
+            "tokens_per_s": round(n / t, 1),
+            "sample": f"{what}, layout + dispatch + combine, median of {reps} passes, "
+                      f"one host thread"}
 
 
 def main() -> int:
@@ -121,6 +131,8 @@ def main() -> int:
     ap.add_argument("--config", default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--cpu-tokens", type=int, default=-1,
+                    help="tokens of the CPU-oracle sample (default: all for bf16, 2048 for FP8)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -215,7 +227,8 @@ def main() -> int:
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         eo_host = eo.view(torch.int16).cpu().numpy().view(np.uint16)
-        cpu = cpu_baseline(cfg, d, eo_host, total, args.cpu_reps)
+        ntok = args.cpu_tokens if args.cpu_tokens > 0 else (2048 if fp8 else T)
+        cpu = cpu_baseline(cfg, d, eo_host, args.cpu_reps, ntok)
         del eo_host
 
     mode = "fp8" if fp8 else "bf16"

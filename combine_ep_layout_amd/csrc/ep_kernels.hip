@@ -220,10 +220,19 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
         const int e = tid >> lg_tpe, part = tid & (tpe - 1);
         int pre = 0, tot = 0;
         if (e < E) {
-            for (int bb = part; bb < nb; bb += tpe) {
-                const int c = a.ws[(int64_t)bb * E + e];
-                tot += c;
-                pre += (bb < b) ? c : 0;
+            // eight independent loads in flight per round
+            for (int bb0 = part; bb0 < nb; bb0 += 8 * tpe) {
+                int c[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int bb = bb0 + i * tpe;
+                    c[i] = (bb < nb) ? a.ws[(int64_t)bb * E + e] : 0;
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    tot += c[i];
+                    pre += (bb0 + i * tpe < b) ? c[i] : 0;
+                }
             }
         }
         for (int d = 1; d < tpe; d <<= 1) {
