@@ -47,17 +47,17 @@
 #ifndef EP_STREAM_TOKENS
 #define EP_STREAM_TOKENS 64    // whole tokens per 1024-thread workgroup in streaming mode
 #endif
-#ifndef EP_DISPATCH_NT
-#define EP_DISPATCH_NT 1       // non-temporal stores for pool rows
+#ifndef EP_DISPATCH_STORE
+#define EP_DISPATCH_STORE 1    // pool stores outside streaming: see store_row
 #endif
-#ifndef EP_COMBINE_NT
-#define EP_COMBINE_NT 1        // non-temporal stores for y
+#ifndef EP_COMBINE_STORE
+#define EP_COMBINE_STORE 1     // y stores: see store_row
 #endif
 #ifndef EP_COMBINE_NT_LOADS
 #define EP_COMBINE_NT_LOADS 1  // non-temporal loads of expert rows
 #endif
 #ifndef EP_STREAM_STORE
-#define EP_STREAM_STORE 2      // streaming pool stores: 0 plain, 1 device-coherent 64-bit, 2 buffer sc1
+#define EP_STREAM_STORE 2      // pool stores in streaming mode: see store_row
 #endif
 
 namespace epk {
@@ -422,22 +422,30 @@ __device__ __forceinline__ void clear_ranges(int E, int* s_lo, int* s_hi) {
     }
 }
 
-// Pool store of chunk c of a row.  Streaming stores may be device-coherent so
-// that the release has no dirty cache lines of this workgroup to write back.
-template <bool STREAM>
-__device__ __forceinline__ void store_pool(u32x4* row, int row_bytes, int c, const u32x4& v) {
-    if constexpr (STREAM && EP_STREAM_STORE == 1) {
+// Store of 16-byte chunk c of a row.  MODE 0: plain; 1: non-temporal;
+// 2: device-coherent (sc1) buffer store; 3: device-coherent 64-bit atomic
+// stores; 4: device-coherent and non-temporal buffer store.  Device-coherent
+// stores leave no dirty lines in the XCD's L2, which makes a later
+// device-scope release (and the end-of-kernel write-back) cheap.
+template <int MODE>
+__device__ __forceinline__ void store_row(u32x4* row, int row_bytes, int c, const u32x4& v) {
+    if constexpr (MODE == 3) {
         uint64_t* q = (uint64_t*)(row + c);
         __hip_atomic_store(q, (uint64_t)v[0] | ((uint64_t)v[1] << 32), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(q + 1, (uint64_t)v[2] | ((uint64_t)v[3] << 32), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-    } else if constexpr (STREAM && EP_STREAM_STORE == 2) {
+    } else if constexpr (MODE == 2 || MODE == 4) {
         __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(row, (short)0, row_bytes, 0x00020000);
-        __builtin_amdgcn_raw_buffer_store_b128(v, r, c * 16, 0, 16);
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, c * 16, 0, MODE == 2 ? 16 : 18);
     } else {
-        store_v<EP_DISPATCH_NT>(row + c, v);
+        store_v<MODE == 1>(row + c, v);
     }
+}
+
+template <bool STREAM>
+__device__ __forceinline__ void store_pool(u32x4* row, int row_bytes, int c, const u32x4& v) {
+    store_row<STREAM ? EP_STREAM_STORE : EP_DISPATCH_STORE>(row, row_bytes, c, v);
 }
 
 template <int KT>
@@ -715,7 +723,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a, int nseg, int ip
             for (int i = 0; i < 4; ++i)
                 o[i] = f32_to_bf16_rne(acc[2 * i]) | (f32_to_bf16_rne(acc[2 * i + 1]) << 16);
             const int c = c0 + u * kWave;
-            if (c < n16) store_v<EP_COMBINE_NT>(dst + c, o);
+            if (c < n16) store_row<EP_COMBINE_STORE>(dst, a.H * 2, c, o);
         }
     }
 }
