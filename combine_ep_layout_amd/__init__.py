@@ -33,6 +33,8 @@ EP_ERR_HIP = 7
 
 EP_DISPATCH_FP8 = 1 << 0
 EP_DISPATCH_TILE_READY = 1 << 1
+EP_DISPATCH_BORROW = 1 << 2
+EP_CONSUME_GATHER = 1 << 3
 
 ARRAYS = {
     "expert_counts": (0, torch.int32),
@@ -51,7 +53,7 @@ EXPORTS = [
     "ep_handle_create", "ep_handle_destroy", "ep_pool_capacity_rows", "ep_max_tiles",
     "ep_num_tokens", "ep_layout", "ep_dispatch", "ep_combine", "ep_handle_get_view",
     "ep_array_bytes", "ep_copy_array", "ep_counts_to_host", "ep_handle_sync_status",
-    "ep_tile_consume", "ep_status_string",
+    "ep_tile_consume", "ep_status_string", "ep_borrow_release",
 ]
 
 
@@ -89,6 +91,7 @@ def _load() -> ctypes.CDLL:
         "ep_handle_sync_status": (st, [P, P]),
         "ep_tile_consume": (st, [P, U32, P, P, I32, U32, P, I32, U32, P]),
         "ep_status_string": (ctypes.c_char_p, [st]),
+        "ep_borrow_release": (st, [P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -168,6 +171,10 @@ def ep_tile_consume(h, seq: int, pool: torch.Tensor, pool_scales: Optional[torch
                                 workgroups, spin_limit_us, _stream(stream)), "ep_tile_consume")
 
 
+def ep_borrow_release(h, consumer_stream=None) -> None:
+    _check(_lib.ep_borrow_release(h, _stream(consumer_stream)), "ep_borrow_release")
+
+
 def ep_handle_sync_status(h, stream=None) -> int:
     return int(_lib.ep_handle_sync_status(h, _stream(stream)))
 
@@ -233,6 +240,17 @@ class EpHandle:
         flags = (EP_DISPATCH_FP8 if fp8 else 0) | (EP_DISPATCH_TILE_READY if tile_ready else 0)
         return ep_dispatch(self._h, x, pool, pool_scales if fp8 else None, flags, stream)
 
+    def borrow(self, x: torch.Tensor, stream=None) -> int:
+        """Dispatch without a copy: lend x through the row map
+        (pool_recv_token).  Holds the handle's lease until release()."""
+        _require(x, torch.bfloat16, "x", self.device)
+        if x.dim() != 2 or x.shape[0] != self.num_tokens:
+            raise ValueError("x must be [num_tokens of the layout, hidden]")
+        return ep_dispatch(self._h, x, None, None, EP_DISPATCH_BORROW, stream)
+
+    def release(self, consumer_stream=None) -> None:
+        ep_borrow_release(self._h, consumer_stream)
+
     def combine(self, epoch: int, expert_out: torch.Tensor, y: Optional[torch.Tensor] = None,
                 stream=None) -> torch.Tensor:
         _require(expert_out, torch.bfloat16, "expert_out", self.device)
@@ -249,11 +267,18 @@ class EpHandle:
 
     def tile_consume(self, seq: int, pool: torch.Tensor, pool_scales: Optional[torch.Tensor],
                      hidden: int, out: torch.Tensor, fp8: bool = False, workgroups: int = 32,
-                     spin_limit_us: int = 2_000_000, stream=None) -> None:
+                     spin_limit_us: int = 2_000_000, stream=None, gather: bool = False) -> None:
         _require(out, torch.bfloat16, "out", self.device)
         if out.shape[0] < self.capacity_rows or out.shape[1] != hidden:
             raise ValueError("out must be at least [capacity_rows, hidden]")
-        flags = EP_DISPATCH_FP8 if fp8 else 0
+        if gather:
+            # pool is the borrowed slab x [num_tokens, hidden]
+            _require(pool, torch.bfloat16, "slab", self.device)
+            if pool.shape != (self.num_tokens, hidden):
+                raise ValueError("the gathered slab must be [num_tokens, hidden]")
+        elif pool.shape[0] < self.capacity_rows:
+            raise ValueError("pool must have at least capacity_rows rows")
+        flags = (EP_DISPATCH_FP8 if fp8 else 0) | (EP_CONSUME_GATHER if gather else 0)
         ep_tile_consume(self._h, seq, pool, pool_scales if fp8 else None, hidden, flags, out,
                         workgroups, spin_limit_us, stream)
 

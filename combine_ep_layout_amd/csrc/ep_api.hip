@@ -37,6 +37,10 @@ struct ep_handle {
     uint32_t epoch;
     uint32_t seq;
     uint32_t round;           // TILE_READY dispatches since the layout
+    // borrowed-view lease
+    bool lease;               // a borrowing dispatch's view is out
+    bool lease_wait;          // the next call waits for lease_event first
+    hipEvent_t lease_event;   // recorded on the consumer stream at release
 };
 
 namespace {
@@ -63,6 +67,14 @@ ep_status check_config(const ep_config* c) {
 }
 
 ep_status hip_status(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP; }
+
+// Calls that rewrite the row map wait for the consumers of a released view.
+ep_status wait_lease(ep_handle* h, hipStream_t stream) {
+    if (!h->lease_wait) return EP_OK;
+    if (hipStreamWaitEvent(stream, h->lease_event, 0) != hipSuccess) return EP_ERR_HIP;
+    h->lease_wait = false;
+    return EP_OK;
+}
 
 }  // namespace
 
@@ -138,22 +150,27 @@ ep_status ep_handle_create(const ep_config* cfg, ep_handle** out) {
         *p.dst = (char*)h->block + off;
         off += round_up(p.bytes ? p.bytes : 1, 256);
     }
-    if (hipMemset(h->block, 0, total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    if (hipMemset(h->block, 0, total) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
+        hipEventCreateWithFlags(&h->lease_event, hipEventDisableTiming) != hipSuccess) {
         (void)hipFree(h->block);
         delete h;
         return EP_ERR_HIP;
     }
+    h->lease = false;
+    h->lease_wait = false;
     *out = h;
     return EP_OK;
 }
 
 ep_status ep_handle_destroy(ep_handle* h) {
     if (!h) return EP_OK;
+    if (h->lease) return EP_ERR_HANDLE_STATE;
     int cur = 0;
     hipError_t e = hipGetDevice(&cur);
     if (e == hipSuccess && cur != h->device) e = hipSetDevice(h->device);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     hipError_t f = hipFree(h->block);
+    (void)hipEventDestroy(h->lease_event);
     if (cur != h->device) (void)hipSetDevice(cur);
     delete h;
     return (e == hipSuccess && f == hipSuccess) ? EP_OK : EP_ERR_HIP;
@@ -171,6 +188,9 @@ ep_status ep_layout(ep_handle* h, const int32_t* topk_idx, const float* topk_wei
     if (num_tokens > 0 && (!topk_idx || !topk_weights || !aligned4(topk_idx) ||
                            !aligned4(topk_weights)))
         return EP_ERR_INVALID_ARGUMENT;
+    if (h->lease) return EP_ERR_HANDLE_STATE;
+    ep_status ws = wait_lease(h, stream);
+    if (ws != EP_OK) return ws;
     epk::LayoutArgs a;
     a.topk_idx = topk_idx;
     a.topk_w = topk_weights;
@@ -205,16 +225,30 @@ ep_status ep_dispatch(ep_handle* h, const void* x, int32_t hidden, void* pool,
                       uint8_t* pool_scales, uint32_t flags, hipStream_t stream,
                       uint32_t* seq_out) {
     if (!h) return EP_ERR_INVALID_ARGUMENT;
-    if (flags & ~(EP_DISPATCH_FP8 | EP_DISPATCH_TILE_READY)) return EP_ERR_INVALID_ARGUMENT;
+    if (flags & ~(EP_DISPATCH_FP8 | EP_DISPATCH_TILE_READY | EP_DISPATCH_BORROW))
+        return EP_ERR_INVALID_ARGUMENT;
     const bool fp8 = (flags & EP_DISPATCH_FP8) != 0;
     const bool ready = (flags & EP_DISPATCH_TILE_READY) != 0;
     if (hidden <= 0 || hidden % 8 != 0) return EP_ERR_INVALID_ARGUMENT;
     if (hidden > kMaxHidden) return EP_ERR_UNSUPPORTED;
+    if (flags & EP_DISPATCH_BORROW) {
+        // lend x through the row map: bf16 only, nothing to copy into
+        if (fp8 || ready) return EP_ERR_UNSUPPORTED;
+        if (pool || pool_scales) return EP_ERR_INVALID_ARGUMENT;
+        if (h->T < 0 || h->lease) return EP_ERR_HANDLE_STATE;
+        if (h->T > 0 && (!x || !aligned16(x))) return EP_ERR_INVALID_ARGUMENT;
+        h->lease = true;
+        h->seq += 1;
+        if (seq_out) *seq_out = h->seq;
+        return EP_OK;
+    }
     if (fp8 && (hidden % 128 != 0 || !pool_scales)) return EP_ERR_INVALID_ARGUMENT;
     if (!fp8 && pool_scales) return EP_ERR_INVALID_ARGUMENT;
-    if (h->T < 0) return EP_ERR_HANDLE_STATE;
+    if (h->T < 0 || h->lease) return EP_ERR_HANDLE_STATE;
     if (h->T > 0 && (!x || !pool || !aligned16(x) || !aligned16(pool)))
         return EP_ERR_INVALID_ARGUMENT;
+    ep_status ws = wait_lease(h, stream);
+    if (ws != EP_OK) return ws;
     epk::DispatchArgs a;
     a.x = x;
     a.T = h->T;
@@ -247,7 +281,7 @@ ep_status ep_combine(const ep_handle* h, uint32_t epoch, const void* expert_out,
     if (!h) return EP_ERR_INVALID_ARGUMENT;
     if (hidden <= 0 || hidden % 8 != 0) return EP_ERR_INVALID_ARGUMENT;
     if (hidden > kMaxHidden) return EP_ERR_UNSUPPORTED;
-    if (h->T < 0 || epoch != h->epoch) return EP_ERR_HANDLE_STATE;
+    if (h->T < 0 || epoch != h->epoch || h->lease) return EP_ERR_HANDLE_STATE;
     if (h->T > 0 && (!expert_out || !y || !aligned16(expert_out) || !aligned16(y)))
         return EP_ERR_INVALID_ARGUMENT;
     epk::CombineArgs a;
@@ -259,6 +293,15 @@ ep_status ep_combine(const ep_handle* h, uint32_t epoch, const void* expert_out,
     a.weights = h->weights;
     a.y = y;
     return hip_status(epk::launch_combine(a, stream));
+}
+
+ep_status ep_borrow_release(ep_handle* h, hipStream_t consumer_stream) {
+    if (!h) return EP_ERR_INVALID_ARGUMENT;
+    if (!h->lease) return EP_ERR_HANDLE_STATE;
+    if (hipEventRecord(h->lease_event, consumer_stream) != hipSuccess) return EP_ERR_HIP;
+    h->lease = false;
+    h->lease_wait = true;
+    return EP_OK;
 }
 
 ep_status ep_handle_get_view(const ep_handle* h, ep_handle_view* out) {
@@ -350,12 +393,15 @@ ep_status ep_tile_consume(const ep_handle* h, uint32_t seq, const void* pool,
                           const uint8_t* pool_scales, int32_t hidden, uint32_t flags, void* out,
                           int32_t workgroups, uint32_t spin_limit_us, hipStream_t stream) {
     if (!h) return EP_ERR_INVALID_ARGUMENT;
-    if (flags & ~(EP_DISPATCH_FP8 | EP_DISPATCH_TILE_READY)) return EP_ERR_INVALID_ARGUMENT;
+    if (flags & ~(EP_DISPATCH_FP8 | EP_DISPATCH_TILE_READY | EP_CONSUME_GATHER))
+        return EP_ERR_INVALID_ARGUMENT;
     const bool fp8 = (flags & EP_DISPATCH_FP8) != 0;
+    const bool gather = (flags & EP_CONSUME_GATHER) != 0;
+    if (fp8 && gather) return EP_ERR_UNSUPPORTED;
     if (hidden <= 0 || hidden % 8 != 0 || (fp8 && (hidden % 128 != 0 || !pool_scales)))
         return EP_ERR_INVALID_ARGUMENT;
     if (hidden > kMaxHidden) return EP_ERR_UNSUPPORTED;
-    if (workgroups < 1 || workgroups > 1024) return EP_ERR_INVALID_ARGUMENT;
+    if (workgroups < 1 || workgroups > 65536) return EP_ERR_INVALID_ARGUMENT;
     if (h->T < 0) return EP_ERR_HANDLE_STATE;
     if (!pool || !out || !aligned16(pool) || !aligned16(out)) return EP_ERR_INVALID_ARGUMENT;
     epk::ConsumeArgs a;
@@ -364,6 +410,7 @@ ep_status ep_tile_consume(const ep_handle* h, uint32_t seq, const void* pool,
     a.H = hidden;
     a.BM = h->cfg.block_m;
     a.fp8 = fp8 ? 1 : 0;
+    a.gather = gather ? 1 : 0;
     a.num_tiles = h->num_tiles;
     a.recv_token = h->recv_token;
     a.tile_ready = h->tile_ready;

@@ -75,6 +75,7 @@ struct ConsumeArgs {
     int32_t H;
     int32_t BM;
     int32_t fp8;
+    int32_t gather;             // rows come from slab row recv_token[r]
     const int32_t* num_tiles;
     const int32_t* recv_token;
     const uint32_t* tile_ready;

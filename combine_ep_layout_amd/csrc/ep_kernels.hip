@@ -766,7 +766,8 @@ __global__ __launch_bounds__(256) void k_tile_consume(ConsumeArgs a) {
         if (!s_go) return;                    // timed out: give up on the remaining tiles too
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         for (int r = j * a.BM + w; r < (j + 1) * a.BM; r += 4) {
-            if (a.recv_token[r] < 0) continue;
+            const int src_tok = a.recv_token[r];
+            if (src_tok < 0) continue;
             if (a.fp8) {
                 const int nunit = a.H / 16;
                 const u32x4* src = (const u32x4*)a.pool + (int64_t)r * nunit;
@@ -795,7 +796,8 @@ __global__ __launch_bounds__(256) void k_tile_consume(ConsumeArgs a) {
                 }
             } else {
                 const int n16 = a.H / 8;
-                const u32x4* src = (const u32x4*)a.pool + (int64_t)r * n16;
+                const int64_t src_row = a.gather ? (int64_t)src_tok : (int64_t)r;
+                const u32x4* src = (const u32x4*)a.pool + src_row * n16;
                 u32x4* dst = (u32x4*)a.out + (int64_t)r * n16;
                 for (int c = lane; c < n16; c += kWave) dst[c] = src[c];
             }

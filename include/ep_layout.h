@@ -21,6 +21,12 @@
  *   [WEIGHTS] same blog, router-weight section: y_t = sum_j p_{t,j} o_{t,j}.
  *   [FP8]  instagit DeepEP low-latency page, "FP8 and Quantization Support":
  *          float8_e4m3fn payload with UE8M0 scales.
+ *   [BORROW] DeepEP PR #769, "Add opt-in borrowed receive storage for compact
+ *          BF16 dispatch", Description: dispatch may skip the activation copy
+ *          and hand an indexed consumer a view (slab, row indices) instead; the
+ *          view is an exclusive lease that is released on the consumer
+ *          streams, calls that would disturb it are rejected while it is held,
+ *          and unsupported modes are rejected up front.
  *
  * Conventions for every call:
  *   - Pointers marked "device" are device memory on the handle's GPU, 16-byte
@@ -78,6 +84,11 @@ typedef struct ep_config {
 /* ep_dispatch flags. */
 #define EP_DISPATCH_FP8        (1u << 0) /* e4m3fn payload + UE8M0 scales ([FP8])    */
 #define EP_DISPATCH_TILE_READY (1u << 1) /* per-tile arrival counts release tile_ready ([SEP]) */
+#define EP_DISPATCH_BORROW     (1u << 2) /* no copy: lend x through the row map ([BORROW]) */
+
+/* ep_tile_consume flag: rows are gathered from a borrowed slab through
+ * pool_recv_token instead of being read from a pool ([BORROW]). */
+#define EP_CONSUME_GATHER      (1u << 3)
 
 /* Allocate a handle and all its device metadata on the current device.
  * Returns EP_ERR_INVALID_ARGUMENT for out-of-range fields or when the pool
@@ -135,6 +146,14 @@ ep_status ep_layout(ep_handle* h, const int32_t* topk_idx, const float* topk_wei
 ep_status ep_dispatch(ep_handle* h, const void* x, int32_t hidden, void* pool,
                       uint8_t* pool_scales, uint32_t flags, hipStream_t stream,
                       uint32_t* seq_out);
+/* EP_DISPATCH_BORROW ([BORROW]): nothing is copied or launched.  The rows are
+ * lent as the view (slab = x, row indices = pool_recv_token of the current
+ * layout): pool row r is row pool_recv_token[r] of x, -1 for padding.  Only a
+ * bf16 dispatch with pool == NULL and pool_scales == NULL may borrow;
+ * EP_DISPATCH_FP8 or EP_DISPATCH_TILE_READY with it is EP_ERR_UNSUPPORTED.
+ * The handle then holds an exclusive lease: ep_layout, ep_dispatch,
+ * ep_combine and ep_handle_destroy return EP_ERR_HANDLE_STATE until
+ * ep_borrow_release.  The caller keeps x alive and unchanged meanwhile. */
 
 /* Weighted sum back in original token order ([WEIGHTS], [ROUND]).
  *   epoch       the value ep_layout returned; else EP_ERR_HANDLE_STATE.
@@ -144,6 +163,13 @@ ep_status ep_dispatch(ep_handle* h, const void* x, int32_t hidden, void* pool,
  * starting from +0 and skipping masked slots; a token with no slot gets +0. */
 ep_status ep_combine(const ep_handle* h, uint32_t epoch, const void* expert_out,
                      int32_t hidden, void* y, hipStream_t stream);
+
+/* End the lease of a borrowing dispatch ([BORROW]).  consumer_stream is the
+ * stream the consumers of the view were enqueued on; the handle's next call
+ * waits (on its own stream) until that stream's work enqueued so far is done,
+ * so a new layout never overwrites the row indices under a delayed reader.
+ * Returns EP_ERR_HANDLE_STATE when no lease is held. */
+ep_status ep_borrow_release(ep_handle* h, hipStream_t consumer_stream);
 
 /* Device pointers into the handle's metadata; valid until the next ep_layout
  * or ep_handle_destroy.  Lengths: counts E, offsets E+1, tile arrays
@@ -196,11 +222,13 @@ ep_status ep_handle_sync_status(ep_handle* h, hipStream_t stream);
 
 /* Stand-in for the consumer of the streaming release ([SEP]: a consumer
  * kernel spins on an acquire-load of tile_ready[tile] >= dispatch_seq from a
- * different stream).  A bounded grid of `workgroups` walks tiles in order,
+ * different stream).  A bounded grid of `workgroups` (1..65536) walks tiles in order,
  * waits until tile_ready[tile] has reached `seq` (wrap-safe), then writes
  * every real row of the tile to `out` (device bf16 [capacity_rows, hidden]):
  * a copy of a bf16 pool, or with EP_DISPATCH_FP8 the dequantised value
- * bf16(e4m3(q) * 2^(scale-127)).  A wait longer than spin_limit_us gives up
+ * bf16(e4m3(q) * 2^(scale-127)).  With EP_CONSUME_GATHER, `pool` is a
+ * borrowed bf16 slab [num_tokens, hidden] and row r is read from slab row
+ * pool_recv_token[r] (the indexed consumer of [BORROW]).  A wait longer than spin_limit_us gives up
  * on that tile and sets EP_ERR_TIMEOUT in the error word, so it always ends.
  * The caller orders it after ep_layout (e.g. with an event). */
 ep_status ep_tile_consume(const ep_handle* h, uint32_t seq, const void* pool,
