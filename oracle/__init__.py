@@ -6,7 +6,8 @@ through ctypes and shares nothing with the HIP library.
 
 Pinned functions (each checked in ``tests/test_oracle_*.py`` against something
 other than itself): layout, bf16 dispatch, FP8 quantisation (scale exponent and
-e4m3fn codes), dequantisation, combine.  Nothing here is "parity unpinned".
+e4m3fn codes), dequantisation, combine, combine and dispatch backward.  Nothing
+here is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -64,6 +65,11 @@ def _load():
     lib.eo_f32_to_bf16_n.restype = None
     lib.eo_ue8m0_exponent_n.argtypes = [P, ctypes.c_int64, P]
     lib.eo_ue8m0_exponent_n.restype = None
+    lib.eo_combine_backward.argtypes = [P, P, P, P, ctypes.c_int64, ctypes.c_int32,
+                                        ctypes.c_int32, P, P]
+    lib.eo_combine_backward.restype = None
+    lib.eo_dispatch_backward.argtypes = [P, P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P]
+    lib.eo_dispatch_backward.restype = None
     _lib = lib
     return lib
 
@@ -224,3 +230,31 @@ def combine_gathered(rows: np.ndarray, valid: np.ndarray, weights: np.ndarray) -
     y = np.empty((n, H), np.uint16)
     _load().eo_combine_gathered(_p(rows), _p(v), _p(w), n, K, H, _p(y))
     return y
+
+
+# ---------------------------------------------------------------- backward --
+
+def combine_backward(grad_y: np.ndarray, expert_out: np.ndarray, slot_to_row: np.ndarray,
+                     weights: np.ndarray, grad_eo_init: Optional[np.ndarray] = None):
+    """Returns (grad_expert_out [cap, H] bf16 bits, grad_weights [T, K] float32)."""
+    gy = np.ascontiguousarray(grad_y, dtype=np.uint16)
+    eo = np.ascontiguousarray(expert_out, dtype=np.uint16)
+    w = np.ascontiguousarray(weights, dtype=np.float32)
+    T, K = w.shape
+    H = gy.shape[1]
+    s2r = np.ascontiguousarray(slot_to_row, dtype=np.int32)
+    geo = (np.zeros_like(eo) if grad_eo_init is None
+           else np.array(grad_eo_init, dtype=np.uint16, copy=True, order="C"))
+    gw = np.empty((T, K), np.float32)
+    _load().eo_combine_backward(_p(gy), _p(eo), _p(s2r), _p(w), T, K, H, _p(geo), _p(gw))
+    return geo, gw
+
+
+def dispatch_backward(grad_pool: np.ndarray, slot_to_row: np.ndarray, tokens: int,
+                      top_k: int) -> np.ndarray:
+    gp = np.ascontiguousarray(grad_pool, dtype=np.uint16)
+    H = gp.shape[1]
+    s2r = np.ascontiguousarray(slot_to_row, dtype=np.int32)
+    gx = np.empty((tokens, H), np.uint16)
+    _load().eo_dispatch_backward(_p(gp), _p(s2r), tokens, top_k, H, _p(gx))
+    return gx

@@ -321,3 +321,58 @@ void eo_ue8m0_exponent_n(const float* amax, int64_t n, int32_t* out)
     for (int64_t i = 0; i < n; ++i)
         out[i] = eo_ue8m0_exponent(amax[i]);
 }
+
+/* ------------------------------------------------------------ backward --- */
+
+/* Backward of the combine (StreamEP README, "What's in the box": the buffer
+ * exposes combine_grads for the backward pass; the pages give no formula, so
+ * this is the derivative of y_t = sum_k w_{t,k} o_{row(t,k)}):
+ *   grad_eo[row(t,k), c] = bf16( fp32( w[t,k] * grad_y[t,c] ) )
+ *   grad_w[t,k]          = fp32( sum over c ascending of grad_y[t,c] * o[row,c] )
+ *                          accumulated in double (each bf16 x bf16 product is
+ *                          exact in double), rounded once to float
+ * Masked slots: grad_w = 0 and no row is written. */
+void eo_combine_backward(const uint16_t* grad_y, const uint16_t* expert_out,
+                         const int32_t* slot_to_row, const float* w, int64_t T, int32_t K,
+                         int32_t H, uint16_t* grad_eo, float* grad_w)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t k = 0; k < K; ++k) {
+            int32_t r = slot_to_row[t * K + k];
+            if (r < 0) {
+                grad_w[t * K + k] = 0.0f;
+                continue;
+            }
+            double dot = 0.0;
+            for (int32_t c = 0; c < H; ++c) {
+                float g = eo_bf16_to_f32(grad_y[t * H + c]);
+                float o = eo_bf16_to_f32(expert_out[(int64_t)r * H + c]);
+                float p = w[t * K + k] * g;
+                grad_eo[(int64_t)r * H + c] = eo_f32_to_bf16(p);
+                dot += (double)g * (double)o;
+            }
+            grad_w[t * K + k] = (float)dot;
+        }
+    }
+}
+
+/* Backward of the dispatch (dispatch_grads): every pool row was a copy of its
+ * token's row, so the token's gradient is the sum of its rows' gradients:
+ *   grad_x[t, c] = bf16( fp32 sum over unmasked k ascending of grad_pool[row(t,k), c] )
+ * starting from +0; a token with no unmasked slot gets +0. */
+void eo_dispatch_backward(const uint16_t* grad_pool, const int32_t* slot_to_row, int64_t T,
+                          int32_t K, int32_t H, uint16_t* grad_x)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t c = 0; c < H; ++c) {
+            float acc = 0.0f;
+            for (int32_t k = 0; k < K; ++k) {
+                int32_t r = slot_to_row[t * K + k];
+                if (r < 0)
+                    continue;
+                acc = acc + eo_bf16_to_f32(grad_pool[(int64_t)r * H + c]);
+            }
+            grad_x[t * H + c] = eo_f32_to_bf16(acc);
+        }
+    }
+}
