@@ -186,6 +186,64 @@ def borrow_compare(steps: int, warmup: int) -> dict:
                              "tokens/rank, -13.5% at 16384, +15.9% at 1024"}
 
 
+def backward_bench(cfg, steps: int, warmup: int) -> dict:
+    """Times combine_grads and dispatch_grads on one workload.  Algorithmic
+    bytes: combine backward reads grad_y (2HT), the expert rows (2H*N_a) and
+    the slot map + weights (8TK), writes the gradient rows (2H*N_a) and grad_w
+    (4TK); dispatch backward reads the gradient rows (2H*N_a) and the slot map
+    (4TK) and writes grad_x (2HT)."""
+    import torch
+    import combine_ep_layout_amd as ep
+    from synth import generate
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    d = generate(cfg, 0)
+    T, K, H = cfg.tokens, cfg.top_k, cfg.hidden
+    idx = torch.from_numpy(d["topk_idx"]).to(dev)
+    w = torch.from_numpy(d["topk_weights"]).to(dev)
+    h = ep.EpHandle(T, K, cfg.num_experts, cfg.block_m)
+    epoch = h.layout(idx, w)
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    eo = torch.empty(h.capacity_rows, H, dtype=torch.bfloat16, device=dev)
+    for r0 in range(0, h.capacity_rows, 16384):
+        r1 = min(h.capacity_rows, r0 + 16384)
+        eo[r0:r1] = torch.randn(r1 - r0, H, generator=g, device=dev).to(torch.bfloat16)
+    gy = torch.randn(T, H, generator=g, device=dev).to(torch.bfloat16)
+    geo = torch.empty_like(eo)
+    gw = torch.empty(T, K, dtype=torch.float32, device=dev)
+    gx = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    for _ in range(warmup):
+        ep.ep_combine_backward(h.raw, epoch, gy, eo, geo, gw)
+        ep.ep_dispatch_backward(h.raw, epoch, geo, gx)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in ev:
+        e[0].record(stream)
+        ep.ep_combine_backward(h.raw, epoch, gy, eo, geo, gw)
+        e[1].record(stream)
+        ep.ep_dispatch_backward(h.raw, epoch, geo, gx)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    cb = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+    db = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
+    assert h.sync_status() == ep.EP_OK
+    h.close()
+    n_a = int((d["topk_idx"] >= 0).sum())
+    b_cb = 2 * H * T + 4 * H * n_a + 12 * T * K
+    b_db = 2 * H * n_a + 4 * T * K + 2 * H * T
+    return {"metric": "combine_grads + dispatch_grads HBM GB/s", "unit": "GB/s",
+            "value": round((b_cb + b_db) / ((cb + db) * 1e-6) / 1e9, 2), "higher_is_better": True,
+            "data": "synthetic", "dtype": "bf16",
+            "config": {"workload": f"{cfg.name}: {T} tokens, hidden {H}, {cfg.num_experts} experts "
+                                   f"{cfg.routing} top-{K}, BLOCK_M {cfg.block_m}"},
+            "kernels_us": {"combine_backward": round(cb, 2), "dispatch_backward": round(db, 2)},
+            "alg_bytes": {"combine_backward": b_cb, "dispatch_backward": b_db},
+            "gbs": {"combine_backward": round(b_cb / (cb * 1e-6) / 1e9, 1),
+                    "dispatch_backward": round(b_db / (db * 1e-6) / 1e9, 1)},
+            "pct_of_peak": round(100.0 * (b_cb + b_db) / ((cb + db) * 1e-6) / 1e9 / PEAK_GBS, 2)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -200,6 +258,8 @@ def main() -> int:
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--borrow-compare", action="store_true",
                     help="print the borrowed-view vs copy comparison instead")
+    ap.add_argument("--backward", action="store_true",
+                    help="print the backward (combine_grads + dispatch_grads) measurement instead")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -214,6 +274,10 @@ def main() -> int:
     if args.borrow_compare:
         torch.cuda.set_device(0)
         print(json.dumps(borrow_compare(args.steps, args.warmup)), flush=True)
+        return 0
+    if args.backward:
+        torch.cuda.set_device(0)
+        print(json.dumps(backward_bench(CONFIGS[args.config], args.steps, args.warmup)), flush=True)
         return 0
 
     cfg = CONFIGS[args.config]

@@ -4,8 +4,8 @@ one MI355X (gfx950).
 Argument marshalling only: every step of layout, dispatch and combine runs in
 the library's HIP kernels.  PyTorch provides device memory and streams; the
 library is loaded after torch so that both share torch's HIP runtime.  Import
-fails loudly when the library has not been built (``python -m
-combine_ep_layout_amd.build``).
+fails loudly when the library has not been built (``python
+combine_ep_layout_amd/build.py``).
 
 The names follow the C ABI in include/ep_layout.h (ep_handle_create,
 ep_layout, ep_dispatch, ep_combine, ...); ``EpHandle`` bundles them.
@@ -53,7 +53,8 @@ EXPORTS = [
     "ep_handle_create", "ep_handle_destroy", "ep_pool_capacity_rows", "ep_max_tiles",
     "ep_num_tokens", "ep_layout", "ep_dispatch", "ep_combine", "ep_handle_get_view",
     "ep_array_bytes", "ep_copy_array", "ep_counts_to_host", "ep_handle_sync_status",
-    "ep_tile_consume", "ep_status_string", "ep_borrow_release",
+    "ep_tile_consume", "ep_status_string", "ep_borrow_release", "ep_combine_backward",
+    "ep_dispatch_backward",
 ]
 
 
@@ -71,7 +72,7 @@ class _Config(ctypes.Structure):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          f"'python -m combine_ep_layout_amd.build' (hipcc, gfx950)")
+                          f"'python combine_ep_layout_amd/build.py' (hipcc, gfx950)")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, U32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_int64
     st = ctypes.c_int
@@ -92,6 +93,8 @@ def _load() -> ctypes.CDLL:
         "ep_tile_consume": (st, [P, U32, P, P, I32, U32, P, I32, U32, P]),
         "ep_status_string": (ctypes.c_char_p, [st]),
         "ep_borrow_release": (st, [P, P]),
+        "ep_combine_backward": (st, [P, U32, P, P, I32, P, P, P]),
+        "ep_dispatch_backward": (st, [P, U32, P, I32, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -171,6 +174,20 @@ def ep_tile_consume(h, seq: int, pool: torch.Tensor, pool_scales: Optional[torch
                                 workgroups, spin_limit_us, _stream(stream)), "ep_tile_consume")
 
 
+def ep_combine_backward(h, epoch: int, grad_y: torch.Tensor, expert_out: torch.Tensor,
+                        grad_expert_out: torch.Tensor, grad_weights: torch.Tensor,
+                        stream=None) -> None:
+    _check(_lib.ep_combine_backward(h, epoch, _ptr(grad_y), _ptr(expert_out), grad_y.shape[1],
+                                    _ptr(grad_expert_out), _ptr(grad_weights), _stream(stream)),
+           "ep_combine_backward")
+
+
+def ep_dispatch_backward(h, epoch: int, grad_pool: torch.Tensor, grad_x: torch.Tensor,
+                         stream=None) -> None:
+    _check(_lib.ep_dispatch_backward(h, epoch, _ptr(grad_pool), grad_pool.shape[1], _ptr(grad_x),
+                                     _stream(stream)), "ep_dispatch_backward")
+
+
 def ep_borrow_release(h, consumer_stream=None) -> None:
     _check(_lib.ep_borrow_release(h, _stream(consumer_stream)), "ep_borrow_release")
 
@@ -239,6 +256,38 @@ class EpHandle:
             _require(pool_scales, torch.uint8, "pool_scales", self.device)
         flags = (EP_DISPATCH_FP8 if fp8 else 0) | (EP_DISPATCH_TILE_READY if tile_ready else 0)
         return ep_dispatch(self._h, x, pool, pool_scales if fp8 else None, flags, stream)
+
+    def combine_backward(self, epoch: int, grad_y: torch.Tensor, expert_out: torch.Tensor,
+                         grad_expert_out: Optional[torch.Tensor] = None, stream=None):
+        """Returns (grad_expert_out [capacity_rows, H] bf16, grad_weights [T, K] fp32)."""
+        _require(grad_y, torch.bfloat16, "grad_y", self.device)
+        _require(expert_out, torch.bfloat16, "expert_out", self.device)
+        H = grad_y.shape[1]
+        if grad_y.shape[0] != self.num_tokens or expert_out.shape[0] < self.capacity_rows \
+                or expert_out.shape[1] != H:
+            raise ValueError("grad_y must be [num_tokens, H], expert_out [capacity_rows, H]")
+        if grad_expert_out is None:
+            grad_expert_out = torch.empty(self.capacity_rows, H, dtype=torch.bfloat16, device=self.device)
+        _require(grad_expert_out, torch.bfloat16, "grad_expert_out", self.device)
+        if grad_expert_out.shape[0] < self.capacity_rows or grad_expert_out.shape[1] != H:
+            raise ValueError("grad_expert_out must be at least [capacity_rows, H]")
+        grad_w = torch.empty(self.num_tokens, self.top_k, dtype=torch.float32, device=self.device)
+        ep_combine_backward(self._h, epoch, grad_y, expert_out, grad_expert_out, grad_w, stream)
+        return grad_expert_out, grad_w
+
+    def dispatch_backward(self, epoch: int, grad_pool: torch.Tensor,
+                          grad_x: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        _require(grad_pool, torch.bfloat16, "grad_pool", self.device)
+        H = grad_pool.shape[1]
+        if grad_pool.shape[0] < self.capacity_rows:
+            raise ValueError("grad_pool must have at least capacity_rows rows")
+        if grad_x is None:
+            grad_x = torch.empty(self.num_tokens, H, dtype=torch.bfloat16, device=self.device)
+        _require(grad_x, torch.bfloat16, "grad_x", self.device)
+        if grad_x.shape != (self.num_tokens, H):
+            raise ValueError("grad_x must be [num_tokens, H]")
+        ep_dispatch_backward(self._h, epoch, grad_pool, grad_x, stream)
+        return grad_x
 
     def borrow(self, x: torch.Tensor, stream=None) -> int:
         """Dispatch without a copy: lend x through the row map

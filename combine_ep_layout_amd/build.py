@@ -1,6 +1,8 @@
 """Build libep_layout.so (gfx950) in-tree with hipcc.
 
-    python -m combine_ep_layout_amd.build [-v] [-DNAME=VALUE ...] [-o OUT]
+    python combine_ep_layout_amd/build.py [-v] [-DNAME=VALUE ...] [-o OUT]
+
+(run as a script: importing the package would load the library it builds)
 
 Extra -D options override the kernels' compile-time tuning macros.
 """

@@ -295,6 +295,49 @@ ep_status ep_combine(const ep_handle* h, uint32_t epoch, const void* expert_out,
     return hip_status(epk::launch_combine(a, stream));
 }
 
+ep_status ep_combine_backward(const ep_handle* h, uint32_t epoch, const void* grad_y,
+                              const void* expert_out, int32_t hidden, void* grad_expert_out,
+                              float* grad_weights, hipStream_t stream) {
+    if (!h) return EP_ERR_INVALID_ARGUMENT;
+    if (hidden <= 0 || hidden % 8 != 0) return EP_ERR_INVALID_ARGUMENT;
+    if (hidden > kMaxHidden) return EP_ERR_UNSUPPORTED;
+    if (h->T < 0 || epoch != h->epoch || h->lease) return EP_ERR_HANDLE_STATE;
+    if (h->T > 0 && (!grad_y || !expert_out || !grad_expert_out || !grad_weights ||
+                     !aligned16(grad_y) || !aligned16(expert_out) ||
+                     !aligned16(grad_expert_out) || !aligned4(grad_weights)))
+        return EP_ERR_INVALID_ARGUMENT;
+    epk::CombineBwdArgs a;
+    a.grad_y = grad_y;
+    a.expert_out = expert_out;
+    a.T = h->T;
+    a.K = h->cfg.top_k;
+    a.H = hidden;
+    a.slot_to_row = h->slot_to_row;
+    a.weights = h->weights;
+    a.grad_eo = grad_expert_out;
+    a.grad_w = grad_weights;
+    return hip_status(epk::launch_combine_bwd(a, stream));
+}
+
+ep_status ep_dispatch_backward(const ep_handle* h, uint32_t epoch, const void* grad_pool,
+                               int32_t hidden, void* grad_x, hipStream_t stream) {
+    if (!h) return EP_ERR_INVALID_ARGUMENT;
+    if (hidden <= 0 || hidden % 8 != 0) return EP_ERR_INVALID_ARGUMENT;
+    if (hidden > kMaxHidden) return EP_ERR_UNSUPPORTED;
+    if (h->T < 0 || epoch != h->epoch || h->lease) return EP_ERR_HANDLE_STATE;
+    if (h->T > 0 && (!grad_pool || !grad_x || !aligned16(grad_pool) || !aligned16(grad_x)))
+        return EP_ERR_INVALID_ARGUMENT;
+    epk::CombineArgs a;
+    a.expert_out = grad_pool;
+    a.T = h->T;
+    a.K = h->cfg.top_k;
+    a.H = hidden;
+    a.slot_to_row = h->slot_to_row;
+    a.weights = nullptr;
+    a.y = grad_x;
+    return hip_status(epk::launch_combine_unit(a, stream));
+}
+
 ep_status ep_borrow_release(ep_handle* h, hipStream_t consumer_stream) {
     if (!h) return EP_ERR_INVALID_ARGUMENT;
     if (!h->lease) return EP_ERR_HANDLE_STATE;

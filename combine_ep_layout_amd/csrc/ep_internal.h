@@ -69,6 +69,18 @@ struct CombineArgs {
     void* y;
 };
 
+struct CombineBwdArgs {
+    const void* grad_y;         // bf16 [T, H]
+    const void* expert_out;     // bf16 [cap, H]
+    int32_t T;
+    int32_t K;
+    int32_t H;
+    const int32_t* slot_to_row;
+    const float* weights;
+    void* grad_eo;              // bf16 [cap, H], real rows written
+    float* grad_w;              // fp32 [T, K]
+};
+
 struct ConsumeArgs {
     const void* pool;
     const uint8_t* scales;
@@ -88,6 +100,9 @@ struct ConsumeArgs {
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
 hipError_t launch_dispatch(const DispatchArgs& a, bool fp8, bool tile_ready, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+// unit_weights: every unmasked slot weighs 1 (the backward of dispatch)
+hipError_t launch_combine_unit(const CombineArgs& a, hipStream_t stream);
+hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t stream);
 hipError_t launch_consume(const ConsumeArgs& a, int workgroups, hipStream_t stream);
 
 // Workgroups the multi-workgroup layout path needs for S slots.

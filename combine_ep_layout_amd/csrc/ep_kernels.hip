@@ -669,7 +669,7 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <int KT>
+template <int KT, bool UNIT>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a, int nseg, int ipb) {
     constexpr int U = EP_COMBINE_UNROLL;
     const int lane = threadIdx.x & (kWave - 1);
@@ -687,7 +687,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a, int nseg, int ip
 #pragma unroll
         for (int k = 0; k < KT; ++k) {
             rows[k] = (k < a.K) ? a.slot_to_row[t * a.K + k] : -1;
-            wt[k] = (k < a.K) ? a.weights[t * a.K + k] : 0.0f;
+            wt[k] = UNIT ? 1.0f : ((k < a.K) ? a.weights[t * a.K + k] : 0.0f);
         }
         const int c0 = seg * (kWave * U) + lane;
         u32x4 v[KT][U];
@@ -725,6 +725,81 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a, int nseg, int ip
             const int c = c0 + u * kWave;
             if (c < n16) store_row<EP_COMBINE_STORE>(dst, a.H * 2, c, o);
         }
+    }
+}
+
+// ----------------------------------------------------- combine backward ---
+
+#ifndef EP_BWD_UNROLL
+#define EP_BWD_UNROLL 2        // 16-byte chunks per lane in flight in combine backward
+#endif
+
+// Backward of the combine, one wave per token: grad_y[t] is read once; for
+// each unmasked slot the gradient row bf16(fp32(w * g)) is stored and the
+// exact bf16 x bf16 products are accumulated in double, per lane in ascending
+// chunk order and then across lanes by a fixed butterfly (lane 0's sum is
+// kept), then rounded once to float.
+template <int KT>
+__global__ __launch_bounds__(256) void k_combine_bwd(CombineBwdArgs a) {
+    constexpr int U = EP_BWD_UNROLL;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = uniform_i(threadIdx.x / kWave);
+    const int t = (int)blockIdx.x * 4 + w;
+    if (t >= a.T) return;
+    const int n16 = a.H / 8;
+    int rows[KT];
+    float wt[KT];
+    double acc[KT];
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+        rows[k] = (k < a.K) ? a.slot_to_row[t * a.K + k] : -1;
+        wt[k] = (k < a.K) ? a.weights[t * a.K + k] : 0.0f;
+        acc[k] = 0.0;
+    }
+    const u32x4* gy = (const u32x4*)a.grad_y + (int64_t)t * n16;
+    const u32x4* eo = (const u32x4*)a.expert_out;
+    u32x4* geo = (u32x4*)a.grad_eo;
+    for (int c0 = lane; c0 < n16; c0 += kWave * U) {
+        u32x4 g[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + u * kWave;
+            if (c < n16) g[u] = gy[c];
+        }
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+            if (rows[k] < 0) continue;
+            u32x4 o[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + u * kWave;
+                if (c < n16) o[u] = load_v<EP_COMBINE_NT_LOADS>(eo + (int64_t)rows[k] * n16 + c);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + u * kWave;
+                if (c >= n16) continue;
+                u32x4 q;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float g0 = __uint_as_float(g[u][i] << 16);
+                    const float g1 = __uint_as_float(g[u][i] & 0xFFFF0000u);
+                    const float o0 = __uint_as_float(o[u][i] << 16);
+                    const float o1 = __uint_as_float(o[u][i] & 0xFFFF0000u);
+                    q[i] = f32_to_bf16_rne(wt[k] * g0) | (f32_to_bf16_rne(wt[k] * g1) << 16);
+                    acc[k] = __builtin_fma((double)g0, (double)o0, acc[k]);
+                    acc[k] = __builtin_fma((double)g1, (double)o1, acc[k]);
+                }
+                store_row<EP_DISPATCH_STORE>(geo + (int64_t)rows[k] * n16, a.H * 2, c, q);
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+        double v = acc[k];
+#pragma unroll
+        for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
+        if (lane == 0 && k < a.K) a.grad_w[t * a.K + k] = rows[k] >= 0 ? (float)v : 0.0f;
     }
 }
 
@@ -836,14 +911,32 @@ hipError_t dispatch_kt(const DispatchArgs& a, bool fp8, bool stream, hipStream_t
     return hipGetLastError();
 }
 
-template <int KT>
+template <int KT, bool UNIT>
 hipError_t combine_kt(const CombineArgs& a, hipStream_t st) {
     const int per_seg = kWave * EP_COMBINE_UNROLL * 8;
     const int nseg = (a.H + per_seg - 1) / per_seg;
     const int ipb = items_per_block(nseg, false);
     const int64_t items = (int64_t)a.T * nseg;
     const int grid = (int)((items + ipb - 1) / ipb);
-    hipLaunchKernelGGL((k_combine<KT>), dim3(grid), dim3(256), 0, st, a, nseg, ipb);
+    hipLaunchKernelGGL((k_combine<KT, UNIT>), dim3(grid), dim3(256), 0, st, a, nseg, ipb);
+    return hipGetLastError();
+}
+
+template <bool UNIT>
+hipError_t combine_any(const CombineArgs& a, hipStream_t stream) {
+    if (a.T == 0) return hipSuccess;
+    if (a.K <= 1) return combine_kt<1, UNIT>(a, stream);
+    if (a.K <= 2) return combine_kt<2, UNIT>(a, stream);
+    if (a.K <= 4) return combine_kt<4, UNIT>(a, stream);
+    if (a.K <= 8) return combine_kt<8, UNIT>(a, stream);
+    if (a.K <= 16) return combine_kt<16, UNIT>(a, stream);
+    return combine_kt<32, UNIT>(a, stream);
+}
+
+template <int KT>
+hipError_t combine_bwd_kt(const CombineBwdArgs& a, hipStream_t st) {
+    const int grid = (a.T + 3) / 4;
+    hipLaunchKernelGGL((k_combine_bwd<KT>), dim3(grid), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
@@ -884,13 +977,21 @@ hipError_t launch_dispatch(const DispatchArgs& a, bool fp8, bool tile_ready, hip
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
+    return combine_any<false>(a, stream);
+}
+
+hipError_t launch_combine_unit(const CombineArgs& a, hipStream_t stream) {
+    return combine_any<true>(a, stream);
+}
+
+hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t stream) {
     if (a.T == 0) return hipSuccess;
-    if (a.K <= 1) return combine_kt<1>(a, stream);
-    if (a.K <= 2) return combine_kt<2>(a, stream);
-    if (a.K <= 4) return combine_kt<4>(a, stream);
-    if (a.K <= 8) return combine_kt<8>(a, stream);
-    if (a.K <= 16) return combine_kt<16>(a, stream);
-    return combine_kt<32>(a, stream);
+    if (a.K <= 1) return combine_bwd_kt<1>(a, stream);
+    if (a.K <= 2) return combine_bwd_kt<2>(a, stream);
+    if (a.K <= 4) return combine_bwd_kt<4>(a, stream);
+    if (a.K <= 8) return combine_bwd_kt<8>(a, stream);
+    if (a.K <= 16) return combine_bwd_kt<16>(a, stream);
+    return combine_bwd_kt<32>(a, stream);
 }
 
 hipError_t launch_consume(const ConsumeArgs& a, int workgroups, hipStream_t stream) {

@@ -164,6 +164,31 @@ ep_status ep_dispatch(ep_handle* h, const void* x, int32_t hidden, void* pool,
 ep_status ep_combine(const ep_handle* h, uint32_t epoch, const void* expert_out,
                      int32_t hidden, void* y, hipStream_t stream);
 
+/* Backward of ep_combine ([SEP] "What's in the box" names combine_grads; the
+ * values are the derivatives of [WEIGHTS]'s y_t = sum_k w_{t,k} o_{row(t,k)}).
+ *   epoch            the layout's epoch, else EP_ERR_HANDLE_STATE.
+ *   grad_y           device bf16 [num_tokens, hidden].
+ *   expert_out       device bf16 [capacity_rows, hidden] (combine's input).
+ *   grad_expert_out  device bf16 [capacity_rows, hidden]: row(t,k) gets
+ *                    bf16(fp32(w[t,k] * grad_y[t])); other rows untouched.
+ *   grad_weights     device fp32 [num_tokens, top_k]: the dot product
+ *                    <grad_y[t], expert_out[row(t,k)]> accumulated in double
+ *                    (bf16 x bf16 products are exact) and rounded once to
+ *                    float; 0 for masked slots.
+ * hidden % 8 == 0.  Rejected while a borrowed view is out. */
+ep_status ep_combine_backward(const ep_handle* h, uint32_t epoch, const void* grad_y,
+                              const void* expert_out, int32_t hidden, void* grad_expert_out,
+                              float* grad_weights, hipStream_t stream);
+
+/* Backward of a bf16 ep_dispatch ([SEP] names dispatch_grads): each pool row
+ * was a copy of its token's row, so
+ *   grad_x[t] = bf16( fp32 sum over unmasked k ascending of grad_pool[row(t,k)] )
+ * from +0 (a token with no unmasked slot gets +0); padding rows of grad_pool
+ * are never read.  grad_pool device bf16 [capacity_rows, hidden], grad_x
+ * device bf16 [num_tokens, hidden]; hidden % 8 == 0. */
+ep_status ep_dispatch_backward(const ep_handle* h, uint32_t epoch, const void* grad_pool,
+                               int32_t hidden, void* grad_x, hipStream_t stream);
+
 /* End the lease of a borrowing dispatch ([BORROW]).  consumer_stream is the
  * stream the consumers of the view were enqueued on; the handle's next call
  * waits (on its own stream) until that stream's work enqueued so far is done,
