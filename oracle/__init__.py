@@ -6,8 +6,9 @@ through ctypes and shares nothing with the HIP library.
 
 Pinned functions (each checked in ``tests/test_oracle_*.py`` against something
 other than itself): layout, bf16 dispatch, FP8 quantisation (scale exponent and
-e4m3fn codes), dequantisation, combine, combine and dispatch backward.  Nothing
-here is "parity unpinned".
+e4m3fn codes) in the UE8M0, float32 and power-of-two float32 scale flavours,
+the MN-major and packed scale layouts, dequantisation (cast back), combine,
+combine and dispatch backward.  Nothing here is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -65,6 +66,10 @@ def _load():
     lib.eo_f32_to_bf16_n.restype = None
     lib.eo_ue8m0_exponent_n.argtypes = [P, ctypes.c_int64, P]
     lib.eo_ue8m0_exponent_n.restype = None
+    lib.eo_quantize_row_f32scale.argtypes = [P, ctypes.c_int32, P, P]
+    lib.eo_quantize_row_f32scale.restype = None
+    lib.eo_dequant_row_f32scale.argtypes = [P, P, ctypes.c_int32, P]
+    lib.eo_dequant_row_f32scale.restype = None
     lib.eo_combine_backward.argtypes = [P, P, P, P, ctypes.c_int64, ctypes.c_int32,
                                         ctypes.c_int32, P, P]
     lib.eo_combine_backward.restype = None
@@ -136,6 +141,148 @@ def quantize_row(x_row: np.ndarray):
     s = np.empty(H // 128, dtype=np.uint8)
     _load().eo_quantize_row(_p(x_row), H, _p(q), _p(s))
     return q, s
+
+
+def quantize_row_f32scale(x_row: np.ndarray):
+    x_row = np.ascontiguousarray(x_row, dtype=np.uint16)
+    H = x_row.size
+    q = np.empty(H, dtype=np.uint8)
+    s = np.empty(H // 128, dtype=np.float32)
+    _load().eo_quantize_row_f32scale(_p(x_row), H, _p(q), _p(s))
+    return q, s
+
+
+def dequant_rows_f32scale(q: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    n, H = q.shape
+    out = np.empty((n, H), dtype=np.uint16)
+    lib = _load()
+    for i in range(n):
+        lib.eo_dequant_row_f32scale(_p(q[i]), _p(scales[i]), H, _p(out[i]))
+    return out
+
+
+def dispatch_fp8_f32scale(x: np.ndarray, recv_token: np.ndarray,
+                          pool_init: Optional[np.ndarray] = None,
+                          scales_init: Optional[np.ndarray] = None):
+    """FP8 dispatch with float32 scales: each real row holds its token's codes."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    recv = np.ascontiguousarray(recv_token, dtype=np.int32)
+    H = x.shape[1]
+    cap = recv.size
+    pool = (np.zeros((cap, H), np.uint8) if pool_init is None
+            else np.array(pool_init, dtype=np.uint8, copy=True, order="C"))
+    scales = (np.zeros((cap, H // 128), np.float32) if scales_init is None
+              else np.array(scales_init, dtype=np.float32, copy=True, order="C"))
+    for r in np.flatnonzero(recv >= 0):
+        pool[r], scales[r] = quantize_row_f32scale(x[recv[r]])
+    return pool, scales
+
+
+# ------------------------------------------------------ scale formats -------
+# The instagit page ("API Signature and Return Values") names three flavours
+# of the per-128-channel scale: use_ue8m0 (a UE8M0 exponent byte), round_scale
+# (a power-of-two scale kept as float32) and neither (a plain float32 scale).
+# Readings where the page is silent: round_scale uses the UE8M0 exponent rule,
+# so its codes equal the UE8M0 flavour's and its scale is the float 2^e; the
+# GEMM-friendly "MN-major" layout stores group g of row r at [g, r] with a
+# leading dimension ld >= rows, and UE8M0 bytes in that layout are packed four
+# groups to a 32-bit word, group 4w + j in byte j of word w (unused bytes 0).
+
+SCALE_UE8M0, SCALE_F32, SCALE_POW2_F32 = "ue8m0", "f32", "pow2_f32"
+
+
+def pow2_scales_from_ue8m0(scale_bytes: np.ndarray) -> np.ndarray:
+    """Float32 value 2^(byte - 127) of each UE8M0 byte (2^-127 is a float32 subnormal)."""
+    e = scale_bytes.astype(np.int64) - 127
+    return np.ldexp(np.float64(1.0), e).astype(np.float32)
+
+
+def scale_words(groups: int) -> int:
+    """32-bit words per row of packed UE8M0 scales."""
+    return (groups + 3) // 4
+
+
+def scales_to_mn_major(scales: np.ndarray, ld: int, init: Optional[np.ndarray] = None,
+                       rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Row-major scales [n, G] -> MN-major.  float32 scales give float32 [G, ld];
+    UE8M0 bytes give packed uint32 [ceil(G/4), ld].  Only the columns listed in
+    `rows` (all n by default) are written; the rest keep `init` (zeros)."""
+    n, G = scales.shape
+    packed = scales.dtype == np.uint8
+    nw = scale_words(G)
+    shape = (nw, ld) if packed else (G, ld)
+    dtype = np.uint32 if packed else np.float32
+    out = np.zeros(shape, dtype) if init is None else np.array(init, dtype=dtype, copy=True)
+    assert out.shape == shape
+    rows = np.arange(n) if rows is None else rows
+    for r in rows:
+        if packed:
+            for w in range(nw):
+                word = 0
+                for j in range(4):
+                    g = 4 * w + j
+                    if g < G:
+                        word |= int(scales[r, g]) << (8 * j)
+                out[w, r] = word
+        else:
+            out[:, r] = scales[r, :]
+    return out
+
+
+def scales_from_mn_major(mn: np.ndarray, n: int, groups: int) -> np.ndarray:
+    """Inverse of scales_to_mn_major for the first n columns."""
+    if mn.dtype == np.uint32:
+        out = np.zeros((n, groups), np.uint8)
+        for r in range(n):
+            for g in range(groups):
+                out[r, g] = (int(mn[g // 4, r]) >> (8 * (g % 4))) & 0xFF
+        return out
+    return np.ascontiguousarray(mn[:, :n].T.astype(np.float32))
+
+
+def dispatch_fp8_scaled(x: np.ndarray, recv_token: np.ndarray, kind: str, mn_major: bool = False,
+                        ld: Optional[int] = None, pool_init: Optional[np.ndarray] = None,
+                        scales_init: Optional[np.ndarray] = None):
+    """FP8 dispatch in any scale flavour and layout.  Real rows hold their
+    token's codes and scales; padding rows (and MN-major columns past the pool)
+    keep their initial contents."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    recv = np.ascontiguousarray(recv_token, dtype=np.int32)
+    H = x.shape[1]
+    G = H // 128
+    cap = recv.size
+    real = np.flatnonzero(recv >= 0)
+    pool = (np.zeros((cap, H), np.uint8) if pool_init is None
+            else np.array(pool_init, dtype=np.uint8, copy=True, order="C"))
+    rm = np.zeros((cap, G), np.uint8 if kind == SCALE_UE8M0 else np.float32)
+    for r in real:
+        if kind == SCALE_F32:
+            pool[r], rm[r] = quantize_row_f32scale(x[recv[r]])
+        else:
+            q, b = quantize_row(x[recv[r]])
+            pool[r] = q
+            rm[r] = b if kind == SCALE_UE8M0 else pow2_scales_from_ue8m0(b)
+    if mn_major:
+        scales = scales_to_mn_major(rm, ld if ld is not None else cap, scales_init, rows=real)
+    else:
+        scales = (np.zeros_like(rm) if scales_init is None
+                  else np.array(scales_init, dtype=rm.dtype, copy=True, order="C"))
+        scales[real] = rm[real]
+    return pool, scales
+
+
+def cast_back(q: np.ndarray, scales: np.ndarray, kind: str, mn_major: bool = False) -> np.ndarray:
+    """bf16 rows from e4m3fn codes [n, H] and their scales (per_token_cast_back
+    on the instagit page): UE8M0 and power-of-two scales are exact powers of
+    two, float32 scales use one float product; both round once to bf16."""
+    n, H = q.shape
+    G = H // 128
+    rm = scales_from_mn_major(scales, n, G) if mn_major else scales
+    if kind == SCALE_UE8M0:
+        return dequant_rows(q, rm)
+    return dequant_rows_f32scale(q, rm.astype(np.float32))
 
 
 def dequant_rows(q: np.ndarray, scales: np.ndarray) -> np.ndarray:

@@ -37,7 +37,9 @@
  *     amax <= 448 * 2^e (e = 127 when none is), byte e + 127;
  *   - e4m3fn code = nearest finite code to |v|, ties to the even code, sign
  *     kept (-0 -> 0x80); |v| >= 448 gives 0x7E (only reachable from an
- *     infinite input), NaN gives 0x7F.
+ *     infinite input), NaN gives 0x7F;
+ *   - float32 scales (no UE8M0): amax floored at 448 * 2^-126, s = amax/448,
+ *     codes of float(x * (448/amax)), see eo_quantize_row_f32scale.
  */
 #include <math.h>
 #include <stdint.h>
@@ -374,5 +376,64 @@ void eo_dispatch_backward(const uint16_t* grad_pool, const int32_t* slot_to_row,
             }
             grad_x[t * H + c] = eo_f32_to_bf16(acc);
         }
+    }
+}
+
+/* ------------------------------------------------- FP8 with fp32 scales --- */
+
+/* Quantisation with a float32 scale per 128-channel group: the use_ue8m0 =
+ * false, round_scale = false flavour of the instagit page ("API Signature and
+ * Return Values", "FP8 and Quantization Support").  The pages give no rule;
+ * the reading is the usual amax scaling, all in float32:
+ *   a      = max(amax, 448 * 2^-126)   (keeps s a normal float, f finite)
+ *   s      = a / 448                   (the stored scale; x ~ value(q) * s)
+ *   f      = 448 / a                   (the quantisation factor)
+ *   q      = nearest e4m3fn code of float(x * f), ties to even, saturating
+ *            at 448; a NaN product (NaN x, or infinite x times f = 0) gives
+ *            0x7F with the sign of x. */
+void eo_quantize_row_f32scale(const uint16_t* x, int32_t H, uint8_t* q, float* scales)
+{
+    const float floor_amax = 448.0f * 0x1p-126f;
+    for (int32_t g = 0; g < H / 128; ++g) {
+        float amax = 0.0f;
+        for (int c = 0; c < 128; ++c) {
+            float a = fabsf(eo_bf16_to_f32(x[g * 128 + c]));
+            if (a > amax)                /* NaN never compares greater */
+                amax = a;
+        }
+        float a = amax > floor_amax ? amax : floor_amax;
+        float s = a / 448.0f;
+        float f = 448.0f / a;
+        scales[g] = s;
+        for (int c = 0; c < 128; ++c) {
+            float xv = eo_bf16_to_f32(x[g * 128 + c]);
+            float v = xv * f;
+            uint8_t code;
+            if (isnan(v))
+                code = 0x7F;
+            else
+                code = eo_e4m3_encode(fabs((double)v));
+            if (signbit(xv))
+                code |= 0x80;
+            q[g * 128 + c] = code;
+        }
+    }
+}
+
+/* Inverse for float32 scales: bf16(float(value(q) * s)), one float product
+ * rounded to nearest even in bf16; NaN codes give a quiet NaN with their sign. */
+void eo_dequant_row_f32scale(const uint8_t* q, const float* scales, int32_t H, uint16_t* out)
+{
+    for (int32_t c = 0; c < H; ++c) {
+        uint8_t b = q[c];
+        if ((b & 0x7F) == 0x7F) {
+            out[c] = (uint16_t)((b & 0x80 ? 0x8000 : 0) | 0x7FC0);
+            continue;
+        }
+        float v = (float)eo_e4m3_value(b & 0x7F);
+        if (b & 0x80)
+            v = -v;
+        float p = v * scales[c / 128];
+        out[c] = eo_f32_to_bf16(p);
     }
 }

@@ -166,3 +166,148 @@ def test_quantize_roundtrip_on_e4m3_grid():
     q, s = oracle.quantize_row(x)
     assert int(s[0]) - 127 == -3
     assert np.array_equal(oracle.dequant_rows(q[None, :], s[None, :])[0], x)
+
+
+# ---------------------------------------------- float32-scale flavour -------
+# Reading (the pages name use_ue8m0 = False without a rule): a = max(amax,
+# 448 * 2^-126), s = a / 448, codes = e4m3fn(float(x * (448 / a))), all in
+# float32.  Pinned against torch's float32 arithmetic and its float8_e4m3fn
+# cast, and by the quantisation error bound.
+
+FLOOR = np.float32(448.0) * np.float32(2.0 ** -126)
+
+
+def _torch_f32scale(xf):
+    a = np.maximum(np.where(np.isnan(xf), 0, np.abs(xf)).max(1), FLOOR).astype(np.float32)  # NaN takes no part
+    s = (a / np.float32(448.0)).astype(np.float32)
+    f = torch.from_numpy((np.float32(448.0) / a).astype(np.float32))
+    v = torch.from_numpy(xf) * f[:, None]                    # float32 products
+    nan = torch.isnan(v)
+    v = torch.clamp(v.abs(), max=448.0)                      # torch's cast does not saturate
+    q = v.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    q[nan.numpy()] = 0x7F
+    q |= np.where(np.signbit(xf), 0x80, 0).astype(np.uint8)
+    return q.ravel(), s
+
+
+def test_f32scale_quantize_matches_torch():
+    rng = np.random.default_rng(12)
+    H = 1024
+    for trial in range(24):
+        x32 = (rng.standard_normal(H) * 2.0 ** rng.integers(-40, 40)).astype(np.float32)
+        if trial == 0:
+            x32[:128] = 0.0                     # an all-zero group: floor scale, codes +-0
+            x32[64] = -0.0
+        if trial == 1:
+            x32[128:256] *= np.float32(2.0 ** -100)   # amax below the floor
+            x32[300] = np.inf                   # an infinite amax: factor 0, inf * 0 is NaN
+            x32[301] = np.nan
+            x32[513] = -np.inf
+        x = bf16_from_f32(x32)
+        q, s = oracle.quantize_row_f32scale(x)
+        want_q, want_s = _torch_f32scale(bf16_to_f32(x).reshape(-1, 128))
+        assert np.array_equal(s, want_s)
+        assert np.array_equal(q, want_q), trial
+
+
+def test_f32scale_dequant_and_error_bound():
+    rng = np.random.default_rng(13)
+    H = 512
+    x = bf16_from_f32(rng.standard_normal(H).astype(np.float32))
+    q, s = oracle.quantize_row_f32scale(x)
+    deq = oracle.dequant_rows_f32scale(q[None, :], s[None, :])[0]
+    val = torch.from_numpy(q.copy()).view(torch.float8_e4m3fn).float()
+    want = (val.reshape(-1, 128) * torch.from_numpy(s)[:, None]).reshape(-1).to(torch.bfloat16)
+    assert np.array_equal(deq, want.view(torch.int16).numpy().view(np.uint16))
+    xf = bf16_to_f32(x).astype(np.float64)
+    df = bf16_to_f32(deq).astype(np.float64)
+    s_c = np.repeat(s.astype(np.float64), 128)
+    normal = np.abs(xf) / s_c >= 2.0 ** -6
+    # e4m3 half-ulp 2^-4 relative, the bf16 half-ulp 2^-9, float roundings
+    assert np.all(np.abs(df - xf)[normal] <= (2.0 ** -4 + 2.0 ** -8) * np.abs(xf)[normal])
+    assert np.all(np.abs(df - xf)[~normal] <= 2.0 ** -10 * s_c[~normal] * 1.01 + 2.0 ** -8 * np.abs(xf)[~normal])
+    # NaN codes come back as quiet NaNs with their sign
+    nanq = np.array([0x7F, 0xFF] + [0] * 126, np.uint8)
+    back = oracle.dequant_rows_f32scale(nanq[None, :], np.ones((1, 1), np.float32))[0]
+    assert back[0] == 0x7FC0 and back[1] == 0xFFC0
+
+
+# ------------------------------------------- power-of-two float32 scales ----
+
+def test_pow2_scale_closed_form_and_codes():
+    """round_scale without UE8M0: s = 2^e with e = ceil(log2(amax / 448)) in
+    [-127, 127] (closed form via frexp), codes = torch's cast of x * 2^-e."""
+    rng = np.random.default_rng(14)
+    H = 1024
+    x32 = (rng.standard_normal(H) * np.repeat(2.0 ** rng.integers(-135, 120, H // 128), 128)).astype(np.float32)
+    x32[:128] = 0.0
+    x = bf16_from_f32(x32)
+    recv = np.array([0], np.int32)
+    pool, s = oracle.dispatch_fp8_scaled(x[None, :], recv, oracle.SCALE_POW2_F32)
+    xf = bf16_to_f32(x).reshape(-1, 128).astype(np.float64)
+    amax = np.abs(xf).max(1)
+    m, ex = np.frexp(amax / 448.0)                        # amax/448 exact in float64
+    e = np.where(m == 0.5, ex - 1, ex)                    # ceil(log2(.)) of m * 2^ex
+    e = np.clip(np.where(amax == 0, -127, e), -127, 127)
+    assert np.array_equal(s[0], np.ldexp(1.0, e).astype(np.float32))
+    v = (xf * np.ldexp(1.0, -e)[:, None]).astype(np.float32)   # exact power-of-two scaling
+    assert np.array_equal(pool[0], _torch_e4m3(v.ravel()))
+
+
+# ----------------------------------------------------- MN-major layouts ------
+
+def test_mn_major_layouts_by_memory_view():
+    """MN-major float scales are the transpose; packed UE8M0 words, read as
+    little-endian bytes, are the row's group bytes four at a time."""
+    rng = np.random.default_rng(15)
+    n, G, ld = 7, 11, 12
+    b = rng.integers(0, 256, size=(n, G), dtype=np.uint8)
+    words = oracle.scales_to_mn_major(b, ld)
+    assert words.shape == (3, ld) and words.dtype == np.uint32
+    as_bytes = words.astype("<u4").view(np.uint8).reshape(3, ld, 4)     # [w, r, j]
+    want = np.zeros((n, 12), np.uint8)
+    want[:, :G] = b
+    assert np.array_equal(as_bytes[:, :n, :].transpose(1, 0, 2).reshape(n, 12), want)
+    assert (words[:, n:] == 0).all()
+    assert np.array_equal(oracle.scales_from_mn_major(words, n, G), b)
+    f = rng.standard_normal((n, G)).astype(np.float32)
+    mn = oracle.scales_to_mn_major(f, ld)
+    assert np.array_equal(mn[:, :n], f.T) and (mn[:, n:] == 0).all()
+    assert np.array_equal(oracle.scales_from_mn_major(mn, n, G), f)
+
+
+def test_scaled_dispatch_untouched_rows_and_cast_back():
+    rng = np.random.default_rng(16)
+    T, H = 5, 384
+    x = bf16_from_f32((rng.standard_normal((T, H)) * 3).astype(np.float32))
+    recv = np.array([2, -1, 0, 4, -1, 1, 3, -1], np.int32)
+    real = recv >= 0
+    for kind in (oracle.SCALE_UE8M0, oracle.SCALE_F32, oracle.SCALE_POW2_F32):
+        p_rm, s_rm = oracle.dispatch_fp8_scaled(x, recv, kind)
+        for mn in (False, True):
+            packed = mn and kind == oracle.SCALE_UE8M0
+            shape = ((1, 9) if packed else (3, 9)) if mn else (8, 3)
+            init = np.full(shape, 0xA5A5A5A5 if packed else 0xA5,
+                           np.uint32 if packed else (np.uint8 if kind == "ue8m0" else np.float32))
+            p, s = oracle.dispatch_fp8_scaled(x, recv, kind, mn, ld=9, pool_init=np.full((8, H), 0x5A, np.uint8),
+                                              scales_init=init)
+            assert np.array_equal(p[real], p_rm[real]) and (p[~real] == 0x5A).all()
+            if mn:
+                cols = np.flatnonzero(real)
+                assert np.array_equal(oracle.scales_from_mn_major(s, 8, 3)[real], s_rm[real])
+                untouched = np.setdiff1d(np.arange(9), cols)
+                assert np.array_equal(s[:, untouched], init[:, untouched])
+            else:
+                assert np.array_equal(s[real], s_rm[real]) and np.array_equal(s[~real], init[~real])
+            back = oracle.cast_back(p[real], s_rm[real], kind)
+            # the error bound ties the three flavours to the source rows
+            src = bf16_to_f32(x[recv[real]]).astype(np.float64)
+            got = bf16_to_f32(back).astype(np.float64)
+            assert np.all(np.abs(got - src) <= 2.0 ** -4 * np.abs(src) + 2.0 ** -9 * np.abs(src) +
+                          np.abs(src).max(1, keepdims=True) * 2.0 ** -15)
+    # UE8M0 and power-of-two float scales decode to the same rows
+    p8, s8 = oracle.dispatch_fp8_scaled(x, recv, oracle.SCALE_UE8M0)
+    p2, s2 = oracle.dispatch_fp8_scaled(x, recv, oracle.SCALE_POW2_F32)
+    assert np.array_equal(p8, p2)
+    assert np.array_equal(oracle.cast_back(p8[real], s8[real], "ue8m0"),
+                          oracle.cast_back(p2[real], s2[real], "pow2_f32"))
