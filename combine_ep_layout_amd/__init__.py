@@ -35,6 +35,17 @@ EP_DISPATCH_FP8 = 1 << 0
 EP_DISPATCH_TILE_READY = 1 << 1
 EP_DISPATCH_BORROW = 1 << 2
 EP_CONSUME_GATHER = 1 << 3
+EP_SCALE_F32 = 1 << 4
+EP_SCALE_ROUND = 1 << 5
+EP_SCALE_MN_MAJOR = 1 << 6
+EP_CONSUME_SIGNAL_DONE = 1 << 7
+
+# scale flavours by name: flags, element dtype
+SCALE_KINDS = {
+    "ue8m0": (0, torch.uint8),
+    "f32": (EP_SCALE_F32, torch.float32),
+    "pow2_f32": (EP_SCALE_F32 | EP_SCALE_ROUND, torch.float32),
+}
 
 ARRAYS = {
     "expert_counts": (0, torch.int32),
@@ -47,6 +58,7 @@ ARRAYS = {
     "slot_to_pool_row": (7, torch.int32),
     "pool_recv_token": (8, torch.int32),
     "topk_weights": (9, torch.float32),
+    "y_done_per_token": (10, torch.int32),
 }
 
 EXPORTS = [
@@ -54,7 +66,7 @@ EXPORTS = [
     "ep_num_tokens", "ep_layout", "ep_dispatch", "ep_combine", "ep_handle_get_view",
     "ep_array_bytes", "ep_copy_array", "ep_counts_to_host", "ep_handle_sync_status",
     "ep_tile_consume", "ep_status_string", "ep_borrow_release", "ep_combine_backward",
-    "ep_dispatch_backward",
+    "ep_dispatch_backward", "ep_combine_gated", "ep_fp8_cast_back", "ep_scale_ld",
 ]
 
 
@@ -95,6 +107,9 @@ def _load() -> ctypes.CDLL:
         "ep_borrow_release": (st, [P, P]),
         "ep_combine_backward": (st, [P, U32, P, P, I32, P, P, P]),
         "ep_dispatch_backward": (st, [P, U32, P, I32, P, P]),
+        "ep_combine_gated": (st, [P, U32, P, I32, P, U32, U32, P]),
+        "ep_fp8_cast_back": (st, [P, P, U32, I64, I64, I32, P, P]),
+        "ep_scale_ld": (I64, [P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -167,6 +182,56 @@ def ep_combine(h, epoch: int, expert_out: torch.Tensor, y: torch.Tensor, stream=
                            _stream(stream)), "ep_combine")
 
 
+def ep_combine_gated(h, epoch: int, expert_out: torch.Tensor, y: torch.Tensor, round: int,
+                     spin_limit_us: int, stream=None) -> None:
+    _check(_lib.ep_combine_gated(h, epoch, _ptr(expert_out), expert_out.shape[1], _ptr(y), round,
+                                 spin_limit_us, _stream(stream)), "ep_combine_gated")
+
+
+def ep_fp8_cast_back(q: torch.Tensor, scales: torch.Tensor, flags: int, rows: int, scale_ld: int,
+                     out: torch.Tensor, stream=None) -> None:
+    _check(_lib.ep_fp8_cast_back(_ptr(q), _ptr(scales), flags, rows, scale_ld, q.shape[1], _ptr(out),
+                                 _stream(stream)), "ep_fp8_cast_back")
+
+
+def scale_shape(rows: int, hidden: int, kind: str, mn_major: bool, ld: Optional[int] = None):
+    """Shape and dtype of a scale array for `rows` pool rows."""
+    _, dtype = SCALE_KINDS[kind]
+    G = hidden // 128
+    if not mn_major:
+        return (rows, G), dtype
+    ld = rows if ld is None else ld
+    if kind == "ue8m0":
+        return ((G + 3) // 4, ld), torch.int32      # packed words
+    return (G, ld), dtype
+
+
+def scale_flags(kind: str, mn_major: bool) -> int:
+    return SCALE_KINDS[kind][0] | (EP_SCALE_MN_MAJOR if mn_major else 0)
+
+
+def cast_back(q: torch.Tensor, scales: torch.Tensor, kind: str = "ue8m0", mn_major: bool = False,
+              rows: Optional[int] = None, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """per_token_cast_back: bf16 [rows, H] from e4m3fn codes and their scales."""
+    if q.dtype != torch.uint8 or not q.is_contiguous() or q.dim() != 2:
+        raise TypeError("q must be a contiguous uint8 [rows, hidden] tensor")
+    rows = q.shape[0] if rows is None else int(rows)
+    H = q.shape[1]
+    if rows > q.shape[0]:
+        raise ValueError("rows exceeds q")
+    shape, dtype = scale_shape(rows, H, kind, mn_major, scales.shape[1] if mn_major else None)
+    if scales.dtype != dtype or not scales.is_contiguous() or scales.shape[0] != shape[0] \
+            or scales.shape[1] < shape[1]:
+        raise ValueError(f"scales must be {dtype} {shape}")
+    if out is None:
+        out = torch.empty(rows, H, dtype=torch.bfloat16, device=q.device)
+    if out.dtype != torch.bfloat16 or not out.is_contiguous() or out.shape[0] < rows or out.shape[1] != H:
+        raise ValueError("out must be bf16 [rows, hidden]")
+    ld = scales.shape[1] if mn_major else 0
+    ep_fp8_cast_back(q, scales, scale_flags(kind, mn_major), rows, ld, out, stream)
+    return out
+
+
 def ep_tile_consume(h, seq: int, pool: torch.Tensor, pool_scales: Optional[torch.Tensor],
                     hidden: int, flags: int, out: torch.Tensor, workgroups: int,
                     spin_limit_us: int, stream=None) -> None:
@@ -208,6 +273,7 @@ class EpHandle:
         self._h = ep_handle_create(max_tokens, top_k, num_experts, block_m)
         self.capacity_rows = int(_lib.ep_pool_capacity_rows(self._h))
         self.max_tiles = int(_lib.ep_max_tiles(self._h))
+        self.scale_ld = int(_lib.ep_scale_ld(self._h))
 
     @property
     def raw(self):
@@ -235,14 +301,20 @@ class EpHandle:
             raise ValueError("topk_idx / topk_weights must both be [num_tokens, top_k]")
         return ep_layout(self._h, topk_idx, topk_weights, stream)
 
-    def new_pool(self, hidden: int, fp8: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    def scale_shape(self, hidden: int, kind: str = "ue8m0", mn_major: bool = False):
+        return scale_shape(self.capacity_rows, hidden, kind, mn_major, self.scale_ld)
+
+    def new_pool(self, hidden: int, fp8: bool = False, scale_kind: str = "ue8m0",
+                 mn_major: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
         if fp8:
+            shape, dtype = self.scale_shape(hidden, scale_kind, mn_major)
             return (torch.empty(self.capacity_rows, hidden, dtype=torch.uint8, device=self.device),
-                    torch.empty(self.capacity_rows, hidden // 128, dtype=torch.uint8, device=self.device))
+                    torch.empty(shape, dtype=dtype, device=self.device))
         return torch.empty(self.capacity_rows, hidden, dtype=torch.bfloat16, device=self.device), None
 
     def dispatch(self, x: torch.Tensor, pool: torch.Tensor, pool_scales: Optional[torch.Tensor] = None,
-                 fp8: bool = False, tile_ready: bool = False, stream=None) -> int:
+                 fp8: bool = False, tile_ready: bool = False, stream=None,
+                 scale_kind: str = "ue8m0", mn_major: bool = False) -> int:
         _require(x, torch.bfloat16, "x", self.device)
         if x.dim() != 2 or x.shape[0] != self.num_tokens:
             raise ValueError("x must be [num_tokens of the layout, hidden]")
@@ -251,10 +323,14 @@ class EpHandle:
             raise ValueError(f"pool must be at least [{self.capacity_rows}, {H}]")
         _require(pool, torch.uint8 if fp8 else torch.bfloat16, "pool", self.device)
         if fp8:
-            if pool_scales is None or pool_scales.shape[0] < self.capacity_rows or pool_scales.shape[1] != H // 128:
-                raise ValueError(f"pool_scales must be at least [{self.capacity_rows}, {H // 128}]")
-            _require(pool_scales, torch.uint8, "pool_scales", self.device)
-        flags = (EP_DISPATCH_FP8 if fp8 else 0) | (EP_DISPATCH_TILE_READY if tile_ready else 0)
+            shape, dtype = self.scale_shape(H, scale_kind, mn_major)
+            if pool_scales is None or tuple(pool_scales.shape) != shape:
+                raise ValueError(f"pool_scales must be {shape}")
+            _require(pool_scales, dtype, "pool_scales", self.device)
+        elif scale_kind != "ue8m0" or mn_major:
+            raise ValueError("scale flavours apply to FP8 dispatch only")
+        flags = (EP_DISPATCH_FP8 | scale_flags(scale_kind, mn_major) if fp8 else 0) | \
+                (EP_DISPATCH_TILE_READY if tile_ready else 0)
         return ep_dispatch(self._h, x, pool, pool_scales if fp8 else None, flags, stream)
 
     def combine_backward(self, epoch: int, grad_y: torch.Tensor, expert_out: torch.Tensor,
@@ -314,9 +390,27 @@ class EpHandle:
         ep_combine(self._h, epoch, expert_out, y, stream)
         return y
 
+    def combine_gated(self, epoch: int, expert_out: torch.Tensor, round: int = 1,
+                      y: Optional[torch.Tensor] = None, spin_limit_us: int = 2_000_000,
+                      stream=None) -> torch.Tensor:
+        """combine behind the per-token gate: token t waits until
+        y_done_per_token[t] >= round * (its unmasked slots)."""
+        _require(expert_out, torch.bfloat16, "expert_out", self.device)
+        H = expert_out.shape[1]
+        if expert_out.shape[0] < self.capacity_rows:
+            raise ValueError(f"expert_out must have at least {self.capacity_rows} rows")
+        if y is None:
+            y = torch.empty(max(self.num_tokens, 0), H, dtype=torch.bfloat16, device=self.device)
+        _require(y, torch.bfloat16, "y", self.device)
+        if y.shape != (self.num_tokens, H):
+            raise ValueError("y must be [num_tokens of the layout, hidden]")
+        ep_combine_gated(self._h, epoch, expert_out, y, round, spin_limit_us, stream)
+        return y
+
     def tile_consume(self, seq: int, pool: torch.Tensor, pool_scales: Optional[torch.Tensor],
                      hidden: int, out: torch.Tensor, fp8: bool = False, workgroups: int = 32,
-                     spin_limit_us: int = 2_000_000, stream=None, gather: bool = False) -> None:
+                     spin_limit_us: int = 2_000_000, stream=None, gather: bool = False,
+                     signal_done: bool = False) -> None:
         _require(out, torch.bfloat16, "out", self.device)
         if out.shape[0] < self.capacity_rows or out.shape[1] != hidden:
             raise ValueError("out must be at least [capacity_rows, hidden]")
@@ -327,7 +421,8 @@ class EpHandle:
                 raise ValueError("the gathered slab must be [num_tokens, hidden]")
         elif pool.shape[0] < self.capacity_rows:
             raise ValueError("pool must have at least capacity_rows rows")
-        flags = (EP_DISPATCH_FP8 if fp8 else 0) | (EP_CONSUME_GATHER if gather else 0)
+        flags = (EP_DISPATCH_FP8 if fp8 else 0) | (EP_CONSUME_GATHER if gather else 0) | \
+                (EP_CONSUME_SIGNAL_DONE if signal_done else 0)
         ep_tile_consume(self._h, seq, pool, pool_scales if fp8 else None, hidden, flags, out,
                         workgroups, spin_limit_us, stream)
 

@@ -32,6 +32,8 @@ FLAGS = [
     "-fno-gpu-flush-denormals-to-zero",
     # the combine's fused multiply-adds are explicit; nothing else is contracted
     "-ffp-contract=off",
+    # float32 division is IEEE (the FP8 float32-scale flavour divides)
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Wall",
     "-Wno-unused-variable",
     "-Wno-unused-parameter",

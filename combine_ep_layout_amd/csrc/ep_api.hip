@@ -32,6 +32,7 @@ struct ep_handle {
     uint32_t* error;
     int32_t* ws;
     uint32_t* done;
+    uint32_t* y_done;         // per-token done counts of the combine gate
     // host state of the current layout
     int32_t T;                // tokens of the current layout, -1 before the first
     uint32_t epoch;
@@ -54,6 +55,21 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+constexpr uint32_t kScaleFlags = EP_SCALE_F32 | EP_SCALE_ROUND | EP_SCALE_MN_MAJOR;
+
+// Scale flavour chosen by the EP_SCALE_* flags.
+int32_t scale_kind(uint32_t flags) {
+    if (!(flags & EP_SCALE_F32)) return epk::kScaleUe8m0;
+    return (flags & EP_SCALE_ROUND) ? epk::kScalePow2F32 : epk::kScaleF32;
+}
+
+// Alignment the scale array needs: floats and packed words are 4 bytes.
+bool scales_aligned(const void* p, uint32_t flags) {
+    return (flags & (EP_SCALE_F32 | EP_SCALE_MN_MAJOR)) ? aligned4(p) : true;
+}
+
+int64_t scale_ld_of(int64_t cap) { return (cap + 3) / 4 * 4; }
 
 ep_status check_config(const ep_config* c) {
     if (!c) return EP_ERR_INVALID_ARGUMENT;
@@ -137,6 +153,7 @@ ep_status ep_handle_create(const ep_config* cfg, ep_handle** out) {
         {(void**)&h->error, sizeof(uint32_t)},
         {(void**)&h->ws, sizeof(int32_t) * (size_t)h->ws_blocks * E},
         {(void**)&h->done, sizeof(uint32_t)},
+        {(void**)&h->y_done, sizeof(uint32_t) * (size_t)cfg->max_tokens},
     };
     size_t total = 0;
     for (const Part& p : parts) total += round_up(p.bytes ? p.bytes : 1, 256);
@@ -182,6 +199,8 @@ int32_t ep_max_tiles(const ep_handle* h) { return h ? h->max_tiles : -1; }
 
 int32_t ep_num_tokens(const ep_handle* h) { return h ? h->T : -1; }
 
+int64_t ep_scale_ld(const ep_handle* h) { return h ? scale_ld_of(h->cap) : -1; }
+
 ep_status ep_layout(ep_handle* h, const int32_t* topk_idx, const float* topk_weights,
                     int32_t num_tokens, hipStream_t stream, uint32_t* epoch_out) {
     if (!h || num_tokens < 0 || num_tokens > h->cfg.max_tokens) return EP_ERR_INVALID_ARGUMENT;
@@ -191,7 +210,7 @@ ep_status ep_layout(ep_handle* h, const int32_t* topk_idx, const float* topk_wei
     if (h->lease) return EP_ERR_HANDLE_STATE;
     ep_status ws = wait_lease(h, stream);
     if (ws != EP_OK) return ws;
-    epk::LayoutArgs a;
+    epk::LayoutArgs a{};
     a.topk_idx = topk_idx;
     a.topk_w = topk_weights;
     a.S = num_tokens * h->cfg.top_k;
@@ -212,6 +231,7 @@ ep_status ep_layout(ep_handle* h, const int32_t* topk_idx, const float* topk_wei
     a.error = h->error;
     a.ws = h->ws;
     a.done = h->done;
+    a.y_done = h->y_done;
     ep_status st = hip_status(epk::launch_layout(a, stream));
     if (st != EP_OK) return st;
     h->T = num_tokens;
@@ -222,12 +242,13 @@ ep_status ep_layout(ep_handle* h, const int32_t* topk_idx, const float* topk_wei
 }
 
 ep_status ep_dispatch(ep_handle* h, const void* x, int32_t hidden, void* pool,
-                      uint8_t* pool_scales, uint32_t flags, hipStream_t stream,
+                      void* pool_scales, uint32_t flags, hipStream_t stream,
                       uint32_t* seq_out) {
     if (!h) return EP_ERR_INVALID_ARGUMENT;
-    if (flags & ~(EP_DISPATCH_FP8 | EP_DISPATCH_TILE_READY | EP_DISPATCH_BORROW))
+    if (flags & ~(EP_DISPATCH_FP8 | EP_DISPATCH_TILE_READY | EP_DISPATCH_BORROW | kScaleFlags))
         return EP_ERR_INVALID_ARGUMENT;
     const bool fp8 = (flags & EP_DISPATCH_FP8) != 0;
+    if (!fp8 && (flags & kScaleFlags)) return EP_ERR_INVALID_ARGUMENT;
     const bool ready = (flags & EP_DISPATCH_TILE_READY) != 0;
     if (hidden <= 0 || hidden % 8 != 0) return EP_ERR_INVALID_ARGUMENT;
     if (hidden > kMaxHidden) return EP_ERR_UNSUPPORTED;
@@ -242,14 +263,15 @@ ep_status ep_dispatch(ep_handle* h, const void* x, int32_t hidden, void* pool,
         if (seq_out) *seq_out = h->seq;
         return EP_OK;
     }
-    if (fp8 && (hidden % 128 != 0 || !pool_scales)) return EP_ERR_INVALID_ARGUMENT;
+    if (fp8 && (hidden % 128 != 0 || !pool_scales || !scales_aligned(pool_scales, flags)))
+        return EP_ERR_INVALID_ARGUMENT;
     if (!fp8 && pool_scales) return EP_ERR_INVALID_ARGUMENT;
     if (h->T < 0 || h->lease) return EP_ERR_HANDLE_STATE;
     if (h->T > 0 && (!x || !pool || !aligned16(x) || !aligned16(pool)))
         return EP_ERR_INVALID_ARGUMENT;
     ep_status ws = wait_lease(h, stream);
     if (ws != EP_OK) return ws;
-    epk::DispatchArgs a;
+    epk::DispatchArgs a{};
     a.x = x;
     a.T = h->T;
     a.K = h->cfg.top_k;
@@ -261,6 +283,9 @@ ep_status ep_dispatch(ep_handle* h, const void* x, int32_t hidden, void* pool,
     a.tile_target = h->tile_target;
     a.pool = pool;
     a.scales = pool_scales;
+    a.scale_kind = scale_kind(flags);
+    a.scale_mn = (flags & EP_SCALE_MN_MAJOR) ? 1 : 0;
+    a.scale_ld = scale_ld_of(h->cap);
     a.arrival = h->arrival;
     a.tile_ready = h->tile_ready;
     a.max_tiles = h->max_tiles;
@@ -284,7 +309,7 @@ ep_status ep_combine(const ep_handle* h, uint32_t epoch, const void* expert_out,
     if (h->T < 0 || epoch != h->epoch || h->lease) return EP_ERR_HANDLE_STATE;
     if (h->T > 0 && (!expert_out || !y || !aligned16(expert_out) || !aligned16(y)))
         return EP_ERR_INVALID_ARGUMENT;
-    epk::CombineArgs a;
+    epk::CombineArgs a{};
     a.expert_out = expert_out;
     a.T = h->T;
     a.K = h->cfg.top_k;
@@ -293,6 +318,51 @@ ep_status ep_combine(const ep_handle* h, uint32_t epoch, const void* expert_out,
     a.weights = h->weights;
     a.y = y;
     return hip_status(epk::launch_combine(a, stream));
+}
+
+ep_status ep_combine_gated(const ep_handle* h, uint32_t epoch, const void* expert_out,
+                           int32_t hidden, void* y, uint32_t round, uint32_t spin_limit_us,
+                           hipStream_t stream) {
+    if (!h) return EP_ERR_INVALID_ARGUMENT;
+    if (hidden <= 0 || hidden % 8 != 0 || round == 0) return EP_ERR_INVALID_ARGUMENT;
+    if (hidden > kMaxHidden) return EP_ERR_UNSUPPORTED;
+    if (h->T < 0 || epoch != h->epoch || h->lease) return EP_ERR_HANDLE_STATE;
+    if (h->T > 0 && (!expert_out || !y || !aligned16(expert_out) || !aligned16(y)))
+        return EP_ERR_INVALID_ARGUMENT;
+    epk::CombineArgs a{};
+    a.expert_out = expert_out;
+    a.T = h->T;
+    a.K = h->cfg.top_k;
+    a.H = hidden;
+    a.slot_to_row = h->slot_to_row;
+    a.weights = h->weights;
+    a.y = y;
+    a.y_done = h->y_done;
+    a.round = round;
+    a.limit_ticks = (uint64_t)spin_limit_us * (uint64_t)h->wall_khz / 1000u;
+    a.error = h->error;
+    return hip_status(epk::launch_combine_gated(a, stream));
+}
+
+ep_status ep_fp8_cast_back(const void* q, const void* scales, uint32_t flags, int64_t rows,
+                           int64_t scale_ld, int32_t hidden, void* out, hipStream_t stream) {
+    if (flags & ~(kScaleFlags | EP_DISPATCH_FP8)) return EP_ERR_INVALID_ARGUMENT;
+    if (rows < 0 || hidden <= 0 || hidden % 128 != 0) return EP_ERR_INVALID_ARGUMENT;
+    if (hidden > kMaxHidden) return EP_ERR_UNSUPPORTED;
+    if ((flags & EP_SCALE_MN_MAJOR) && scale_ld < rows) return EP_ERR_INVALID_ARGUMENT;
+    if (rows == 0) return EP_OK;
+    if (!q || !scales || !out || !aligned16(q) || !aligned16(out) || !scales_aligned(scales, flags))
+        return EP_ERR_INVALID_ARGUMENT;
+    epk::CastBackArgs a{};
+    a.q = q;
+    a.scales = scales;
+    a.scale_kind = scale_kind(flags);
+    a.scale_mn = (flags & EP_SCALE_MN_MAJOR) ? 1 : 0;
+    a.scale_ld = scale_ld;
+    a.rows = rows;
+    a.H = hidden;
+    a.out = out;
+    return hip_status(epk::launch_cast_back(a, stream));
 }
 
 ep_status ep_combine_backward(const ep_handle* h, uint32_t epoch, const void* grad_y,
@@ -306,7 +376,7 @@ ep_status ep_combine_backward(const ep_handle* h, uint32_t epoch, const void* gr
                      !aligned16(grad_y) || !aligned16(expert_out) ||
                      !aligned16(grad_expert_out) || !aligned4(grad_weights)))
         return EP_ERR_INVALID_ARGUMENT;
-    epk::CombineBwdArgs a;
+    epk::CombineBwdArgs a{};
     a.grad_y = grad_y;
     a.expert_out = expert_out;
     a.T = h->T;
@@ -327,7 +397,7 @@ ep_status ep_dispatch_backward(const ep_handle* h, uint32_t epoch, const void* g
     if (h->T < 0 || epoch != h->epoch || h->lease) return EP_ERR_HANDLE_STATE;
     if (h->T > 0 && (!grad_pool || !grad_x || !aligned16(grad_pool) || !aligned16(grad_x)))
         return EP_ERR_INVALID_ARGUMENT;
-    epk::CombineArgs a;
+    epk::CombineArgs a{};
     a.expert_out = grad_pool;
     a.T = h->T;
     a.K = h->cfg.top_k;
@@ -359,6 +429,7 @@ ep_status ep_handle_get_view(const ep_handle* h, ep_handle_view* out) {
     out->slot_to_pool_row = h->slot_to_row;
     out->pool_recv_token = h->recv_token;
     out->topk_weights = h->weights;
+    out->y_done_per_token = h->y_done;
     return EP_OK;
 }
 
@@ -377,6 +448,7 @@ int64_t ep_array_bytes(const ep_handle* h, ep_array which) {
         case EP_ARRAY_SLOT_TO_POOL_ROW:
         case EP_ARRAY_TOPK_WEIGHTS: return 4 * slots;
         case EP_ARRAY_POOL_RECV_TOKEN: return 4 * h->cap;
+        case EP_ARRAY_Y_DONE: return 4 * (int64_t)(h->T < 0 ? 0 : h->T);
     }
     return -1;
 }
@@ -399,6 +471,7 @@ ep_status ep_copy_array(const ep_handle* h, ep_array which, void* dst, int64_t d
         case EP_ARRAY_SLOT_TO_POOL_ROW: src = h->slot_to_row; break;
         case EP_ARRAY_POOL_RECV_TOKEN: src = h->recv_token; break;
         case EP_ARRAY_TOPK_WEIGHTS: src = h->weights; break;
+        case EP_ARRAY_Y_DONE: src = h->y_done; break;
     }
     return hip_status(hipMemcpyAsync(dst, src, (size_t)n, hipMemcpyDeviceToDevice, stream));
 }
@@ -436,8 +509,10 @@ ep_status ep_tile_consume(const ep_handle* h, uint32_t seq, const void* pool,
                           const uint8_t* pool_scales, int32_t hidden, uint32_t flags, void* out,
                           int32_t workgroups, uint32_t spin_limit_us, hipStream_t stream) {
     if (!h) return EP_ERR_INVALID_ARGUMENT;
-    if (flags & ~(EP_DISPATCH_FP8 | EP_DISPATCH_TILE_READY | EP_CONSUME_GATHER))
+    if (flags & ~(EP_DISPATCH_FP8 | EP_DISPATCH_TILE_READY | EP_CONSUME_GATHER |
+                  EP_CONSUME_SIGNAL_DONE | kScaleFlags))
         return EP_ERR_INVALID_ARGUMENT;
+    if (flags & kScaleFlags) return EP_ERR_UNSUPPORTED;
     const bool fp8 = (flags & EP_DISPATCH_FP8) != 0;
     const bool gather = (flags & EP_CONSUME_GATHER) != 0;
     if (fp8 && gather) return EP_ERR_UNSUPPORTED;
@@ -447,7 +522,7 @@ ep_status ep_tile_consume(const ep_handle* h, uint32_t seq, const void* pool,
     if (workgroups < 1 || workgroups > 65536) return EP_ERR_INVALID_ARGUMENT;
     if (h->T < 0) return EP_ERR_HANDLE_STATE;
     if (!pool || !out || !aligned16(pool) || !aligned16(out)) return EP_ERR_INVALID_ARGUMENT;
-    epk::ConsumeArgs a;
+    epk::ConsumeArgs a{};
     a.pool = pool;
     a.scales = pool_scales;
     a.H = hidden;
@@ -461,6 +536,7 @@ ep_status ep_tile_consume(const ep_handle* h, uint32_t seq, const void* pool,
     a.limit_ticks = (uint64_t)spin_limit_us * (uint64_t)h->wall_khz / 1000u;
     a.out = out;
     a.error = h->error;
+    a.y_done = (flags & EP_CONSUME_SIGNAL_DONE) ? h->y_done : nullptr;
     return hip_status(epk::launch_consume(a, workgroups, stream));
 }
 

@@ -36,6 +36,14 @@ struct LayoutArgs {
     uint32_t* error;            // [1]
     int32_t* ws;                // [blocks * E] per-workgroup counts, then bases
     uint32_t* done;             // [1] last-workgroup counter (self-resetting)
+    uint32_t* y_done;           // [T] per-token done counts, zeroed here
+};
+
+// Scale flavours of the FP8 dispatch and the cast back.
+enum ScaleKind : int32_t {
+    kScaleUe8m0 = 0,            // UE8M0 exponent byte
+    kScaleF32 = 1,              // float32 amax / 448
+    kScalePow2F32 = 2,          // float32 2^e (the UE8M0 exponent as a float)
 };
 
 struct DispatchArgs {
@@ -49,7 +57,10 @@ struct DispatchArgs {
     const int32_t* tile_expert;
     const int32_t* tile_target;
     void* pool;
-    uint8_t* scales;
+    void* scales;
+    int32_t scale_kind;         // ScaleKind
+    int32_t scale_mn;           // 1: MN-major [G, scale_ld] (UE8M0 packed 4 per word)
+    int64_t scale_ld;
     // streaming release
     uint32_t* arrival;
     uint32_t* tile_ready;
@@ -67,6 +78,11 @@ struct CombineArgs {
     const int32_t* slot_to_row;
     const float* weights;
     void* y;
+    // per-token gate (ep_combine_gated): wait for y_done[t] >= round * slots(t)
+    const uint32_t* y_done;
+    uint32_t round;
+    uint64_t limit_ticks;
+    uint32_t* error;
 };
 
 struct CombineBwdArgs {
@@ -95,11 +111,25 @@ struct ConsumeArgs {
     uint64_t limit_ticks;
     void* out;
     uint32_t* error;
+    uint32_t* y_done;           // non-null: count each written row for its token
+};
+
+struct CastBackArgs {
+    const void* q;              // e4m3fn [rows, H]
+    const void* scales;
+    int32_t scale_kind;
+    int32_t scale_mn;
+    int64_t scale_ld;
+    int64_t rows;
+    int32_t H;
+    void* out;                  // bf16 [rows, H]
 };
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
 hipError_t launch_dispatch(const DispatchArgs& a, bool fp8, bool tile_ready, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+hipError_t launch_combine_gated(const CombineArgs& a, hipStream_t stream);
+hipError_t launch_cast_back(const CastBackArgs& a, hipStream_t stream);
 // unit_weights: every unmasked slot weighs 1 (the backward of dispatch)
 hipError_t launch_combine_unit(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t stream);

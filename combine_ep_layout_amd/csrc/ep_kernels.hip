@@ -367,6 +367,11 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
     const int s1 = min(a.S, (b + 1) * kLayoutSlotsPerBlock);
     for (int s = b * kLayoutSlotsPerBlock + tid; s < s1; s += kLayoutThreads)
         a.weights[s] = a.topk_w[s];
+    // ... and of the per-token done counts of the tokens whose first slot is here
+    const int T = a.S / a.K;
+    const int tb0 = (b * kLayoutSlotsPerBlock + a.K - 1) / a.K;
+    const int tb1 = min(T, (s1 + a.K - 1) / a.K);
+    for (int t = tb0 + tid; t < tb1; t += kLayoutThreads) a.y_done[t] = 0u;
 }
 
 // ------------------------------------------------------------- dispatch ---
@@ -557,12 +562,110 @@ __device__ __forceinline__ uint32_t e4m3_code(uint32_t b, int e) {
     return sign | code;
 }
 
+// e4m3fn code magnitude of a finite non-negative float32 (bit pattern v),
+// round to nearest even, saturating at 448 (code 0x7E).
+__device__ __forceinline__ uint32_t e4m3_code_f32(uint32_t v) {
+    if (v >= 0x43E00000u) return 0x7Eu;             // >= 448
+    const int eb = (int)(v >> 23);
+    const uint32_t sig = eb ? (0x800000u | (v & 0x7FFFFFu)) : (v & 0x7FFFFFu);
+    if (sig == 0u) return 0u;
+    const int p = eb ? eb - 150 : -149;              // value = sig * 2^p
+    const int nb = 32 - __clz(sig);
+    const int k = p + nb - 1;
+    if (k >= -6) {                                   // normal: keep 4 significant bits
+        const int sh = nb - 4;                       // >= 1: sig has >= 5 bits here
+        const uint32_t m = sig >> sh;
+        const uint32_t rem = sig & ((1u << sh) - 1u), half = 1u << (sh - 1);
+        const uint32_t up = (rem > half || (rem == half && (m & 1u))) ? 1u : 0u;
+        const uint32_t code = ((uint32_t)(k + 7) << 3) + (m - 8u) + up;
+        return code > 0x7Eu ? 0x7Eu : code;
+    }
+    const int sh = -(p + 9);                         // subnormal: multiples of 2^-9
+    if (sh <= 0) return sig << (-sh);
+    if (sh >= 25) return 0u;
+    const uint32_t m = sig >> sh;
+    const uint32_t rem = sig & ((1u << sh) - 1u), half = 1u << (sh - 1);
+    return m + ((rem > half || (rem == half && (m & 1u))) ? 1u : 0u);
+}
+
+// Float32-scale flavour: code of float(x * f) for the bf16 pattern b, with
+// the sign of x; a NaN product gives 0x7F.
+__device__ __forceinline__ uint32_t e4m3_code_scaled(uint32_t b, float f) {
+    const uint32_t sign = (b >> 8) & 0x80u;
+    const float v = __uint_as_float(b << 16) * f;
+    const uint32_t mag = __float_as_uint(v) & 0x7FFFFFFFu;
+    if (mag > 0x7F800000u) return sign | 0x7Fu;
+    return sign | e4m3_code_f32(mag);
+}
+
 __device__ __forceinline__ uint32_t mag_for_max(uint32_t b) {
     const uint32_t m = b & 0x7FFFu;
     return m > 0x7F80u ? 0u : m;                     // NaN does not take part
 }
 
+// Scale stores of one 64-lane step (8 groups): every lane of a group holds
+// its group's byte (UE8M0) and float (the other flavours).  Device-coherent
+// atomic stores when streaming, so the release stays cheap.
+template <bool STREAM, typename V>
+__device__ __forceinline__ void put_scale(V* p, V v) {
+    if constexpr (STREAM)
+        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        *p = v;
+}
+
 template <int KT, bool STREAM>
+__device__ __forceinline__ void store_scales(const DispatchArgs& a, const int (&rows)[KT], int c,
+                                             int nunit, int ngrp, bool pack8, uint32_t sbyte,
+                                             float sval) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int g = c >> 3;
+    if (a.scale_kind == kScaleUe8m0 && a.scale_mn) {
+        // packed words: group 4w + j in byte j; lanes 0 and 32 hold groups 4w
+        const uint32_t word = sbyte | ((uint32_t)__shfl((int)sbyte, lane + 8, kWave) << 8) |
+                              ((uint32_t)__shfl((int)sbyte, lane + 16, kWave) << 16) |
+                              ((uint32_t)__shfl((int)sbyte, lane + 24, kWave) << 24);
+        if ((lane & 31) == 0 && g < ngrp) {
+            uint32_t* col = (uint32_t*)a.scales + (int64_t)(g >> 2) * a.scale_ld;
+#pragma unroll
+            for (int k = 0; k < KT; ++k)
+                if (rows[k] >= 0) put_scale<STREAM>(col + rows[k], word);
+        }
+    } else if (a.scale_kind == kScaleUe8m0) {
+        // the 8 bytes of a full step go out as one 64-bit store per row
+        if (pack8 && c - lane + kWave <= nunit) {
+            uint64_t word = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                word |= (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)sbyte, 8 * j) << (8 * j);
+            const int g0 = (c - lane) >> 3;
+#pragma unroll
+            for (int k = 0; k < KT; ++k) {
+                if (rows[k] < 0 || lane != k) continue;
+                put_scale<STREAM>((uint64_t*)((uint8_t*)a.scales + (int64_t)rows[k] * ngrp + g0), word);
+            }
+        } else if (c < nunit && (lane & 7) == 0) {
+#pragma unroll
+            for (int k = 0; k < KT; ++k) {
+                if (rows[k] < 0) continue;
+                ((uint8_t*)a.scales)[(int64_t)rows[k] * ngrp + g] = (uint8_t)sbyte;
+            }
+        }
+    } else if (c < nunit && (lane & 7) == 0) {
+        float* sc = (float*)a.scales;
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+            if (rows[k] < 0) continue;
+            float* p = a.scale_mn ? sc + (int64_t)g * a.scale_ld + rows[k]
+                                  : sc + (int64_t)rows[k] * ngrp + g;
+            put_scale<STREAM>(p, sval);
+        }
+    }
+}
+
+// F32Q: float32 scale amax / 448 and codes of x * (448 / amax); otherwise the
+// UE8M0 exponent (stored as a byte, or as the float 2^e).
+template <int KT, bool STREAM, bool F32Q>
 __global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg, int ipb) {
     extern __shared__ int smem[];
     constexpr int U = EP_FP8_UNROLL;
@@ -613,16 +716,39 @@ __global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg,
             amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, kWave));
             amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2, kWave));
             amax = max(amax, (uint32_t)__shfl_xor((int)amax, 4, kWave));
-            const int e = ue8m0_exp(amax);
             u32x4 q;
+            uint32_t sbyte = 0;
+            float sval;
+            if constexpr (F32Q) {
+                // a = max(amax, 448 * 2^-126); s = a / 448; f = 448 / a (IEEE divisions)
+                const float af = fmaxf(__uint_as_float(amax << 16), 448.0f * 0x1p-126f);
+                sval = af / 448.0f;
+                const float f = 448.0f / af;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const uint32_t w0 = lo[u][2 * i], w1 = lo[u][2 * i + 1];
-                q[i] = e4m3_code(w0 & 0xFFFFu, e) | (e4m3_code(w0 >> 16, e) << 8) |
-                       (e4m3_code(w1 & 0xFFFFu, e) << 16) | (e4m3_code(w1 >> 16, e) << 24);
-                const uint32_t h0 = hi[u][2 * i], h1 = hi[u][2 * i + 1];
-                q[2 + i] = e4m3_code(h0 & 0xFFFFu, e) | (e4m3_code(h0 >> 16, e) << 8) |
-                           (e4m3_code(h1 & 0xFFFFu, e) << 16) | (e4m3_code(h1 >> 16, e) << 24);
+                for (int i = 0; i < 2; ++i) {
+                    const uint32_t w0 = lo[u][2 * i], w1 = lo[u][2 * i + 1];
+                    q[i] = e4m3_code_scaled(w0 & 0xFFFFu, f) | (e4m3_code_scaled(w0 >> 16, f) << 8) |
+                           (e4m3_code_scaled(w1 & 0xFFFFu, f) << 16) |
+                           (e4m3_code_scaled(w1 >> 16, f) << 24);
+                    const uint32_t h0 = hi[u][2 * i], h1 = hi[u][2 * i + 1];
+                    q[2 + i] = e4m3_code_scaled(h0 & 0xFFFFu, f) | (e4m3_code_scaled(h0 >> 16, f) << 8) |
+                               (e4m3_code_scaled(h1 & 0xFFFFu, f) << 16) |
+                               (e4m3_code_scaled(h1 >> 16, f) << 24);
+                }
+            } else {
+                const int e = ue8m0_exp(amax);
+                sbyte = (uint32_t)(e + 127);
+                // 2^e as a float32 pattern (2^-127 is the subnormal 0x00400000)
+                sval = __uint_as_float(e > -127 ? sbyte << 23 : 0x00400000u);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const uint32_t w0 = lo[u][2 * i], w1 = lo[u][2 * i + 1];
+                    q[i] = e4m3_code(w0 & 0xFFFFu, e) | (e4m3_code(w0 >> 16, e) << 8) |
+                           (e4m3_code(w1 & 0xFFFFu, e) << 16) | (e4m3_code(w1 >> 16, e) << 24);
+                    const uint32_t h0 = hi[u][2 * i], h1 = hi[u][2 * i + 1];
+                    q[2 + i] = e4m3_code(h0 & 0xFFFFu, e) | (e4m3_code(h0 >> 16, e) << 8) |
+                               (e4m3_code(h1 & 0xFFFFu, e) << 16) | (e4m3_code(h1 >> 16, e) << 24);
+                }
             }
             if (c < nunit) {
 #pragma unroll
@@ -631,31 +757,7 @@ __global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg,
                     store_pool<STREAM>(pool + (int64_t)rows[k] * nunit, a.H, c, q);
                 }
             }
-            // scale bytes: the 8 groups of a full 64-lane step go out as one
-            // 64-bit store per row (device-coherent when streaming)
-            const uint32_t sbyte = (uint32_t)(e + 127);
-            if (pack8 && c - lane + kWave <= nunit) {
-                uint64_t word = 0;
-#pragma unroll
-                for (int g = 0; g < 8; ++g)
-                    word |= (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)sbyte, 8 * g) << (8 * g);
-                const int g0 = (c - lane) >> 3;
-#pragma unroll
-                for (int k = 0; k < KT; ++k) {
-                    if (rows[k] < 0 || lane != k) continue;
-                    uint64_t* dst = (uint64_t*)(a.scales + (int64_t)rows[k] * ngrp + g0);
-                    if constexpr (STREAM)
-                        __hip_atomic_store(dst, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    else
-                        *dst = word;
-                }
-            } else if (c < nunit && (lane & 7) == 0) {
-#pragma unroll
-                for (int k = 0; k < KT; ++k) {
-                    if (rows[k] < 0) continue;
-                    a.scales[(int64_t)rows[k] * ngrp + (c >> 3)] = (uint8_t)sbyte;
-                }
-            }
+            store_scales<KT, STREAM>(a, rows, c, nunit, ngrp, pack8, sbyte, sval);
         }
     }
     if constexpr (STREAM) release_block(a, i0 / nseg, i1 / nseg, smem, smem + a.E);
@@ -669,7 +771,34 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <int KT, bool UNIT>
+// Per-token gate (StreamEP README, y_done_per_token): wait until the token's
+// done count has reached `target`, then acquire at device scope so the expert
+// rows the producers released are seen.  Bounded: past limit_ticks, or once
+// another wave has timed out (error bit 2), it gives up and returns false.
+__device__ __forceinline__ bool wait_done(const uint32_t* cnt, uint32_t target, uint64_t limit,
+                                          uint32_t* error) {
+    uint32_t v = (uint32_t)uniform_i((int)__hip_atomic_load(cnt, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT));
+    if ((int32_t)(v - target) < 0) {
+        const uint64_t start = wall_clock64();
+        do {
+            const uint32_t err = (uint32_t)uniform_i((int)__hip_atomic_load(
+                error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            if ((err & 2u) || wall_clock64() - start > limit) {
+                if ((threadIdx.x & (kWave - 1)) == 0) atomicOr(error, 2u);
+                return false;
+            }
+            __builtin_amdgcn_s_sleep(4);
+            v = (uint32_t)uniform_i((int)__hip_atomic_load(cnt, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT));
+        } while ((int32_t)(v - target) < 0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return true;
+}
+
+// GATE: the per-token gated combine; a token whose gate times out is skipped.
+template <int KT, bool UNIT, bool GATE>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a, int nseg, int ipb) {
     constexpr int U = EP_COMBINE_UNROLL;
     const int lane = threadIdx.x & (kWave - 1);
@@ -688,6 +817,12 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a, int nseg, int ip
         for (int k = 0; k < KT; ++k) {
             rows[k] = (k < a.K) ? a.slot_to_row[t * a.K + k] : -1;
             wt[k] = UNIT ? 1.0f : ((k < a.K) ? a.weights[t * a.K + k] : 0.0f);
+        }
+        if constexpr (GATE) {
+            uint32_t n = 0;
+#pragma unroll
+            for (int k = 0; k < KT; ++k) n += rows[k] >= 0 ? 1u : 0u;
+            if (n && !wait_done(a.y_done + t, n * a.round, a.limit_ticks, a.error)) continue;
         }
         const int c0 = seg * (kWave * U) + lane;
         u32x4 v[KT][U];
@@ -877,7 +1012,109 @@ __global__ __launch_bounds__(256) void k_tile_consume(ConsumeArgs a) {
                 for (int c = lane; c < n16; c += kWave) dst[c] = src[c];
             }
         }
+        if (a.y_done) {
+            // producer side of the per-token gate: publish the tile's rows at
+            // device scope, then count each real row for its token
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (w == 0) {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                for (int r = j * a.BM + lane; r < (j + 1) * a.BM; r += kWave) {
+                    const int tok = a.recv_token[r];
+                    if (tok >= 0)
+                        __hip_atomic_fetch_add(&a.y_done[tok], 1u, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+        }
         __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------ cast back ---
+
+#ifndef EP_CAST_UNROLL
+#define EP_CAST_UNROLL 2       // 16-channel units per lane per cast-back work item
+#endif
+
+// Exact float32 value of an e4m3fn code magnitude (0..0x7E).
+__device__ __forceinline__ float e4m3_value_f32(uint32_t mag) {
+    const uint32_t ef = mag >> 3, m = mag & 7u;
+    return ef ? __uint_as_float(((ef + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+}
+
+// bf16 of value(code) * s in float32 (one rounded product, then RNE); NaN
+// codes and NaN products give a quiet NaN with the code's sign.
+__device__ __forceinline__ uint32_t e4m3_scaled_to_bf16(uint32_t code, float s) {
+    const uint32_t sign = (code & 0x80u) << 8;
+    const uint32_t mag = code & 0x7Fu;
+    if (mag == 0x7Fu) return sign | 0x7FC0u;
+    const float v = e4m3_value_f32(mag);
+    const float p = ((code & 0x80u) ? -v : v) * s;
+    if ((__float_as_uint(p) & 0x7FFFFFFFu) > 0x7F800000u) return sign | 0x7FC0u;
+    return f32_to_bf16_rne(p);
+}
+
+// per_token_cast_back (instagit DeepEP low-latency page, example usage):
+// bf16 rows from e4m3fn codes and their per-128-channel scales in any of the
+// dispatch's flavours and layouts.  One work item is one wave over up to
+// 64 * EP_CAST_UNROLL units of 16 channels of one row: 16 bytes of codes in,
+// 32 bytes of bf16 out per unit, the group's scale read once per unit.
+__global__ __launch_bounds__(256) void k_cast_back(CastBackArgs a, int nseg) {
+    constexpr int U = EP_CAST_UNROLL;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t items = a.rows * nseg;
+    for (int64_t it = (int64_t)blockIdx.x * 4 + (threadIdx.x / kWave); it < items;
+         it += (int64_t)gridDim.x * 4) {
+        const int64_t r = it / nseg;
+        const int seg = (int)(it - r * nseg);
+        const int nunit = a.H / 16;
+        const int ngrp = a.H / 128;
+        const u32x4* src = (const u32x4*)a.q + r * nunit;
+        u32x4* dst = (u32x4*)a.out + r * (a.H / 8);
+        u32x4 q[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = seg * (kWave * U) + u * kWave + lane;
+            if (c < nunit) q[u] = load_v<true>(src + c);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = seg * (kWave * U) + u * kWave + lane;
+            if (c >= nunit) continue;
+            const int g = c >> 3;
+            u32x4 o0, o1;
+            if (a.scale_kind == kScaleUe8m0) {
+                const uint32_t byte =
+                    a.scale_mn ? (((const uint32_t*)a.scales)[(int64_t)(g >> 2) * a.scale_ld + r] >>
+                                  (8 * (g & 3))) & 0xFFu
+                               : ((const uint8_t*)a.scales)[r * ngrp + g];
+                const int e = (int)byte - 127;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t word = q[u][i];
+                    const uint32_t lo = e4m3_to_bf16(word & 0xFFu, e) | (e4m3_to_bf16((word >> 8) & 0xFFu, e) << 16);
+                    const uint32_t hi = e4m3_to_bf16((word >> 16) & 0xFFu, e) | (e4m3_to_bf16(word >> 24, e) << 16);
+                    if (i < 2) { o0[2 * i] = lo; o0[2 * i + 1] = hi; }
+                    else { o1[2 * (i - 2)] = lo; o1[2 * (i - 2) + 1] = hi; }
+                }
+            } else {
+                const float sc = a.scale_mn ? ((const float*)a.scales)[(int64_t)g * a.scale_ld + r]
+                                            : ((const float*)a.scales)[r * ngrp + g];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t word = q[u][i];
+                    const uint32_t lo = e4m3_scaled_to_bf16(word & 0xFFu, sc) |
+                                        (e4m3_scaled_to_bf16((word >> 8) & 0xFFu, sc) << 16);
+                    const uint32_t hi = e4m3_scaled_to_bf16((word >> 16) & 0xFFu, sc) |
+                                        (e4m3_scaled_to_bf16(word >> 24, sc) << 16);
+                    if (i < 2) { o0[2 * i] = lo; o0[2 * i + 1] = hi; }
+                    else { o1[2 * (i - 2)] = lo; o1[2 * (i - 2) + 1] = hi; }
+                }
+            }
+            store_row<EP_COMBINE_STORE>(dst, a.H * 2, 2 * c, o0);
+            store_row<EP_COMBINE_STORE>(dst, a.H * 2, 2 * c + 1, o1);
+        }
     }
 }
 
@@ -898,10 +1135,15 @@ hipError_t dispatch_kt(const DispatchArgs& a, bool fp8, bool stream, hipStream_t
     const size_t lds = stream ? 2 * sizeof(int) * (size_t)a.E : 0;
     const dim3 block(stream ? 1024 : 256);
     if (fp8) {
-        if (stream)
-            hipLaunchKernelGGL((k_dispatch_fp8<KT, true>), dim3(grid), block, lds, st, a, nseg, ipb);
+        const bool f32q = a.scale_kind == kScaleF32;
+        if (stream && f32q)
+            hipLaunchKernelGGL((k_dispatch_fp8<KT, true, true>), dim3(grid), block, lds, st, a, nseg, ipb);
+        else if (stream)
+            hipLaunchKernelGGL((k_dispatch_fp8<KT, true, false>), dim3(grid), block, lds, st, a, nseg, ipb);
+        else if (f32q)
+            hipLaunchKernelGGL((k_dispatch_fp8<KT, false, true>), dim3(grid), block, lds, st, a, nseg, ipb);
         else
-            hipLaunchKernelGGL((k_dispatch_fp8<KT, false>), dim3(grid), block, lds, st, a, nseg, ipb);
+            hipLaunchKernelGGL((k_dispatch_fp8<KT, false, false>), dim3(grid), block, lds, st, a, nseg, ipb);
     } else {
         if (stream)
             hipLaunchKernelGGL((k_dispatch_bf16<KT, true>), dim3(grid), block, lds, st, a, nseg, ipb);
@@ -911,26 +1153,26 @@ hipError_t dispatch_kt(const DispatchArgs& a, bool fp8, bool stream, hipStream_t
     return hipGetLastError();
 }
 
-template <int KT, bool UNIT>
+template <int KT, bool UNIT, bool GATE>
 hipError_t combine_kt(const CombineArgs& a, hipStream_t st) {
     const int per_seg = kWave * EP_COMBINE_UNROLL * 8;
     const int nseg = (a.H + per_seg - 1) / per_seg;
     const int ipb = items_per_block(nseg, false);
     const int64_t items = (int64_t)a.T * nseg;
     const int grid = (int)((items + ipb - 1) / ipb);
-    hipLaunchKernelGGL((k_combine<KT, UNIT>), dim3(grid), dim3(256), 0, st, a, nseg, ipb);
+    hipLaunchKernelGGL((k_combine<KT, UNIT, GATE>), dim3(grid), dim3(256), 0, st, a, nseg, ipb);
     return hipGetLastError();
 }
 
-template <bool UNIT>
+template <bool UNIT, bool GATE>
 hipError_t combine_any(const CombineArgs& a, hipStream_t stream) {
     if (a.T == 0) return hipSuccess;
-    if (a.K <= 1) return combine_kt<1, UNIT>(a, stream);
-    if (a.K <= 2) return combine_kt<2, UNIT>(a, stream);
-    if (a.K <= 4) return combine_kt<4, UNIT>(a, stream);
-    if (a.K <= 8) return combine_kt<8, UNIT>(a, stream);
-    if (a.K <= 16) return combine_kt<16, UNIT>(a, stream);
-    return combine_kt<32, UNIT>(a, stream);
+    if (a.K <= 1) return combine_kt<1, UNIT, GATE>(a, stream);
+    if (a.K <= 2) return combine_kt<2, UNIT, GATE>(a, stream);
+    if (a.K <= 4) return combine_kt<4, UNIT, GATE>(a, stream);
+    if (a.K <= 8) return combine_kt<8, UNIT, GATE>(a, stream);
+    if (a.K <= 16) return combine_kt<16, UNIT, GATE>(a, stream);
+    return combine_kt<32, UNIT, GATE>(a, stream);
 }
 
 template <int KT>
@@ -977,11 +1219,15 @@ hipError_t launch_dispatch(const DispatchArgs& a, bool fp8, bool tile_ready, hip
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
-    return combine_any<false>(a, stream);
+    return combine_any<false, false>(a, stream);
+}
+
+hipError_t launch_combine_gated(const CombineArgs& a, hipStream_t stream) {
+    return combine_any<false, true>(a, stream);
 }
 
 hipError_t launch_combine_unit(const CombineArgs& a, hipStream_t stream) {
-    return combine_any<true>(a, stream);
+    return combine_any<true, false>(a, stream);
 }
 
 hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t stream) {
@@ -992,6 +1238,17 @@ hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t stream) {
     if (a.K <= 8) return combine_bwd_kt<8>(a, stream);
     if (a.K <= 16) return combine_bwd_kt<16>(a, stream);
     return combine_bwd_kt<32>(a, stream);
+}
+
+hipError_t launch_cast_back(const CastBackArgs& a, hipStream_t stream) {
+    if (a.rows == 0) return hipSuccess;
+    const int nunit = a.H / 16;
+    const int nseg = (nunit + kWave * EP_CAST_UNROLL - 1) / (kWave * EP_CAST_UNROLL);
+    const int64_t items = a.rows * nseg;
+    int64_t grid = (items + 3) / 4;
+    if (grid > (1 << 20)) grid = 1 << 20;          // grid-stride beyond a million workgroups
+    hipLaunchKernelGGL(k_cast_back, dim3((uint32_t)grid), dim3(256), 0, stream, a, nseg);
+    return hipGetLastError();
 }
 
 hipError_t launch_consume(const ConsumeArgs& a, int workgroups, hipStream_t stream) {

@@ -19,8 +19,14 @@
  *   [CONTRACT] same blog, integration data-contract section: a per-execution
  *          epoch guards against reusing a stale handle.
  *   [WEIGHTS] same blog, router-weight section: y_t = sum_j p_{t,j} o_{t,j}.
- *   [FP8]  instagit DeepEP low-latency page, "FP8 and Quantization Support":
- *          float8_e4m3fn payload with UE8M0 scales.
+ *   [FP8]  instagit DeepEP low-latency page, "FP8 and Quantization Support"
+ *          and "API Signature and Return Values": float8_e4m3fn payload with
+ *          UE8M0 scales (use_ue8m0), float32 scales otherwise, optionally
+ *          rounded to a power of two (round_scale); per_token_cast_back turns
+ *          the payload back into bf16 (the page's example usage).
+ *   [GATE] StreamEP README, opening paragraph: a per-receive-token gate on
+ *          combine (y_done_per_token) lets combine start on a token as soon
+ *          as that token's expert compute has drained.
  *   [BORROW] DeepEP PR #769, "Add opt-in borrowed receive storage for compact
  *          BF16 dispatch", Description: dispatch may skip the activation copy
  *          and hand an indexed consumer a view (slab, row indices) instead; the
@@ -82,13 +88,40 @@ typedef struct ep_config {
 } ep_config;
 
 /* ep_dispatch flags. */
-#define EP_DISPATCH_FP8        (1u << 0) /* e4m3fn payload + UE8M0 scales ([FP8])    */
+#define EP_DISPATCH_FP8        (1u << 0) /* e4m3fn payload + per-128-channel scales ([FP8]) */
 #define EP_DISPATCH_TILE_READY (1u << 1) /* per-tile arrival counts release tile_ready ([SEP]) */
 #define EP_DISPATCH_BORROW     (1u << 2) /* no copy: lend x through the row map ([BORROW]) */
 
-/* ep_tile_consume flag: rows are gathered from a borrowed slab through
- * pool_recv_token instead of being read from a pool ([BORROW]). */
+/* Scale flavour and layout of an FP8 dispatch (and of ep_fp8_cast_back).
+ * Without EP_SCALE_F32 a scale is a UE8M0 byte 2^(byte-127) (use_ue8m0).
+ *   EP_SCALE_F32          float32 scales s = a/448 with a = max(amax,
+ *                         448*2^-126); codes are float(x * (448/a)) rounded
+ *                         to nearest-even e4m3fn, saturating at 448.
+ *   EP_SCALE_F32 | EP_SCALE_ROUND
+ *                         float32 scales rounded to a power of two: the UE8M0
+ *                         exponent e as the float 2^e, codes as for UE8M0.
+ *                         (EP_SCALE_ROUND alone changes nothing: UE8M0 scales
+ *                         are powers of two already.)
+ *   EP_SCALE_MN_MAJOR     group g of pool row r at [g, r] with leading
+ *                         dimension ep_scale_ld(); UE8M0 bytes are then packed
+ *                         four groups to a uint32 word, group 4w+j in byte j of
+ *                         word w (bytes past the last group are 0), an array
+ *                         uint32 [ceil(G/4), ld].  Without it scales are
+ *                         row-major [capacity_rows, G], G = hidden/128.
+ * The flavour names and the per-128-channel grouping follow [FP8]; the page
+ * gives no formulas, the ones above are this library's reading. */
+#define EP_SCALE_F32           (1u << 4)
+#define EP_SCALE_ROUND         (1u << 5)
+#define EP_SCALE_MN_MAJOR      (1u << 6)
+
+/* ep_tile_consume flags: EP_CONSUME_GATHER reads rows from a borrowed slab
+ * through pool_recv_token instead of from a pool ([BORROW]);
+ * EP_CONSUME_SIGNAL_DONE makes the consumer act as the expert-output
+ * producer of the per-token gate ([GATE]): after writing a tile it publishes
+ * the rows at device scope and adds 1 to y_done_per_token[pool_recv_token[r]]
+ * for each real row r of the tile. */
 #define EP_CONSUME_GATHER      (1u << 3)
+#define EP_CONSUME_SIGNAL_DONE (1u << 7)
 
 /* Allocate a handle and all its device metadata on the current device.
  * Returns EP_ERR_INVALID_ARGUMENT for out-of-range fields or when the pool
@@ -109,6 +142,10 @@ int32_t ep_max_tiles(const ep_handle* h);
 /* Tokens of the current layout, or -1 when there is none. */
 int32_t ep_num_tokens(const ep_handle* h);
 
+/* Leading dimension of MN-major scales: capacity_rows rounded up to a
+ * multiple of 4 (16-byte aligned columns). */
+int64_t ep_scale_ld(const ep_handle* h);
+
 /* Build the expert-major layout of one routing ([SEP], [ROUND]).
  *   topk_idx      device int32 [num_tokens, top_k]; -1 marks a masked slot.
  *   topk_weights  device fp32  [num_tokens, top_k]; copied into the handle.
@@ -122,7 +159,7 @@ int32_t ep_num_tokens(const ep_handle* h);
  *   slot_to_pool_row[t*K+k]      pool row of slot (t,k), -1 if masked
  *   pool_recv_token[r]           source token of pool row r, -1 for padding
  * Rows of one expert are in ascending slot order t*K+k.  pool_arrival_count is
- * zeroed for the layout's tiles.  Ids outside [-1, E) are treated as masked and
+ * zeroed for the layout's tiles and y_done_per_token for its tokens.  Ids outside [-1, E) are treated as masked and
  * set EP_ERR_BAD_ROUTING in the error word.  Invalidates earlier epochs. */
 ep_status ep_layout(ep_handle* h, const int32_t* topk_idx, const float* topk_weights,
                     int32_t num_tokens, hipStream_t stream, uint32_t* epoch_out);
@@ -131,20 +168,24 @@ ep_status ep_layout(ep_handle* h, const int32_t* topk_idx, const float* topk_wei
  *   x            device bf16 [num_tokens, hidden], hidden % 8 == 0.
  *   pool         device; bf16 [capacity_rows, hidden], or with EP_DISPATCH_FP8
  *                e4m3fn bytes [capacity_rows, hidden] (hidden % 128 == 0).
- *   pool_scales  device u8 [capacity_rows, hidden/128] UE8M0 bytes (scale =
- *                2^(byte-127)) with EP_DISPATCH_FP8, else must be NULL.
- *   flags        EP_DISPATCH_FP8 | EP_DISPATCH_TILE_READY.
+ *   pool_scales  device, with EP_DISPATCH_FP8 only (else must be NULL): the
+ *                scales in the flavour and layout the EP_SCALE_* flags choose
+ *                (default u8 [capacity_rows, hidden/128] UE8M0 bytes, scale =
+ *                2^(byte-127)); 4-byte aligned for float32 or MN-major scales.
+ *   flags        EP_DISPATCH_FP8 | EP_DISPATCH_TILE_READY | EP_SCALE_*
+ *                (EP_SCALE_* only with EP_DISPATCH_FP8).
  *   seq_out      host, may be NULL; receives this dispatch's sequence number
  *                (1, 2, ... per handle, wraps; compare wrap-safe).
- * Only real rows are written; padding rows and rows past the layout keep
- * their contents.  FP8: per token and 128-channel group, e = smallest integer
- * in [-127,127] with amax <= 448*2^e; codes are x*2^-e rounded to nearest-even
+ * Only real rows are written (scales too); padding rows and rows past the
+ * layout keep their contents.  FP8 with UE8M0 scales: per token and
+ * 128-channel group, e = smallest integer in [-127,127] with amax <= 448*2^e
+ * (NaN takes no part in amax); codes are x*2^-e rounded to nearest-even
  * e4m3fn.  With EP_DISPATCH_TILE_READY each tile's arrival count is raised as
  * its rows land and the dispatch that completes the tile release-stores the
  * sequence number into tile_ready[tile] (device scope), so a consumer on
  * another stream may acquire-load it and read the tile's rows. */
 ep_status ep_dispatch(ep_handle* h, const void* x, int32_t hidden, void* pool,
-                      uint8_t* pool_scales, uint32_t flags, hipStream_t stream,
+                      void* pool_scales, uint32_t flags, hipStream_t stream,
                       uint32_t* seq_out);
 /* EP_DISPATCH_BORROW ([BORROW]): nothing is copied or launched.  The rows are
  * lent as the view (slab = x, row indices = pool_recv_token of the current
@@ -163,6 +204,36 @@ ep_status ep_dispatch(ep_handle* h, const void* x, int32_t hidden, void* pool,
  * starting from +0 and skipping masked slots; a token with no slot gets +0. */
 ep_status ep_combine(const ep_handle* h, uint32_t epoch, const void* expert_out,
                      int32_t hidden, void* y, hipStream_t stream);
+
+/* ep_combine behind the per-token gate ([GATE]).  Before combining token t
+ * the kernel waits (acquire, device scope) until y_done_per_token[t] has
+ * reached round * n_t, n_t = unmasked slots of t (tokens with none do not
+ * wait); the comparison is wrap-safe.  The producers of expert_out (on other
+ * streams) make each row visible at device scope and then add 1 to the count
+ * of that row's token, e.g. ep_tile_consume with EP_CONSUME_SIGNAL_DONE.
+ *   round          >= 1: producer passes since ep_layout this call waits for.
+ *   spin_limit_us  bound on one token's wait; past it, or once any wait of
+ *                  this handle has timed out, the remaining waiting tokens are
+ *                  skipped (their y rows are left as they were) and
+ *                  EP_ERR_TIMEOUT is set in the error word.
+ * Everything else as ep_combine: the result equals ep_combine's bit for bit. */
+ep_status ep_combine_gated(const ep_handle* h, uint32_t epoch, const void* expert_out,
+                           int32_t hidden, void* y, uint32_t round, uint32_t spin_limit_us,
+                           hipStream_t stream);
+
+/* per_token_cast_back ([FP8], example usage): bf16 rows from e4m3fn codes and
+ * their scales, in any flavour and layout of the FP8 dispatch.
+ *   q          device e4m3fn bytes [rows, hidden], hidden % 128 == 0.
+ *   scales     device; layout and type as EP_SCALE_* in `flags` say, with row
+ *              index r in [0, rows) (MN-major: column r of leading dimension
+ *              scale_ld >= rows; ignored otherwise).
+ *   out        device bf16 [rows, hidden], fully written.
+ * out[r,c] = bf16_rne(value(q[r,c]) * s(r, c/128)): UE8M0 scales multiply
+ * exactly; float32 scales give one float product first.  NaN codes (0x7F,
+ * 0xFF), and NaN products, give a quiet NaN with the code's sign.  Needs no
+ * handle. */
+ep_status ep_fp8_cast_back(const void* q, const void* scales, uint32_t flags, int64_t rows,
+                           int64_t scale_ld, int32_t hidden, void* out, hipStream_t stream);
 
 /* Backward of ep_combine ([SEP] "What's in the box" names combine_grads; the
  * values are the derivatives of [WEIGHTS]'s y_t = sum_k w_{t,k} o_{row(t,k)}).
@@ -198,7 +269,8 @@ ep_status ep_borrow_release(ep_handle* h, hipStream_t consumer_stream);
 
 /* Device pointers into the handle's metadata; valid until the next ep_layout
  * or ep_handle_destroy.  Lengths: counts E, offsets E+1, tile arrays
- * max_tiles, pool_recv_token capacity_rows, slot arrays num_tokens*top_k. */
+ * max_tiles, pool_recv_token capacity_rows, slot arrays num_tokens*top_k,
+ * y_done_per_token num_tokens. */
 typedef struct ep_handle_view {
     const int32_t* expert_counts;
     const int32_t* expert_pool_block_offset;
@@ -210,6 +282,7 @@ typedef struct ep_handle_view {
     const int32_t* slot_to_pool_row;
     const int32_t* pool_recv_token;
     const float* topk_weights;
+    uint32_t* y_done_per_token;     /* [num_tokens], written by expert-output producers */
 } ep_handle_view;
 
 ep_status ep_handle_get_view(const ep_handle* h, ep_handle_view* out);
@@ -225,7 +298,8 @@ typedef enum ep_array {
     EP_ARRAY_TILE_READY = 6,
     EP_ARRAY_SLOT_TO_POOL_ROW = 7,
     EP_ARRAY_POOL_RECV_TOKEN = 8,
-    EP_ARRAY_TOPK_WEIGHTS = 9
+    EP_ARRAY_TOPK_WEIGHTS = 9,
+    EP_ARRAY_Y_DONE = 10
 } ep_array;
 
 /* Byte size of a metadata array for the current layout. */
@@ -255,7 +329,9 @@ ep_status ep_handle_sync_status(ep_handle* h, hipStream_t stream);
  * borrowed bf16 slab [num_tokens, hidden] and row r is read from slab row
  * pool_recv_token[r] (the indexed consumer of [BORROW]).  A wait longer than spin_limit_us gives up
  * on that tile and sets EP_ERR_TIMEOUT in the error word, so it always ends.
- * The caller orders it after ep_layout (e.g. with an event). */
+ * The caller orders it after ep_layout (e.g. with an event).  flags:
+ * EP_DISPATCH_FP8 (row-major UE8M0 scales only; other EP_SCALE_* flags are
+ * EP_ERR_UNSUPPORTED), EP_CONSUME_GATHER, EP_CONSUME_SIGNAL_DONE. */
 ep_status ep_tile_consume(const ep_handle* h, uint32_t seq, const void* pool,
                           const uint8_t* pool_scales, int32_t hidden, uint32_t flags,
                           void* out, int32_t workgroups, uint32_t spin_limit_us,

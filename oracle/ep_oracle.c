@@ -421,7 +421,9 @@ void eo_quantize_row_f32scale(const uint16_t* x, int32_t H, uint8_t* q, float* s
 }
 
 /* Inverse for float32 scales: bf16(float(value(q) * s)), one float product
- * rounded to nearest even in bf16; NaN codes give a quiet NaN with their sign. */
+ * rounded to nearest even in bf16.  NaN codes, and NaN products (a zero code
+ * times an infinite scale), give a quiet NaN with the code's sign (the scale
+ * is never negative; IEEE leaves the sign of such a NaN open). */
 void eo_dequant_row_f32scale(const uint8_t* q, const float* scales, int32_t H, uint16_t* out)
 {
     for (int32_t c = 0; c < H; ++c) {
@@ -434,6 +436,9 @@ void eo_dequant_row_f32scale(const uint8_t* q, const float* scales, int32_t H, u
         if (b & 0x80)
             v = -v;
         float p = v * scales[c / 128];
-        out[c] = eo_f32_to_bf16(p);
+        if (isnan(p))
+            out[c] = (uint16_t)((b & 0x80 ? 0x8000 : 0) | 0x7FC0);
+        else
+            out[c] = eo_f32_to_bf16(p);
     }
 }

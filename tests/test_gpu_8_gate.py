@@ -1,0 +1,154 @@
+"""Per-token combine gate (StreamEP README, opening paragraph: combine is
+gated per receive token by y_done_per_token, so it can start on a token as
+soon as that token's expert compute has drained).
+
+The expert-output producer is the tile consumer stand-in with
+EP_CONSUME_SIGNAL_DONE: it copies (or dequantises) each tile's rows into
+expert_out, publishes them at device scope and adds 1 to the done count of
+each row's token.  ep_combine_gated waits per token for round * (unmasked
+slots) and must then equal the ungated combine bit for bit.  Every wait is
+bounded; an expired wait shows up as EP_ERR_TIMEOUT, never as a hang."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import (say, inputs, new_handle, device_routing, to_dev_bf16, bits_of, dev,
+                         POISON_BF16)
+
+pytestmark = pytest.mark.gpu
+
+SPIN_US = 3_000_000
+
+
+def _slots_per_token(L, T, K):
+    return (L["slot_to_pool_row"].reshape(T, K) >= 0).sum(1).astype(np.uint32)
+
+
+def _expected_y(d, L, fp8):
+    """Oracle combine of the producer's rows: copies of x (bf16) or the
+    dequantised FP8 rows; padding rows are NaN and never read."""
+    recv = L["pool_recv_token"]
+    H = d["x"].shape[1]
+    eo = np.full((recv.size, H), 0x7FC0, np.uint16)
+    real = np.flatnonzero(recv >= 0)
+    if fp8:
+        q, s = oracle.dispatch_fp8(d["x"], recv)
+        eo[real] = oracle.dequant_rows(q[real], s[real])
+    else:
+        eo[real] = d["x"][recv[real]]
+    return oracle.combine(eo, L["slot_to_pool_row"], d["topk_weights"])
+
+
+def _pipeline(name, tokens, fp8, rounds=1, one_stream=False):
+    """layout on A; then per round: dispatch (tile_ready) on A, the producer on
+    B and the gated combine on C, enqueued in that order.  Streams may share a
+    hardware queue, which runs their kernels one after another, so the
+    enqueue order is always one that also works serialised.  The producer
+    waits only for the layout and overlaps the dispatch; the combine starts
+    once the dispatch has ended (no dispatch workgroup has to find room beside
+    spinning combine waves) and waits on tokens the producer is still
+    writing.  With one_stream everything runs in order on A."""
+    import combine_ep_layout_amd as ep
+    cfg, d = inputs(name, tokens)
+    T, K, H = cfg.tokens, cfg.top_k, cfg.hidden
+    L = oracle.layout(d["topk_idx"], cfg.num_experts, cfg.block_m)
+    want = _expected_y(d, L, fp8)
+    h = new_handle(cfg)
+    sa = torch.cuda.current_stream()
+    sb, sc = (sa, sa) if one_stream else (torch.cuda.Stream(), torch.cuda.Stream())  # default priority
+    epoch = h.layout(*device_routing(d))
+    x = to_dev_bf16(d["x"])
+    pool, scales = h.new_pool(H, fp8=fp8)
+    for rnd in range(1, rounds + 1):
+        eo = torch.zeros(h.capacity_rows, H, dtype=torch.bfloat16, device=dev())
+        y = torch.full((T, H), POISON_BF16 - 0x10000, dtype=torch.int16, device=dev()).view(torch.bfloat16)
+        ev = torch.cuda.Event()
+        ev.record(sa)                       # layout, eo's and y's fills are done
+        sb.wait_event(ev)
+        h.dispatch(x, pool, scales, fp8=fp8, tile_ready=True, stream=sa)
+        h.tile_consume(rnd, pool, scales, H, eo, fp8=fp8, workgroups=16,
+                       spin_limit_us=SPIN_US, stream=sb, signal_done=True)
+        if not one_stream:
+            ev_d = torch.cuda.Event()
+            ev_d.record(sa)
+            sc.wait_event(ev_d)
+        h.combine_gated(epoch, eo, round=rnd, y=y, spin_limit_us=SPIN_US, stream=sc)
+        for s in (sa, sb, sc):
+            s.synchronize()
+        assert h.sync_status() == ep.EP_OK, "a bounded wait timed out"
+        done = h.array("y_done_per_token").cpu().numpy().view(np.uint32)
+        assert np.array_equal(done, rnd * _slots_per_token(L, T, K))
+        assert np.array_equal(bits_of(y), want)
+        # the ungated combine of the same rows agrees bit for bit
+        assert np.array_equal(bits_of(h.combine(epoch, eo)), want)
+    h.close()
+
+
+@pytest.mark.parametrize("name,tokens,fp8", [("tiny", -1, False), ("decode", -1, True),
+                                              ("share", 3000, False), ("prefill", 1000, False)])
+def test_gate_after_producer(name, tokens, fp8):
+    say(f"[gate] producer finishes first: {name} tokens={tokens} fp8={fp8}")
+    _pipeline(name, tokens, fp8, one_stream=True)
+
+
+@pytest.mark.parametrize("name,tokens,fp8", [("decode", -1, True), ("share", 3000, False),
+                                              ("stream", 2000, True)])
+def test_gate_concurrent_streams(name, tokens, fp8):
+    """Producer and gated combine run at the same time on two streams, next to
+    the dispatch on a third; the combine waits on tokens whose rows are still
+    being written."""
+    say(f"[gate] concurrent: {name} tokens={tokens} fp8={fp8}")
+    _pipeline(name, tokens, fp8)
+
+
+def test_gate_rounds_without_relayout():
+    say("[gate] three producer rounds on one layout, counts never reset")
+    _pipeline("share", 2000, False, rounds=3)
+
+
+def test_gate_timeout_is_bounded_and_reported():
+    """No producer runs: every token with a slot times out (the first expiry
+    makes the others give up at once) and keeps its old y row; tokens without
+    a slot are written (+0).  The handle works normally afterwards."""
+    import combine_ep_layout_amd as ep
+    say("[gate] timeout with no producer")
+    cfg, d = inputs("share", 3000)
+    T, K, H = cfg.tokens, cfg.top_k, cfg.hidden
+    L = oracle.layout(d["topk_idx"], cfg.num_experts, cfg.block_m)
+    n_t = _slots_per_token(L, T, K)
+    assert (n_t == 0).any() and (n_t > 0).any()
+    h = new_handle(cfg)
+    epoch = h.layout(*device_routing(d))
+    eo = torch.zeros(h.capacity_rows, H, dtype=torch.bfloat16, device=dev())
+    y = torch.full((T, H), POISON_BF16 - 0x10000, dtype=torch.int16, device=dev()).view(torch.bfloat16)
+    h.combine_gated(epoch, eo, round=1, y=y, spin_limit_us=2000)
+    assert h.sync_status() == ep.EP_ERR_TIMEOUT
+    got = bits_of(y)
+    assert (got[n_t == 0] == 0).all()
+    assert (got[n_t > 0] == POISON_BF16).all()
+    assert h.sync_status() == ep.EP_OK                       # cleared by the first read
+    _pipeline("share", 3000, False)
+    h.close()
+
+
+def test_gate_rejections():
+    import combine_ep_layout_amd as ep
+    say("[gate] rejections")
+    lib = ep.library()
+    cfg, d = inputs("tiny")
+    h = new_handle(cfg)
+    epoch = h.layout(*device_routing(d))
+    H = cfg.hidden
+    eo = torch.zeros(h.capacity_rows, H, dtype=torch.bfloat16, device=dev())
+    y = torch.empty(cfg.tokens, H, dtype=torch.bfloat16, device=dev())
+    P = lambda t: t.data_ptr()
+    assert lib.ep_combine_gated(h.raw, epoch, P(eo), H, P(y), 0, 1000, None) == ep.EP_ERR_INVALID_ARGUMENT
+    assert lib.ep_combine_gated(h.raw, epoch + 1, P(eo), H, P(y), 1, 1000, None) == ep.EP_ERR_HANDLE_STATE
+    assert lib.ep_combine_gated(h.raw, epoch, P(eo) + 8, H, P(y), 1, 1000, None) == ep.EP_ERR_INVALID_ARGUMENT
+    h.borrow(to_dev_bf16(d["x"]))
+    assert lib.ep_combine_gated(h.raw, epoch, P(eo), H, P(y), 1, 1000, None) == ep.EP_ERR_HANDLE_STATE
+    h.release()
+    torch.cuda.synchronize()
+    assert h.sync_status() == ep.EP_OK
+    h.close()

@@ -230,6 +230,10 @@ def test_f32scale_dequant_and_error_bound():
     nanq = np.array([0x7F, 0xFF] + [0] * 126, np.uint8)
     back = oracle.dequant_rows_f32scale(nanq[None, :], np.ones((1, 1), np.float32))[0]
     assert back[0] == 0x7FC0 and back[1] == 0xFFC0
+    # a zero code times an infinite scale (a group whose amax was infinite)
+    zq = np.array([0x00, 0x80, 0x38] + [0] * 125, np.uint8)
+    back = oracle.dequant_rows_f32scale(zq[None, :], np.full((1, 1), np.inf, np.float32))[0]
+    assert back[0] == 0x7FC0 and back[1] == 0xFFC0 and back[2] == 0x7F80      # 1.0 * inf = inf
 
 
 # ------------------------------------------- power-of-two float32 scales ----
