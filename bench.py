@@ -9,6 +9,7 @@ resident in HBM when the timed region starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
                     [--no-cpu-baseline] [--copy-calibration]
+                    [--borrow-compare | --backward | --gate | --fp8-variants]
 
 Prints one JSON line.  Per-kernel times come from HIP events recorded on the
 stream the kernels are launched on (torch's current stream, which is passed
@@ -244,6 +245,150 @@ def backward_bench(cfg, steps: int, warmup: int) -> dict:
             "pct_of_peak": round(100.0 * (b_cb + b_db) / ((cb + db) * 1e-6) / 1e9 / PEAK_GBS, 2)}
 
 
+def _time_us(fn, steps: int, warmup: int, stream) -> float:
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps * 1e3
+
+
+def gate_bench(cfg, steps: int, warmup: int) -> dict:
+    """Per-token combine gate.  (1) The gate's own cost: the gated combine
+    with every token already done vs the plain combine.  (2) A forward pass
+    layout -> dispatch (tile_ready) -> expert-output producer (the tile
+    consumer stand-in, copying each tile to expert_out and signalling its
+    tokens) -> combine, once in order on one stream with the plain combine,
+    once with the producer on a second stream overlapping the dispatch and
+    the gated combine on a third overlapping the producer."""
+    import torch
+    import combine_ep_layout_amd as ep
+    from synth import generate
+    dev = torch.device("cuda", 0)
+    sa = torch.cuda.current_stream()
+    sb, sc = torch.cuda.Stream(), torch.cuda.Stream()          # default priority
+    d = generate(cfg, 0)
+    T, K, H = cfg.tokens, cfg.top_k, cfg.hidden
+    idx = torch.from_numpy(d["topk_idx"]).to(dev)
+    w = torch.from_numpy(d["topk_weights"]).to(dev)
+    x = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    h = ep.EpHandle(T, K, cfg.num_experts, cfg.block_m)
+    pool, _ = h.new_pool(H)
+    eo = torch.zeros(h.capacity_rows, H, dtype=torch.bfloat16, device=dev)
+    y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    wg = 256
+    spin = 2_000_000
+    # (1) gate cost with all tokens done
+    epoch = h.layout(idx, w)
+    seq = h.dispatch(x, pool, tile_ready=True)
+    h.tile_consume(seq, pool, None, H, eo, workgroups=wg, spin_limit_us=spin, signal_done=True)
+    torch.cuda.synchronize()
+    plain = _time_us(lambda: h.combine(epoch, eo, y), steps, warmup, sa)
+    gated = _time_us(lambda: h.combine_gated(epoch, eo, 1, y, spin), steps, warmup, sa)
+
+    # (2) forward pass, in order vs overlapped
+    def in_order():
+        ep_ = h.layout(idx, w)
+        s = h.dispatch(x, pool, tile_ready=True)
+        h.tile_consume(s, pool, None, H, eo, workgroups=wg, spin_limit_us=spin, signal_done=True)
+        h.combine(ep_, eo, y)
+
+    def overlapped():
+        ep_ = h.layout(idx, w)
+        e0 = torch.cuda.Event()
+        e0.record(sa)
+        sb.wait_event(e0)
+        s = h.dispatch(x, pool, tile_ready=True, stream=sa)
+        h.tile_consume(s, pool, None, H, eo, workgroups=wg, spin_limit_us=spin, signal_done=True,
+                       stream=sb)
+        e1 = torch.cuda.Event()
+        e1.record(sa)
+        sc.wait_event(e1)
+        h.combine_gated(ep_, eo, 1, y, spin, stream=sc)
+        e2 = torch.cuda.Event()
+        e2.record(sc)
+        e3 = torch.cuda.Event()
+        e3.record(sb)
+        sa.wait_event(e2)
+        sa.wait_event(e3)
+
+    t_order = _time_us(in_order, steps, warmup, sa)
+    t_over = _time_us(overlapped, steps, warmup, sa)
+    t_order2 = _time_us(in_order, steps, warmup, sa)
+    t_over2 = _time_us(overlapped, steps, warmup, sa)
+    assert h.sync_status() == ep.EP_OK
+    h.close()
+    n_a = int((d["topk_idx"] >= 0).sum())
+    comb_bytes = 8 * T * K + 2 * H * n_a + 2 * H * T
+    return {"metric": "per-token combine gate: gate cost and forward pass with overlap",
+            "unit": "us", "higher_is_better": False, "data": "synthetic", "dtype": "bf16",
+            "config": {"workload": f"{cfg.name}: {T} tokens, hidden {H}, {cfg.num_experts} experts "
+                                   f"{cfg.routing} top-{K}, BLOCK_M {cfg.block_m}",
+                       "producer_workgroups": wg},
+            "combine_us": round(plain, 2), "combine_gated_all_done_us": round(gated, 2),
+            "gate_cost_pct": round(100.0 * (gated - plain) / plain, 2),
+            "combine_gated_gbs": round(comb_bytes / (gated * 1e-6) / 1e9, 1),
+            "forward_in_order_us": round(min(t_order, t_order2), 2),
+            "forward_overlapped_us": round(min(t_over, t_over2), 2),
+            "overlap_change_pct": round(100.0 * (min(t_over, t_over2) - min(t_order, t_order2))
+                                        / min(t_order, t_order2), 2)}
+
+
+def fp8_variants_bench(cfg, steps: int, warmup: int) -> dict:
+    """FP8 dispatch in every scale flavour and layout, and the cast back of
+    the used pool rows.  Dispatch bytes as in the main benchmark (scale bytes
+    1 per group for UE8M0, 4 for float32); cast back reads P rows of codes and
+    their scales and writes P bf16 rows (P = used pool rows)."""
+    import torch
+    import combine_ep_layout_amd as ep
+    from synth import generate
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    d = generate(cfg, 0)
+    T, K, H = cfg.tokens, cfg.top_k, cfg.hidden
+    G = H // 128
+    idx = torch.from_numpy(d["topk_idx"]).to(dev)
+    w = torch.from_numpy(d["topk_weights"]).to(dev)
+    x = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    h = ep.EpHandle(T, K, cfg.num_experts, cfg.block_m)
+    h.layout(idx, w)
+    counts, nt = h.counts_to_host()
+    P = nt * cfg.block_m
+    valid = d["topk_idx"] >= 0
+    n_a = int(valid.sum())
+    t_act = int(valid.any(1).sum())
+    out = torch.empty(P, H, dtype=torch.bfloat16, device=dev)
+    rows = []
+    for kind in ("ue8m0", "f32", "pow2_f32"):
+        for mn in (False, True):
+            pool, scales = h.new_pool(H, fp8=True, scale_kind=kind, mn_major=mn)
+            sb = 1 if kind == "ue8m0" else 4
+            t_d = _time_us(lambda: h.dispatch(x, pool, scales, fp8=True, scale_kind=kind,
+                                              mn_major=mn), steps, warmup, stream)
+            t_c = _time_us(lambda: ep.cast_back(pool, scales, kind, mn, rows=P, out=out),
+                           steps, warmup, stream)
+            b_d = 4 * T * K + 2 * H * t_act + H * n_a + sb * G * n_a
+            b_c = P * H + sb * G * P + 2 * H * P
+            rows.append({"scales": kind, "mn_major": mn,
+                         "dispatch_us": round(t_d, 2), "dispatch_gbs": round(b_d / (t_d * 1e-6) / 1e9, 1),
+                         "cast_back_us": round(t_c, 2), "cast_back_gbs": round(b_c / (t_c * 1e-6) / 1e9, 1)})
+    assert h.sync_status() == ep.EP_OK
+    h.close()
+    return {"metric": "FP8 dispatch and cast back per scale flavour and layout", "unit": "us",
+            "higher_is_better": False, "data": "synthetic", "dtype": "fp8 e4m3fn",
+            "config": {"workload": f"{cfg.name}: {T} tokens, hidden {H}, {cfg.num_experts} experts "
+                                   f"{cfg.routing} top-{K}, BLOCK_M {cfg.block_m}",
+                       "pool_rows_cast_back": P},
+            "results": rows}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -260,6 +405,10 @@ def main() -> int:
                     help="print the borrowed-view vs copy comparison instead")
     ap.add_argument("--backward", action="store_true",
                     help="print the backward (combine_grads + dispatch_grads) measurement instead")
+    ap.add_argument("--gate", action="store_true",
+                    help="print the per-token combine gate measurement instead")
+    ap.add_argument("--fp8-variants", action="store_true",
+                    help="print the FP8 scale flavour / cast back measurement instead")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -278,6 +427,15 @@ def main() -> int:
     if args.backward:
         torch.cuda.set_device(0)
         print(json.dumps(backward_bench(CONFIGS[args.config], args.steps, args.warmup)), flush=True)
+        return 0
+    if args.gate:
+        torch.cuda.set_device(0)
+        print(json.dumps(gate_bench(CONFIGS[args.config], args.steps, args.warmup)), flush=True)
+        return 0
+    if args.fp8_variants:
+        torch.cuda.set_device(0)
+        print(json.dumps(fp8_variants_bench(CONFIGS[args.config], args.steps, args.warmup)),
+              flush=True)
         return 0
 
     cfg = CONFIGS[args.config]

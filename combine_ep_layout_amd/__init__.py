@@ -220,8 +220,11 @@ def cast_back(q: torch.Tensor, scales: torch.Tensor, kind: str = "ue8m0", mn_maj
     if rows > q.shape[0]:
         raise ValueError("rows exceeds q")
     shape, dtype = scale_shape(rows, H, kind, mn_major, scales.shape[1] if mn_major else None)
-    if scales.dtype != dtype or not scales.is_contiguous() or scales.shape[0] != shape[0] \
-            or scales.shape[1] < shape[1]:
+    if mn_major:      # [groups or words, ld >= rows]
+        ok = scales.dim() == 2 and scales.shape[0] == shape[0] and scales.shape[1] >= rows
+    else:             # [>= rows, groups]
+        ok = scales.dim() == 2 and scales.shape[0] >= rows and scales.shape[1] == shape[1]
+    if scales.dtype != dtype or not scales.is_contiguous() or not ok:
         raise ValueError(f"scales must be {dtype} {shape}")
     if out is None:
         out = torch.empty(rows, H, dtype=torch.bfloat16, device=q.device)

@@ -771,95 +771,140 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Per-token gate (StreamEP README, y_done_per_token): wait until the token's
-// done count has reached `target`, then acquire at device scope so the expert
-// rows the producers released are seen.  Bounded: past limit_ticks, or once
-// another wave has timed out (error bit 2), it gives up and returns false.
-__device__ __forceinline__ bool wait_done(const uint32_t* cnt, uint32_t target, uint64_t limit,
-                                          uint32_t* error) {
-    uint32_t v = (uint32_t)uniform_i((int)__hip_atomic_load(cnt, __ATOMIC_RELAXED,
-                                                            __HIP_MEMORY_SCOPE_AGENT));
-    if ((int32_t)(v - target) < 0) {
-        const uint64_t start = wall_clock64();
-        do {
-            const uint32_t err = (uint32_t)uniform_i((int)__hip_atomic_load(
-                error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-            if ((err & 2u) || wall_clock64() - start > limit) {
-                if ((threadIdx.x & (kWave - 1)) == 0) atomicOr(error, 2u);
-                return false;
-            }
-            __builtin_amdgcn_s_sleep(4);
-            v = (uint32_t)uniform_i((int)__hip_atomic_load(cnt, __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_AGENT));
-        } while ((int32_t)(v - target) < 0);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    return true;
-}
-
-// GATE: the per-token gated combine; a token whose gate times out is skipped.
-template <int KT, bool UNIT, bool GATE>
-__global__ __launch_bounds__(256) void k_combine(CombineArgs a, int nseg, int ipb) {
+// One combine work item: segment `seg` of token t (a wave gathers the token's
+// expert rows for that segment, accumulates w * o in fp32 with one fused
+// multiply-add per slot in slot order, and rounds once to bf16).
+template <int KT, bool UNIT>
+__device__ __forceinline__ void combine_item(const CombineArgs& a, int t, int seg, int lane) {
     constexpr int U = EP_COMBINE_UNROLL;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int w = uniform_i(threadIdx.x / kWave);
     const int n16 = a.H / 8;
-    const int i0 = (int)blockIdx.x * ipb;
-    const int i1 = min(a.T * nseg, i0 + ipb);
     const u32x4* eo = (const u32x4*)a.expert_out;
-    u32x4* y = (u32x4*)a.y;
-    for (int it = i0 + w; it < i1; it += 4) {
-        const int t = it / nseg;
-        const int seg = it - t * nseg;
-        int rows[KT];
-        float wt[KT];
+    int rows[KT];
+    float wt[KT];
 #pragma unroll
-        for (int k = 0; k < KT; ++k) {
-            rows[k] = (k < a.K) ? a.slot_to_row[t * a.K + k] : -1;
-            wt[k] = UNIT ? 1.0f : ((k < a.K) ? a.weights[t * a.K + k] : 0.0f);
-        }
-        if constexpr (GATE) {
-            uint32_t n = 0;
+    for (int k = 0; k < KT; ++k) {
+        rows[k] = (k < a.K) ? a.slot_to_row[t * a.K + k] : -1;
+        wt[k] = UNIT ? 1.0f : ((k < a.K) ? a.weights[t * a.K + k] : 0.0f);
+    }
+    const int c0 = seg * (kWave * U) + lane;
+    u32x4 v[KT][U];
 #pragma unroll
-            for (int k = 0; k < KT; ++k) n += rows[k] >= 0 ? 1u : 0u;
-            if (n && !wait_done(a.y_done + t, n * a.round, a.limit_ticks, a.error)) continue;
+    for (int k = 0; k < KT; ++k) {
+        if (rows[k] < 0) continue;
+        const u32x4* src = eo + (int64_t)rows[k] * n16;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + u * kWave;
+            if (c < n16) v[k][u] = load_v<EP_COMBINE_NT_LOADS>(src + c);
         }
-        const int c0 = seg * (kWave * U) + lane;
-        u32x4 v[KT][U];
+    }
+    u32x4* dst = (u32x4*)a.y + (int64_t)t * n16;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
 #pragma unroll
         for (int k = 0; k < KT; ++k) {
             if (rows[k] < 0) continue;
-            const u32x4* src = eo + (int64_t)rows[k] * n16;
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int c = c0 + u * kWave;
-                if (c < n16) v[k][u] = load_v<EP_COMBINE_NT_LOADS>(src + c);
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t p = v[k][u][i];
+                acc[2 * i] = __builtin_fmaf(wt[k], __uint_as_float(p << 16), acc[2 * i]);
+                acc[2 * i + 1] =
+                    __builtin_fmaf(wt[k], __uint_as_float(p & 0xFFFF0000u), acc[2 * i + 1]);
             }
         }
-        u32x4* dst = y + (int64_t)t * n16;
+        u32x4 o;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float acc[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-#pragma unroll
-            for (int k = 0; k < KT; ++k) {
-                if (rows[k] < 0) continue;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t p = v[k][u][i];
-                    acc[2 * i] = __builtin_fmaf(wt[k], __uint_as_float(p << 16), acc[2 * i]);
-                    acc[2 * i + 1] =
-                        __builtin_fmaf(wt[k], __uint_as_float(p & 0xFFFF0000u), acc[2 * i + 1]);
+        for (int i = 0; i < 4; ++i)
+            o[i] = f32_to_bf16_rne(acc[2 * i]) | (f32_to_bf16_rne(acc[2 * i + 1]) << 16);
+        const int c = c0 + u * kWave;
+        if (c < n16) store_row<EP_COMBINE_STORE>(dst, a.H * 2, c, o);
+    }
+}
+
+template <int KT, bool UNIT>
+__global__ __launch_bounds__(256) void k_combine(CombineArgs a, int nseg, int ipb) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = uniform_i(threadIdx.x / kWave);
+    const int i0 = (int)blockIdx.x * ipb;
+    const int i1 = min(a.T * nseg, i0 + ipb);
+    for (int it = i0 + w; it < i1; it += 4) {
+        const int t = it / nseg;
+        combine_item<KT, UNIT>(a, t, it - t * nseg, lane);
+    }
+}
+
+#ifndef EP_GATE_TOKENS
+#define EP_GATE_TOKENS 16      // tokens per workgroup of the gated combine (<= 64)
+#endif
+static_assert(EP_GATE_TOKENS >= 1 && EP_GATE_TOKENS <= 64, "one wave lane per gated token");
+#ifndef EP_GATE_WAVES
+#define EP_GATE_WAVES 16       // waves per workgroup of the gated combine
+#endif
+#ifndef EP_GATE_STRIDED
+#define EP_GATE_STRIDED 1      // 1: a workgroup's tokens are strided by the grid size
+#endif
+
+// Per-token gate (StreamEP README, y_done_per_token).  A workgroup takes
+// EP_GATE_TOKENS tokens, strided by the grid size so that the workgroups in
+// flight cover a compact window of tokens (their expert rows are then close
+// together in each expert's block, as in the plain combine); one acquire per
+// workgroup keeps the cache invalidations few.  Wave 0 waits, one lane per token, until
+// every token's done count has reached round * (its unmasked slots), then
+// acquires at device scope once for the batch, so the expert rows the
+// producers released are seen; the workgroup then combines the batch.  The
+// wait is bounded: past limit_ticks, or once another workgroup has timed out
+// (error bit 2), it gives up, sets bit 2, and the batch's tokens that were
+// not done are skipped (their y rows keep their contents).
+template <int KT>
+__global__ __launch_bounds__(64 * EP_GATE_WAVES) void k_combine_gated(CombineArgs a, int nseg) {
+    __shared__ uint64_t s_done;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = uniform_i(threadIdx.x / kWave);
+    const int b = (int)blockIdx.x, nb = (int)gridDim.x;
+    // batch slot j holds token b + j * nb (strided: the workgroups in flight
+    // cover a compact window of tokens) or b * EP_GATE_TOKENS + j
+    auto token_of = [&](int j) {
+        return EP_GATE_STRIDED ? b + j * nb : b * EP_GATE_TOKENS + j;
+    };
+    if (w == 0) {
+        const int t = token_of(lane);
+        const bool mine = lane < EP_GATE_TOKENS && t < a.T;
+        uint32_t target = 0;
+        if (mine)
+            for (int k = 0; k < a.K; ++k) target += a.slot_to_row[t * a.K + k] >= 0 ? 1u : 0u;
+        target *= a.round;
+        auto done = [&]() {
+            return !mine || target == 0 ||
+                   (int32_t)(__hip_atomic_load(a.y_done + t, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT) - target) >= 0;
+        };
+        uint64_t mask = __ballot(done());
+        if (mask != ~0ull) {
+            const uint64_t start = wall_clock64();
+            while (true) {
+                __builtin_amdgcn_s_sleep(8);
+                mask = __ballot(done());
+                if (mask == ~0ull) break;
+                const uint32_t err = (uint32_t)uniform_i((int)__hip_atomic_load(
+                    a.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                if ((err & 2u) || wall_clock64() - start > a.limit_ticks) {
+                    if (lane == 0) atomicOr(a.error, 2u);
+                    break;
                 }
             }
-            u32x4 o;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                o[i] = f32_to_bf16_rne(acc[2 * i]) | (f32_to_bf16_rne(acc[2 * i + 1]) << 16);
-            const int c = c0 + u * kWave;
-            if (c < n16) store_row<EP_COMBINE_STORE>(dst, a.H * 2, c, o);
         }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        if (lane == 0) s_done = mask;
+    }
+    __syncthreads();
+    const uint64_t mask = s_done;
+    for (int i = w; i < EP_GATE_TOKENS * nseg; i += EP_GATE_WAVES) {
+        const int j = i / nseg;
+        const int t = token_of(j);
+        if (t < a.T && ((mask >> j) & 1ull)) combine_item<KT, false>(a, t, i - j * nseg, lane);
     }
 }
 
@@ -1157,10 +1202,15 @@ template <int KT, bool UNIT, bool GATE>
 hipError_t combine_kt(const CombineArgs& a, hipStream_t st) {
     const int per_seg = kWave * EP_COMBINE_UNROLL * 8;
     const int nseg = (a.H + per_seg - 1) / per_seg;
+    if constexpr (GATE) {
+        const int grid = (a.T + EP_GATE_TOKENS - 1) / EP_GATE_TOKENS;
+        hipLaunchKernelGGL((k_combine_gated<KT>), dim3(grid), dim3(64 * EP_GATE_WAVES), 0, st, a, nseg);
+        return hipGetLastError();
+    }
     const int ipb = items_per_block(nseg, false);
     const int64_t items = (int64_t)a.T * nseg;
     const int grid = (int)((items + ipb - 1) / ipb);
-    hipLaunchKernelGGL((k_combine<KT, UNIT, GATE>), dim3(grid), dim3(256), 0, st, a, nseg, ipb);
+    hipLaunchKernelGGL((k_combine<KT, UNIT>), dim3(grid), dim3(256), 0, st, a, nseg, ipb);
     return hipGetLastError();
 }
 
