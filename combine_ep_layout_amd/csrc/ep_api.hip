@@ -18,6 +18,7 @@ struct ep_handle {
     int32_t ws_blocks;        // workgroups the layout workspace holds
     int device;
     int wall_khz;             // device wall-clock rate (kHz)
+    int num_cu;               // compute units of the device
     void* block;              // single device allocation holding every array
     int32_t* counts;
     int32_t* offsets;
@@ -130,11 +131,13 @@ ep_status ep_handle_create(const ep_config* cfg, ep_handle** out) {
     h->round = 0;
 
     if (hipGetDevice(&h->device) != hipSuccess ||
-        hipDeviceGetAttribute(&h->wall_khz, hipDeviceAttributeWallClockRate, h->device) != hipSuccess) {
+        hipDeviceGetAttribute(&h->wall_khz, hipDeviceAttributeWallClockRate, h->device) != hipSuccess ||
+        hipDeviceGetAttribute(&h->num_cu, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess) {
         delete h;
         return EP_ERR_HIP;
     }
     if (h->wall_khz <= 0) h->wall_khz = 100000;
+    if (h->num_cu <= 0) h->num_cu = 1;
 
     // one allocation, every array 256-byte aligned
     struct Part { void** dst; size_t bytes; };
@@ -291,6 +294,7 @@ ep_status ep_dispatch(ep_handle* h, const void* x, int32_t hidden, void* pool,
     a.max_tiles = h->max_tiles;
     a.tile_bits = 1;
     while ((1 << a.tile_bits) <= h->max_tiles) ++a.tile_bits;
+    a.stream_grid = h->num_cu * EP_STREAM_WG_PER_CU;
     a.seq = h->seq + 1;
     a.round = h->round + (ready ? 1u : 0u);
     ep_status st = hip_status(epk::launch_dispatch(a, fp8, ready, stream));

@@ -11,6 +11,10 @@ namespace epk {
 #define EP_LAYOUT_SLOTS_PER_LANE 2
 #endif
 
+#ifndef EP_STREAM_WG_PER_CU
+#define EP_STREAM_WG_PER_CU 1  // streaming dispatch: 1024-thread workgroups per compute unit
+#endif
+
 // Slots ranked by one layout workgroup (1024 threads x EP_LAYOUT_SLOTS_PER_LANE).
 // Up to this many slots the whole layout runs in a single workgroup and launch.
 constexpr int kLayoutSlotsPerBlock = 1024 * EP_LAYOUT_SLOTS_PER_LANE;
@@ -68,6 +72,7 @@ struct DispatchArgs {
     uint32_t round;             // TILE_READY dispatches since the layout (1, 2, ...)
     int32_t max_tiles;
     int32_t tile_bits;          // bits of a tile id, max_tiles included
+    int32_t stream_grid;        // workgroups of a streaming dispatch (resident)
 };
 
 struct CombineArgs {

@@ -45,7 +45,10 @@
 #define EP_ITEMS_PER_WAVE 1    // work items per wave outside streaming mode
 #endif
 #ifndef EP_STREAM_TOKENS
-#define EP_STREAM_TOKENS 64    // whole tokens per 1024-thread workgroup in streaming mode
+#define EP_STREAM_TOKENS 64    // tokens per released chunk in streaming mode
+#endif
+#ifndef EP_STREAM_THREADS
+#define EP_STREAM_THREADS 1024 // threads per streaming workgroup
 #endif
 #ifndef EP_DISPATCH_STORE
 #define EP_DISPATCH_STORE 1    // pool stores outside streaming: see store_row
@@ -376,18 +379,26 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
 
 // ------------------------------------------------------------- dispatch ---
 
-// Streaming release of the rows a workgroup has just stored for its tokens
-// [t0, t1).  Every wave waits until its own stores have reached the cache,
-// the workgroup meets at a barrier, and one wave then publishes them all at
-// device scope with a single release fence and makes the arrival adds: rows
-// of one expert written for a contiguous token range are contiguous, so it
-// adds once per (expert, tile) touched.  The add that brings a tile to its
-// target acquires the other workgroups' releases and release-stores the
-// sequence number into tile_ready[tile]; a consumer that acquire-loads
-// tile_ready then sees every row of the tile.
-__device__ void release_block(const DispatchArgs& a, int t0, int t1, int* s_lo, int* s_hi) {
+// Streaming release of the rows a workgroup has just stored for the tokens
+// [t0, t1) of one chunk.  Every wave waits until its own stores have reached
+// the cache and the workgroup meets at a barrier (which also means wave 0 has
+// finished the previous chunk's adds); the per-expert row ranges of the chunk
+// are gathered in LDS; then wave 0 alone publishes them at device scope with a
+// single release fence and makes the arrival adds while the other waves go on
+// with the next chunk.  Rows of one expert written for a contiguous token range
+// are contiguous, so it adds once per (expert, tile) touched.  The add that
+// brings a tile to its target acquires the other workgroups' releases and
+// release-stores the sequence number into tile_ready[tile]; a consumer that
+// acquire-loads tile_ready then sees every row of the tile.
+__device__ void release_chunk(const DispatchArgs& a, int t0, int t1, int* s_lo, int* s_hi) {
     __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
     const int tid = threadIdx.x;
+    for (int e = tid; e < a.E; e += blockDim.x) {
+        s_lo[e] = INT_MAX;
+        s_hi[e] = -1;
+    }
+    __syncthreads();
     const int s0 = t0 * a.K, s1 = t1 * a.K;
     for (int s = s0 + tid; s < s1; s += blockDim.x) {
         const int r = a.slot_to_row[s];
@@ -416,14 +427,6 @@ __device__ void release_block(const DispatchArgs& a, int t0, int t1, int* s_lo, 
                                    __HIP_MEMORY_SCOPE_AGENT);
             }
         }
-    }
-}
-
-// Clears the LDS per-expert row ranges of a streaming workgroup.
-__device__ __forceinline__ void clear_ranges(int E, int* s_lo, int* s_hi) {
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        s_lo[e] = INT_MAX;
-        s_hi[e] = -1;
     }
 }
 
@@ -474,15 +477,15 @@ __global__ __launch_bounds__(1024) void k_dispatch_bf16(DispatchArgs a, int nseg
     const int lane = threadIdx.x & (kWave - 1);
     const int w = uniform_i(threadIdx.x / kWave);
     const int n16 = a.H / 8;
-    const int i0 = (int)blockIdx.x * ipb;
-    const int i1 = min(a.T * nseg, i0 + ipb);
     const u32x4* x = (const u32x4*)a.x;
     u32x4* pool = (u32x4*)a.pool;
     const int nw = (int)blockDim.x / kWave;
-    if constexpr (STREAM) {
-        clear_ranges(a.E, smem, smem + a.E);
-        __syncthreads();
-    }
+    // streaming: chunks of EP_STREAM_TOKENS tokens in global order, strided
+    // over a resident grid, each released as soon as it is stored
+    const int nchunk = STREAM ? (a.T + EP_STREAM_TOKENS - 1) / EP_STREAM_TOKENS : 1;
+    for (int ch = STREAM ? (int)blockIdx.x : 0; ch < nchunk; ch += STREAM ? (int)gridDim.x : 1) {
+    const int i0 = STREAM ? ch * EP_STREAM_TOKENS * nseg : (int)blockIdx.x * ipb;
+    const int i1 = min(a.T * nseg, STREAM ? i0 + EP_STREAM_TOKENS * nseg : i0 + ipb);
     for (int it = i0 + w; it < i1; it += nw) {
         const int t = it / nseg;
         const int seg = it - t * nseg;
@@ -507,7 +510,8 @@ __global__ __launch_bounds__(1024) void k_dispatch_bf16(DispatchArgs a, int nseg
             }
         }
     }
-    if constexpr (STREAM) release_block(a, i0 / nseg, i1 / nseg, smem, smem + a.E);
+    if constexpr (STREAM) release_chunk(a, i0 / nseg, i1 / nseg, smem, smem + a.E);
+    }
 }
 
 // --- FP8 e4m3fn with UE8M0 scales, from bf16 bit patterns, integer only ---
@@ -674,15 +678,13 @@ __global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg,
     const int nunit = a.H / 16;          // 16 channels (32 bytes in, 16 bytes out) per unit
     const int ngrp = a.H / 128;
     const bool pack8 = (ngrp & 7) == 0 && ((uintptr_t)a.scales & 7) == 0;
-    const int i0 = (int)blockIdx.x * ipb;
-    const int i1 = min(a.T * nseg, i0 + ipb);
     const u32x4* x = (const u32x4*)a.x;
     u32x4* pool = (u32x4*)a.pool;
     const int nw = (int)blockDim.x / kWave;
-    if constexpr (STREAM) {
-        clear_ranges(a.E, smem, smem + a.E);
-        __syncthreads();
-    }
+    const int nchunk = STREAM ? (a.T + EP_STREAM_TOKENS - 1) / EP_STREAM_TOKENS : 1;
+    for (int ch = STREAM ? (int)blockIdx.x : 0; ch < nchunk; ch += STREAM ? (int)gridDim.x : 1) {
+    const int i0 = STREAM ? ch * EP_STREAM_TOKENS * nseg : (int)blockIdx.x * ipb;
+    const int i1 = min(a.T * nseg, STREAM ? i0 + EP_STREAM_TOKENS * nseg : i0 + ipb);
     for (int it = i0 + w; it < i1; it += nw) {
         const int t = it / nseg;
         const int seg = it - t * nseg;
@@ -760,7 +762,8 @@ __global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg,
             store_scales<KT, STREAM>(a, rows, c, nunit, ngrp, pack8, sbyte, sval);
         }
     }
-    if constexpr (STREAM) release_block(a, i0 / nseg, i1 / nseg, smem, smem + a.E);
+    if constexpr (STREAM) release_chunk(a, i0 / nseg, i1 / nseg, smem, smem + a.E);
+    }
 }
 
 // -------------------------------------------------------------- combine ---
@@ -1176,9 +1179,10 @@ hipError_t dispatch_kt(const DispatchArgs& a, bool fp8, bool stream, hipStream_t
     const int nseg = (a.H + per_seg - 1) / per_seg;
     const int ipb = items_per_block(nseg, stream);
     const int64_t items = (int64_t)a.T * nseg;
-    const int grid = (int)((items + ipb - 1) / ipb);
+    int grid = (int)((items + ipb - 1) / ipb);
+    if (stream && grid > a.stream_grid) grid = a.stream_grid;      // resident grid, chunks strided
     const size_t lds = stream ? 2 * sizeof(int) * (size_t)a.E : 0;
-    const dim3 block(stream ? 1024 : 256);
+    const dim3 block(stream ? EP_STREAM_THREADS : 256);
     if (fp8) {
         const bool f32q = a.scale_kind == kScaleF32;
         if (stream && f32q)
