@@ -367,20 +367,27 @@ def fp8_variants_bench(cfg, steps: int, warmup: int) -> dict:
     n_a = int(valid.sum())
     t_act = int(valid.any(1).sum())
     out = torch.empty(P, H, dtype=torch.bfloat16, device=dev)
-    rows = []
-    for kind in ("ue8m0", "f32", "pow2_f32"):
-        for mn in (False, True):
-            pool, scales = h.new_pool(H, fp8=True, scale_kind=kind, mn_major=mn)
-            sb = 1 if kind == "ue8m0" else 4
+    combos = [(kind, mn) for kind in ("ue8m0", "f32", "pow2_f32") for mn in (False, True)]
+    pools = {c: h.new_pool(H, fp8=True, scale_kind=c[0], mn_major=c[1]) for c in combos}
+    best = {}
+    for rep in range(2):                  # two passes over every combination, best of each
+        for kind, mn in combos:
+            pool, scales = pools[(kind, mn)]
             t_d = _time_us(lambda: h.dispatch(x, pool, scales, fp8=True, scale_kind=kind,
                                               mn_major=mn), steps, warmup, stream)
             t_c = _time_us(lambda: ep.cast_back(pool, scales, kind, mn, rows=P, out=out),
                            steps, warmup, stream)
-            b_d = 4 * T * K + 2 * H * t_act + H * n_a + sb * G * n_a
-            b_c = P * H + sb * G * P + 2 * H * P
-            rows.append({"scales": kind, "mn_major": mn,
-                         "dispatch_us": round(t_d, 2), "dispatch_gbs": round(b_d / (t_d * 1e-6) / 1e9, 1),
-                         "cast_back_us": round(t_c, 2), "cast_back_gbs": round(b_c / (t_c * 1e-6) / 1e9, 1)})
+            o = best.get((kind, mn), (1e18, 1e18))
+            best[(kind, mn)] = (min(o[0], t_d), min(o[1], t_c))
+    rows = []
+    for kind, mn in combos:
+        t_d, t_c = best[(kind, mn)]
+        sb = 1 if kind == "ue8m0" else 4
+        b_d = 4 * T * K + 2 * H * t_act + H * n_a + sb * G * n_a
+        b_c = P * H + sb * G * P + 2 * H * P
+        rows.append({"scales": kind, "mn_major": mn,
+                     "dispatch_us": round(t_d, 2), "dispatch_gbs": round(b_d / (t_d * 1e-6) / 1e9, 1),
+                     "cast_back_us": round(t_c, 2), "cast_back_gbs": round(b_c / (t_c * 1e-6) / 1e9, 1)})
     assert h.sync_status() == ep.EP_OK
     h.close()
     return {"metric": "FP8 dispatch and cast back per scale flavour and layout", "unit": "us",

@@ -38,6 +38,9 @@
 #ifndef EP_FP8_UNROLL
 #define EP_FP8_UNROLL 2        // 16-channel units per lane per FP8 dispatch work item
 #endif
+#ifndef EP_FP8_PACK8
+#define EP_FP8_PACK8 1         // UE8M0 scale bytes of a full step as one 64-bit store per row
+#endif
 #ifndef EP_COMBINE_UNROLL
 #define EP_COMBINE_UNROLL 2    // 16-byte chunks per lane per combine work item
 #endif
@@ -677,7 +680,8 @@ __global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg,
     const int w = uniform_i(threadIdx.x / kWave);
     const int nunit = a.H / 16;          // 16 channels (32 bytes in, 16 bytes out) per unit
     const int ngrp = a.H / 128;
-    const bool pack8 = (ngrp & 7) == 0 && ((uintptr_t)a.scales & 7) == 0;
+    // (the streaming release is faster with plain byte stores written back by its fence)
+    const bool pack8 = EP_FP8_PACK8 && !STREAM && (ngrp & 7) == 0 && ((uintptr_t)a.scales & 7) == 0;
     const u32x4* x = (const u32x4*)a.x;
     u32x4* pool = (u32x4*)a.pool;
     const int nw = (int)blockDim.x / kWave;
@@ -999,6 +1003,19 @@ __device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t code, int e) {
     return sign | f32_to_bf16_rne(v);
 }
 
+// The same value built directly as a bf16 pattern when the code is normal and
+// the scaled value is a normal bf16: 1.m * 2^(ef-7+e) has 4 significant bits,
+// so it is exact, with biased exponent ef + e + 120.  Everything else takes
+// the general path above.
+__device__ __forceinline__ uint32_t e4m3_to_bf16_fast(uint32_t code, int e) {
+    const uint32_t mag = code & 0x7Fu;
+    const uint32_t ef = mag >> 3;
+    const uint32_t be = ef + (uint32_t)(e + 120);
+    if (ef != 0u && mag != 0x7Fu && be - 1u < 254u)
+        return ((code & 0x80u) << 8) | (be << 7) | ((mag & 7u) << 4);
+    return e4m3_to_bf16(code, e);
+}
+
 __global__ __launch_bounds__(256) void k_tile_consume(ConsumeArgs a) {
     __shared__ int s_go;
     const int tid = threadIdx.x;
@@ -1141,8 +1158,10 @@ __global__ __launch_bounds__(256) void k_cast_back(CastBackArgs a, int nseg) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const uint32_t word = q[u][i];
-                    const uint32_t lo = e4m3_to_bf16(word & 0xFFu, e) | (e4m3_to_bf16((word >> 8) & 0xFFu, e) << 16);
-                    const uint32_t hi = e4m3_to_bf16((word >> 16) & 0xFFu, e) | (e4m3_to_bf16(word >> 24, e) << 16);
+                    const uint32_t lo = e4m3_to_bf16_fast(word & 0xFFu, e) |
+                                        (e4m3_to_bf16_fast((word >> 8) & 0xFFu, e) << 16);
+                    const uint32_t hi = e4m3_to_bf16_fast((word >> 16) & 0xFFu, e) |
+                                        (e4m3_to_bf16_fast(word >> 24, e) << 16);
                     if (i < 2) { o0[2 * i] = lo; o0[2 * i + 1] = hi; }
                     else { o1[2 * (i - 2)] = lo; o1[2 * (i - 2) + 1] = hi; }
                 }
