@@ -295,6 +295,7 @@ ep_status ep_dispatch(ep_handle* h, const void* x, int32_t hidden, void* pool,
     a.tile_bits = 1;
     while ((1 << a.tile_bits) <= h->max_tiles) ++a.tile_bits;
     a.stream_grid = h->num_cu * EP_STREAM_WG_PER_CU;
+    a.num_cu = h->num_cu;
     a.seq = h->seq + 1;
     a.round = h->round + (ready ? 1u : 0u);
     ep_status st = hip_status(epk::launch_dispatch(a, fp8, ready, stream));

@@ -73,6 +73,7 @@ struct DispatchArgs {
     int32_t max_tiles;
     int32_t tile_bits;          // bits of a tile id, max_tiles included
     int32_t stream_grid;        // workgroups of a streaming dispatch (resident)
+    int32_t num_cu;             // compute units of the device
 };
 
 struct CombineArgs {

@@ -38,6 +38,9 @@
 #ifndef EP_FP8_UNROLL
 #define EP_FP8_UNROLL 2        // 16-channel units per lane per FP8 dispatch work item
 #endif
+#ifndef EP_FP8_SMALL_SPLIT
+#define EP_FP8_SMALL_SPLIT 1   // one-unit FP8 items for batches too small to fill the SIMDs
+#endif
 #ifndef EP_FP8_PACK8
 #define EP_FP8_PACK8 1         // UE8M0 scale bytes of a full step as one 64-bit store per row
 #endif
@@ -671,11 +674,11 @@ __device__ __forceinline__ void store_scales(const DispatchArgs& a, const int (&
 }
 
 // F32Q: float32 scale amax / 448 and codes of x * (448 / amax); otherwise the
-// UE8M0 exponent (stored as a byte, or as the float 2^e).
-template <int KT, bool STREAM, bool F32Q>
+// UE8M0 exponent (stored as a byte, or as the float 2^e).  U: 16-channel
+// units per lane per work item.
+template <int KT, bool STREAM, bool F32Q, int U>
 __global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg, int ipb) {
     extern __shared__ int smem[];
-    constexpr int U = EP_FP8_UNROLL;
     const int lane = threadIdx.x & (kWave - 1);
     const int w = uniform_i(threadIdx.x / kWave);
     const int nunit = a.H / 16;          // 16 channels (32 bytes in, 16 bytes out) per unit
@@ -1194,7 +1197,13 @@ inline int items_per_block(int nseg, bool stream) {
 
 template <int KT>
 hipError_t dispatch_kt(const DispatchArgs& a, bool fp8, bool stream, hipStream_t st) {
-    const int per_seg = fp8 ? kWave * EP_FP8_UNROLL * 16 : kWave * EP_DISPATCH_UNROLL * 8;  // channels
+    // FP8 items of one unit per lane when the batch is too small to give every
+    // SIMD two waves of EP_FP8_UNROLL-unit items (decode): the quantiser's ALU
+    // chain is then split over twice the waves
+    const int n2 = (a.H / 16 + kWave * EP_FP8_UNROLL - 1) / (kWave * EP_FP8_UNROLL);
+    const bool small = EP_FP8_SMALL_SPLIT && fp8 && !stream && (int64_t)a.T * n2 < (int64_t)a.num_cu * 8;
+    const int fu = small ? 1 : EP_FP8_UNROLL;
+    const int per_seg = fp8 ? kWave * fu * 16 : kWave * EP_DISPATCH_UNROLL * 8;  // channels
     const int nseg = (a.H + per_seg - 1) / per_seg;
     const int ipb = items_per_block(nseg, stream);
     const int64_t items = (int64_t)a.T * nseg;
@@ -1203,15 +1212,20 @@ hipError_t dispatch_kt(const DispatchArgs& a, bool fp8, bool stream, hipStream_t
     const size_t lds = stream ? 2 * sizeof(int) * (size_t)a.E : 0;
     const dim3 block(stream ? EP_STREAM_THREADS : 256);
     if (fp8) {
+        constexpr int FU = EP_FP8_UNROLL;
         const bool f32q = a.scale_kind == kScaleF32;
         if (stream && f32q)
-            hipLaunchKernelGGL((k_dispatch_fp8<KT, true, true>), dim3(grid), block, lds, st, a, nseg, ipb);
+            hipLaunchKernelGGL((k_dispatch_fp8<KT, true, true, FU>), dim3(grid), block, lds, st, a, nseg, ipb);
         else if (stream)
-            hipLaunchKernelGGL((k_dispatch_fp8<KT, true, false>), dim3(grid), block, lds, st, a, nseg, ipb);
+            hipLaunchKernelGGL((k_dispatch_fp8<KT, true, false, FU>), dim3(grid), block, lds, st, a, nseg, ipb);
+        else if (f32q && small)
+            hipLaunchKernelGGL((k_dispatch_fp8<KT, false, true, 1>), dim3(grid), block, lds, st, a, nseg, ipb);
         else if (f32q)
-            hipLaunchKernelGGL((k_dispatch_fp8<KT, false, true>), dim3(grid), block, lds, st, a, nseg, ipb);
+            hipLaunchKernelGGL((k_dispatch_fp8<KT, false, true, FU>), dim3(grid), block, lds, st, a, nseg, ipb);
+        else if (small)
+            hipLaunchKernelGGL((k_dispatch_fp8<KT, false, false, 1>), dim3(grid), block, lds, st, a, nseg, ipb);
         else
-            hipLaunchKernelGGL((k_dispatch_fp8<KT, false, false>), dim3(grid), block, lds, st, a, nseg, ipb);
+            hipLaunchKernelGGL((k_dispatch_fp8<KT, false, false, FU>), dim3(grid), block, lds, st, a, nseg, ipb);
     } else {
         if (stream)
             hipLaunchKernelGGL((k_dispatch_bf16<KT, true>), dim3(grid), block, lds, st, a, nseg, ipb);
