@@ -106,21 +106,29 @@ def cpu_baseline(cfg, d, eo_host: np.ndarray, reps: int, tokens: int):
     L0 = oracle.layout(sub["topk_idx"], cfg.num_experts, cfg.block_m)
     ab = algorithmic_bytes(scfg, sub["topk_idx"], L0["expert_counts"], cfg.fp8)
     alg = ab["layout"] + ab["dispatch"] + ab["combine"]
-    times = []
+    times, stages = [], []
     for _ in range(reps):
         t0 = time.perf_counter()
         L = oracle.layout(sub["topk_idx"], cfg.num_experts, cfg.block_m)
+        t1 = time.perf_counter()
         if cfg.fp8:
             oracle.dispatch_fp8(sub["x"], L["pool_recv_token"])
         else:
             oracle.dispatch_bf16(sub["x"], L["pool_recv_token"])
+        t2 = time.perf_counter()
         oracle.combine(eo_host, L["slot_to_pool_row"], sub["topk_weights"])
-        times.append(time.perf_counter() - t0)
+        t3 = time.perf_counter()
+        times.append(t3 - t0)
+        stages.append((t1 - t0, t2 - t1, t3 - t2))
     t = float(np.median(times))
+    st = np.median(np.array(stages), axis=0)
     what = (f"the full {cfg.name} workload ({n} tokens)" if n == cfg.tokens else
             f"the first {n} of {cfg.tokens} tokens of the {cfg.name} workload")
     return {"value": round(alg / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "seconds_per_pass": round(t, 3),
+            "stage_seconds": {"layout": round(float(st[0]), 4), "dispatch": round(float(st[1]), 4),
+                              "combine": round(float(st[2]), 4)},
+            "tokens": n,
             "tokens_per_s": round(n / t, 1),
             "sample": f"{what}, layout + dispatch + combine, median of {reps} passes, "
                       f"one host thread"}
@@ -515,9 +523,34 @@ def main() -> int:
     i_end.record(stream)
     torch.cuda.synchronize()
     ms_instrumented = i_start.elapsed_time(i_end) / args.steps
-    lay = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    dis = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    com = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    lay_s = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
+    dis_s = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
+    com_s = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e3
+    lay, dis, com = (float(v.mean()) / 1e3 for v in (lay_s, dis_s, com_s))
+
+    def pct(v):
+        return {"p10": round(float(np.percentile(v, 10)), 2), "p50": round(float(np.median(v)), 2),
+                "p90": round(float(np.percentile(v, 90)), 2)}
+
+    # Cold per-kernel times: a 1 GiB write between steps evicts L2 and MALL
+    # (the smaller workloads fit in the 256 MB MALL when run back to back).
+    log(f"[bench] timing {args.steps} cold steps")
+    flush = torch.empty(1 << 28, dtype=torch.int32, device=dev)
+    cold = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        flush.fill_(i)
+        step(cold[i])
+    torch.cuda.synchronize()
+    del flush
+    cold_us = {k: pct(np.array([e[j].elapsed_time(e[j + 1]) for e in cold]) * 1e3)
+               for j, k in enumerate(("layout", "dispatch", "combine"))}
+
+    # With the streaming release on, the same dispatch without it, for comparison.
+    no_ready = None
+    if ready:
+        h.layout(idx, w)
+        no_ready = _time_us(lambda: h.dispatch(x, pool, scales, fp8=fp8, tile_ready=False),
+                            args.steps, args.warmup, stream)
 
     counts, _ = h.counts_to_host()
     ab = algorithmic_bytes(cfg, d["topk_idx"], counts, fp8)
@@ -545,6 +578,13 @@ def main() -> int:
         cpu = cpu_baseline(cfg, d, eo_host, args.cpu_reps, ntok)
         del eo_host
 
+    if cpu is not None:
+        # per stage: oracle seconds scaled to the whole workload (linear in
+        # tokens for a sample) over the GPU kernel's seconds
+        scale = T / cpu["tokens"]
+        gpu_s = {"layout": lay * 1e-3, "dispatch": dis * 1e-3, "combine": com * 1e-3}
+        cpu["speedup_per_stage"] = {k: round(cpu["stage_seconds"][k] * scale / gpu_s[k], 1)
+                                    for k in gpu_s}
     mode = "fp8" if fp8 else "bf16"
     out = {
         "metric": METRIC,
@@ -568,6 +608,10 @@ def main() -> int:
         "pct_of_peak": round(100.0 * value / PEAK_GBS, 2),
         "kernels_us": {"layout": round(lay * 1e3, 2), "dispatch": round(dis * 1e3, 2),
                        "combine": round(com * 1e3, 2)},
+        "kernels_us_percentiles": {"layout": pct(lay_s), "dispatch": pct(dis_s),
+                                   "combine": pct(com_s)},
+        "kernels_us_cold": cold_us,
+        "dispatch_us_without_tile_ready": None if no_ready is None else round(no_ready, 2),
         "alg_bytes": {k: ab[k] for k in ("layout", "dispatch", "combine")},
         "routing_stats": {"n_assign": ab["n_a"], "active_tokens": ab["t_act"],
                           "pool_rows": ab["pool_rows"], "max_expert_rows": int(counts.max())},

@@ -71,3 +71,45 @@ def test_null_handle_calls_are_rejected():
     assert lib.ep_handle_destroy(None) == ep.EP_OK
     assert lib.ep_pool_capacity_rows(None) == -1 and lib.ep_max_tiles(None) == -1
     assert lib.ep_handle_create(None, None) == ep.EP_ERR_INVALID_ARGUMENT
+
+
+def test_new_entry_points_reject_before_any_hip_call():
+    import combine_ep_layout_amd as ep
+    lib = ep.library()
+    INV = ep.EP_ERR_INVALID_ARGUMENT
+    assert lib.ep_combine_gated(None, 1, None, 128, None, 1, 1000, None) == INV
+    assert lib.ep_combine_backward(None, 1, None, None, 128, None, None, None) == INV
+    assert lib.ep_dispatch_backward(None, 1, None, 128, None, None) == INV
+    assert lib.ep_tile_consume(None, 1, None, None, 128, 0, None, 1, 1000, None) == INV
+    assert lib.ep_borrow_release(None, None) == INV
+    assert lib.ep_scale_ld(None) == -1
+    # the cast back needs no handle: every check happens on the host first
+    assert lib.ep_fp8_cast_back(None, None, 0, 0, 0, 256, None, None) == ep.EP_OK      # no rows
+    assert lib.ep_fp8_cast_back(None, None, ep.EP_DISPATCH_TILE_READY, 0, 0, 256, None, None) == INV
+    assert lib.ep_fp8_cast_back(None, None, 0, 4, 0, 192, None, None) == INV            # hidden % 128
+    assert lib.ep_fp8_cast_back(None, None, 0, -1, 0, 256, None, None) == INV
+    assert lib.ep_fp8_cast_back(None, None, ep.EP_SCALE_MN_MAJOR, 8, 7, 256, None, None) == INV
+    assert lib.ep_fp8_cast_back(None, None, 0, 4, 0, 256, None, None) == INV             # null buffers
+    assert lib.ep_fp8_cast_back(0x1000, 0x2002, ep.EP_SCALE_F32, 4, 0, 256, 0x3000,
+                                None) == INV                                              # float scales misaligned
+    assert lib.ep_fp8_cast_back(0x1008, 0x2000, 0, 4, 0, 256, 0x3000, None) == INV       # codes not 16-byte aligned
+    assert lib.ep_fp8_cast_back(None, None, 0, 0, 0, 1 << 17, None, None) == ep.EP_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kind,mn,shape,dtype", [
+    ("ue8m0", False, (100, 5), "uint8"),
+    ("f32", False, (100, 5), "float32"),
+    ("pow2_f32", False, (100, 5), "float32"),
+    ("ue8m0", True, (2, 104), "int32"),          # 5 groups packed into 2 words per row
+    ("f32", True, (5, 104), "float32"),
+    ("pow2_f32", True, (5, 104), "float32"),
+])
+def test_scale_shapes_and_flags(kind, mn, shape, dtype):
+    import torch
+    import combine_ep_layout_amd as ep
+    got, dt = ep.scale_shape(100, 640, kind, mn, 104)
+    assert got == shape and dt == getattr(torch, dtype)
+    f = ep.scale_flags(kind, mn)
+    assert bool(f & ep.EP_SCALE_MN_MAJOR) == mn
+    assert bool(f & ep.EP_SCALE_F32) == (kind != "ue8m0")
+    assert bool(f & ep.EP_SCALE_ROUND) == (kind == "pow2_f32")
