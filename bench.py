@@ -532,16 +532,21 @@ def main() -> int:
         return {"p10": round(float(np.percentile(v, 10)), 2), "p50": round(float(np.median(v)), 2),
                 "p90": round(float(np.percentile(v, 90)), 2)}
 
-    # Cold per-kernel times: a 1 GiB write between steps evicts L2 and MALL
-    # (the smaller workloads fit in the 256 MB MALL when run back to back).
+    # Cold per-kernel times: reading 1 GiB between steps replaces L2 and MALL
+    # with clean lines (the smaller workloads fit in the 256 MB MALL when run
+    # back to back).  A read, not a write, so no dirty lines are left to be
+    # written back during the timed kernels.
     log(f"[bench] timing {args.steps} cold steps")
-    flush = torch.empty(1 << 28, dtype=torch.int32, device=dev)
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    sink = torch.empty((), dtype=torch.int64, device=dev)
+    torch.sum(flush, dim=0, dtype=torch.int64, out=sink)        # the fill's dirty lines go out here
+    torch.cuda.synchronize()
     cold = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for i in range(args.steps):
-        flush.fill_(i)
+        torch.sum(flush, dim=0, dtype=torch.int64, out=sink)
         step(cold[i])
     torch.cuda.synchronize()
-    del flush
+    del flush, sink
     cold_us = {k: pct(np.array([e[j].elapsed_time(e[j + 1]) for e in cold]) * 1e3)
                for j, k in enumerate(("layout", "dispatch", "combine"))}
 
