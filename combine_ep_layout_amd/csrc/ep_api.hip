@@ -51,6 +51,10 @@ constexpr int32_t kMaxTopK = 32;
 constexpr int32_t kMaxExperts = 1024;
 constexpr int32_t kMaxBlockM = 4096;
 constexpr int32_t kMaxHidden = 1 << 16;
+// Work items are (token, row segment) pairs, at most 64 segments per row
+// (hidden 65536 in 1024-channel segments), each one wave of a 4-wave
+// workgroup: 2^19 tokens keep every grid below 2^31 threads.
+constexpr int32_t kMaxTokens = 1 << 19;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
@@ -74,7 +78,7 @@ int64_t scale_ld_of(int64_t cap) { return (cap + 3) / 4 * 4; }
 
 ep_status check_config(const ep_config* c) {
     if (!c) return EP_ERR_INVALID_ARGUMENT;
-    if (c->max_tokens < 0 || c->top_k < 1 || c->top_k > kMaxTopK || c->num_experts < 1 ||
+    if (c->max_tokens < 0 || c->max_tokens > kMaxTokens || c->top_k < 1 || c->top_k > kMaxTopK || c->num_experts < 1 ||
         c->num_experts > kMaxExperts || c->block_m < 1 || c->block_m > kMaxBlockM)
         return EP_ERR_INVALID_ARGUMENT;
     const int64_t slots = (int64_t)c->max_tokens * c->top_k;

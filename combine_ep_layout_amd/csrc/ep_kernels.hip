@@ -492,19 +492,37 @@ __global__ __launch_bounds__(1024) void k_dispatch_bf16(DispatchArgs a, int nseg
     for (int ch = STREAM ? (int)blockIdx.x : 0; ch < nchunk; ch += STREAM ? (int)gridDim.x : 1) {
     const int i0 = STREAM ? ch * EP_STREAM_TOKENS * nseg : (int)blockIdx.x * ipb;
     const int i1 = min(a.T * nseg, STREAM ? i0 + EP_STREAM_TOKENS * nseg : i0 + ipb);
+    // software-pipelined as in the FP8 dispatch: the next item's rows and x
+    // segment are loaded before the current one is stored
+    auto fetch = [&](int it_, int (&r)[KT], u32x4 (&v_)[U]) -> bool {
+        const int t_ = it_ / nseg;
+        const int seg_ = it_ - t_ * nseg;
+        if (!load_rows<KT>(a.slot_to_row, t_, a.K, r)) return false;
+        const int c0_ = seg_ * (kWave * U) + lane;
+        const u32x4* src_ = x + (int64_t)t_ * n16;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0_ + u * kWave;
+            if (c < n16) v_[u] = src_[c];
+        }
+        return true;
+    };
+    int rows_n[KT];
+    u32x4 v_n[U];
+    bool any_n = (i0 + w < i1) && fetch(i0 + w, rows_n, v_n);
     for (int it = i0 + w; it < i1; it += nw) {
         const int t = it / nseg;
         const int seg = it - t * nseg;
         int rows[KT];
-        if (!load_rows<KT>(a.slot_to_row, t, a.K, rows)) continue;
-        const int c0 = seg * (kWave * U) + lane;
-        const u32x4* src = x + (int64_t)t * n16;
         u32x4 v[U];
+        const bool any = any_n;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int c = c0 + u * kWave;
-            if (c < n16) v[u] = src[c];
-        }
+        for (int k = 0; k < KT; ++k) rows[k] = rows_n[k];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = v_n[u];
+        any_n = (it + nw < i1) && fetch(it + nw, rows_n, v_n);
+        if (!any) continue;
+        const int c0 = seg * (kWave * U) + lane;
 #pragma unroll
         for (int k = 0; k < KT; ++k) {
             if (rows[k] < 0) continue;
@@ -692,25 +710,46 @@ __global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg,
     for (int ch = STREAM ? (int)blockIdx.x : 0; ch < nchunk; ch += STREAM ? (int)gridDim.x : 1) {
     const int i0 = STREAM ? ch * EP_STREAM_TOKENS * nseg : (int)blockIdx.x * ipb;
     const int i1 = min(a.T * nseg, STREAM ? i0 + EP_STREAM_TOKENS * nseg : i0 + ipb);
+    // a wave's items are software-pipelined: the next item's rows and x
+    // segment are loaded before the current one is quantised and stored
+    auto fetch = [&](int it_, int (&r)[KT], u32x4 (&l)[U], u32x4 (&h)[U]) -> bool {
+        const int t_ = it_ / nseg;
+        const int seg_ = it_ - t_ * nseg;
+        if (!load_rows<KT>(a.slot_to_row, t_, a.K, r)) return false;
+        const int u0_ = seg_ * (kWave * U) + lane;
+        const u32x4* src_ = x + (int64_t)t_ * (a.H / 8);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = u0_ + u * kWave;
+            if (c < nunit) {
+                l[u] = src_[2 * c];
+                h[u] = src_[2 * c + 1];
+            } else {
+                l[u] = u32x4{0, 0, 0, 0};
+                h[u] = u32x4{0, 0, 0, 0};
+            }
+        }
+        return true;
+    };
+    int rows_n[KT];
+    u32x4 lo_n[U], hi_n[U];
+    bool any_n = (i0 + w < i1) && fetch(i0 + w, rows_n, lo_n, hi_n);
     for (int it = i0 + w; it < i1; it += nw) {
         const int t = it / nseg;
         const int seg = it - t * nseg;
         int rows[KT];
-        if (!load_rows<KT>(a.slot_to_row, t, a.K, rows)) continue;
-        const int u0 = seg * (kWave * U) + lane;
-        const u32x4* src = x + (int64_t)t * (a.H / 8);
         u32x4 lo[U], hi[U];
+        const bool any = any_n;
+#pragma unroll
+        for (int k = 0; k < KT; ++k) rows[k] = rows_n[k];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int c = u0 + u * kWave;
-            if (c < nunit) {
-                lo[u] = src[2 * c];
-                hi[u] = src[2 * c + 1];
-            } else {
-                lo[u] = u32x4{0, 0, 0, 0};
-                hi[u] = u32x4{0, 0, 0, 0};
-            }
+            lo[u] = lo_n[u];
+            hi[u] = hi_n[u];
         }
+        any_n = (it + nw < i1) && fetch(it + nw, rows_n, lo_n, hi_n);
+        if (!any) continue;
+        const int u0 = seg * (kWave * U) + lane;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int c = u0 + u * kWave;

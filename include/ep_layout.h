@@ -76,7 +76,7 @@ typedef struct ep_handle ep_handle;
 
 /* Capacities fixed at creation ([ROUND]; the blog's buffer section: the
  * buffer is sized once from max tokens, hidden size and top-k).
- *   max_tokens  >= 0   largest num_tokens ep_layout will accept
+ *   max_tokens  0..2^19 largest num_tokens ep_layout will accept
  *   top_k       1..32  slots per token
  *   num_experts 1..1024 experts handled by this GPU (local experts)
  *   block_m     1..4096 rows per pool tile (BLOCK_M) */

@@ -54,6 +54,7 @@ def test_status_strings():
     (16, 2, 8, 0),         # block_m 0
     (16, 2, 8, 4097),      # block_m above 4096
     (1 << 30, 8, 8, 16),   # capacity beyond int32 rows
+    ((1 << 19) + 1, 1, 1, 1),  # more tokens than one launch's grid allows
 ])
 def test_create_rejects_bad_config_without_gpu(cfg):
     import combine_ep_layout_amd as ep
