@@ -163,23 +163,6 @@ def dequant_rows_f32scale(q: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return out
 
 
-def dispatch_fp8_f32scale(x: np.ndarray, recv_token: np.ndarray,
-                          pool_init: Optional[np.ndarray] = None,
-                          scales_init: Optional[np.ndarray] = None):
-    """FP8 dispatch with float32 scales: each real row holds its token's codes."""
-    x = np.ascontiguousarray(x, dtype=np.uint16)
-    recv = np.ascontiguousarray(recv_token, dtype=np.int32)
-    H = x.shape[1]
-    cap = recv.size
-    pool = (np.zeros((cap, H), np.uint8) if pool_init is None
-            else np.array(pool_init, dtype=np.uint8, copy=True, order="C"))
-    scales = (np.zeros((cap, H // 128), np.float32) if scales_init is None
-              else np.array(scales_init, dtype=np.float32, copy=True, order="C"))
-    for r in np.flatnonzero(recv >= 0):
-        pool[r], scales[r] = quantize_row_f32scale(x[recv[r]])
-    return pool, scales
-
-
 # ------------------------------------------------------ scale formats -------
 # The instagit page ("API Signature and Return Values") names three flavours
 # of the per-128-channel scale: use_ue8m0 (a UE8M0 exponent byte), round_scale
