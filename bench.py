@@ -9,7 +9,7 @@ resident in HBM when the timed region starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
                     [--no-cpu-baseline] [--copy-calibration]
-                    [--borrow-compare | --backward | --gate | --fp8-variants]
+                    [--borrow-compare | --backward | --gate | --fp8-variants | --ceiling]
 
 Prints one JSON line.  "value" is algorithmic bytes moved per step / step
 time, over exactly K steps with nothing else on the stream.  Per-kernel times
@@ -406,6 +406,28 @@ def fp8_variants_bench(cfg, steps: int, warmup: int) -> dict:
             "results": rows}
 
 
+def ceiling_bench(steps: int, warmup: int) -> dict:
+    """Context for the roofline: what plain torch kernels stream on this GPU
+    (a 2 GiB fill, a 2 GiB read-reduce, a 2 GiB -> 2 GiB copy).  These are
+    measured ceilings of simple HBM-bound kernels, not the nameplate peak."""
+    import torch
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    n = 1 << 29                                          # 2 GiB of float32
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    res = {}
+    for name, fn, nbytes in (("write", lambda: b.fill_(3.0), 4 * n),
+                             ("read", lambda: torch.amax(a), 4 * n),
+                             ("copy", lambda: b.copy_(a), 8 * n)):
+        t = min(_time_us(fn, steps, warmup, stream) for _ in range(2))
+        res[name] = {"us": round(t, 1), "GB_s": round(nbytes / (t * 1e-6) / 1e9, 1),
+                     "frac_of_8TBs": round(nbytes / (t * 1e-6) / 1e9 / PEAK_GBS, 4)}
+    del a, b
+    return {"metric": "HBM bandwidth of plain torch kernels (context for the roofline)",
+            "unit": "GB/s", "data": "synthetic", "results": res}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -426,6 +448,8 @@ def main() -> int:
                     help="print the per-token combine gate measurement instead")
     ap.add_argument("--fp8-variants", action="store_true",
                     help="print the FP8 scale flavour / cast back measurement instead")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="print the bandwidth of plain torch fill / read / copy kernels instead")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -448,6 +472,10 @@ def main() -> int:
     if args.gate:
         torch.cuda.set_device(0)
         print(json.dumps(gate_bench(CONFIGS[args.config], args.steps, args.warmup)), flush=True)
+        return 0
+    if args.ceiling:
+        torch.cuda.set_device(0)
+        print(json.dumps(ceiling_bench(args.steps, args.warmup)), flush=True)
         return 0
     if args.fp8_variants:
         torch.cuda.set_device(0)
