@@ -413,7 +413,8 @@ class EpHandle:
     def tile_consume(self, seq: int, pool: torch.Tensor, pool_scales: Optional[torch.Tensor],
                      hidden: int, out: torch.Tensor, fp8: bool = False, workgroups: int = 32,
                      spin_limit_us: int = 2_000_000, stream=None, gather: bool = False,
-                     signal_done: bool = False) -> None:
+                     signal_done: bool = False, scale_kind: str = "ue8m0",
+                     mn_major: bool = False) -> None:
         _require(out, torch.bfloat16, "out", self.device)
         if out.shape[0] < self.capacity_rows or out.shape[1] != hidden:
             raise ValueError("out must be at least [capacity_rows, hidden]")
@@ -424,8 +425,10 @@ class EpHandle:
                 raise ValueError("the gathered slab must be [num_tokens, hidden]")
         elif pool.shape[0] < self.capacity_rows:
             raise ValueError("pool must have at least capacity_rows rows")
-        flags = (EP_DISPATCH_FP8 if fp8 else 0) | (EP_CONSUME_GATHER if gather else 0) | \
-                (EP_CONSUME_SIGNAL_DONE if signal_done else 0)
+        if not fp8 and (scale_kind != "ue8m0" or mn_major):
+            raise ValueError("scale flavours apply to FP8 pools only")
+        flags = (EP_DISPATCH_FP8 | scale_flags(scale_kind, mn_major) if fp8 else 0) | \
+                (EP_CONSUME_GATHER if gather else 0) | (EP_CONSUME_SIGNAL_DONE if signal_done else 0)
         ep_tile_consume(self._h, seq, pool, pool_scales if fp8 else None, hidden, flags, out,
                         workgroups, spin_limit_us, stream)
 

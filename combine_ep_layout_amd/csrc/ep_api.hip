@@ -515,17 +515,18 @@ ep_status ep_handle_sync_status(ep_handle* h, hipStream_t stream) {
 }
 
 ep_status ep_tile_consume(const ep_handle* h, uint32_t seq, const void* pool,
-                          const uint8_t* pool_scales, int32_t hidden, uint32_t flags, void* out,
+                          const void* pool_scales, int32_t hidden, uint32_t flags, void* out,
                           int32_t workgroups, uint32_t spin_limit_us, hipStream_t stream) {
     if (!h) return EP_ERR_INVALID_ARGUMENT;
     if (flags & ~(EP_DISPATCH_FP8 | EP_DISPATCH_TILE_READY | EP_CONSUME_GATHER |
                   EP_CONSUME_SIGNAL_DONE | kScaleFlags))
         return EP_ERR_INVALID_ARGUMENT;
-    if (flags & kScaleFlags) return EP_ERR_UNSUPPORTED;
     const bool fp8 = (flags & EP_DISPATCH_FP8) != 0;
     const bool gather = (flags & EP_CONSUME_GATHER) != 0;
+    if (!fp8 && (flags & kScaleFlags)) return EP_ERR_INVALID_ARGUMENT;
     if (fp8 && gather) return EP_ERR_UNSUPPORTED;
-    if (hidden <= 0 || hidden % 8 != 0 || (fp8 && (hidden % 128 != 0 || !pool_scales)))
+    if (hidden <= 0 || hidden % 8 != 0 ||
+        (fp8 && (hidden % 128 != 0 || !pool_scales || !scales_aligned(pool_scales, flags))))
         return EP_ERR_INVALID_ARGUMENT;
     if (hidden > kMaxHidden) return EP_ERR_UNSUPPORTED;
     if (workgroups < 1 || workgroups > 65536) return EP_ERR_INVALID_ARGUMENT;
@@ -546,6 +547,9 @@ ep_status ep_tile_consume(const ep_handle* h, uint32_t seq, const void* pool,
     a.out = out;
     a.error = h->error;
     a.y_done = (flags & EP_CONSUME_SIGNAL_DONE) ? h->y_done : nullptr;
+    a.scale_kind = scale_kind(flags);
+    a.scale_mn = (flags & EP_SCALE_MN_MAJOR) ? 1 : 0;
+    a.scale_ld = scale_ld_of(h->cap);
     return hip_status(epk::launch_consume(a, workgroups, stream));
 }
 

@@ -105,7 +105,7 @@ struct CombineBwdArgs {
 
 struct ConsumeArgs {
     const void* pool;
-    const uint8_t* scales;
+    const void* scales;
     int32_t H;
     int32_t BM;
     int32_t fp8;
@@ -118,6 +118,9 @@ struct ConsumeArgs {
     void* out;
     uint32_t* error;
     uint32_t* y_done;           // non-null: count each written row for its token
+    int32_t scale_kind;         // FP8 scales: ScaleKind, layout and leading dimension
+    int32_t scale_mn;
+    int64_t scale_ld;
 };
 
 struct CastBackArgs {

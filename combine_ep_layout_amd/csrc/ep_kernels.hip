@@ -1058,8 +1058,77 @@ __device__ __forceinline__ uint32_t e4m3_to_bf16_fast(uint32_t code, int e) {
     return e4m3_to_bf16(code, e);
 }
 
+// ---------------------------------------------------- FP8 decode helpers ---
+
+#ifndef EP_CAST_UNROLL
+#define EP_CAST_UNROLL 2       // 16-channel units per lane per cast-back work item
+#endif
+
+// Exact float32 value of an e4m3fn code magnitude (0..0x7E).
+__device__ __forceinline__ float e4m3_value_f32(uint32_t mag) {
+    const uint32_t ef = mag >> 3, m = mag & 7u;
+    return ef ? __uint_as_float(((ef + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+}
+
+// bf16 of value(code) * s in float32 (one rounded product, then RNE); NaN
+// codes and NaN products give a quiet NaN with the code's sign.
+__device__ __forceinline__ uint32_t e4m3_scaled_to_bf16(uint32_t code, float s) {
+    const uint32_t sign = (code & 0x80u) << 8;
+    const uint32_t mag = code & 0x7Fu;
+    if (mag == 0x7Fu) return sign | 0x7FC0u;
+    const float v = e4m3_value_f32(mag);
+    const float p = ((code & 0x80u) ? -v : v) * s;
+    if ((__float_as_uint(p) & 0x7FFFFFFFu) > 0x7F800000u) return sign | 0x7FC0u;
+    return f32_to_bf16_rne(p);
+}
+
+// Scales of an FP8 pool in any flavour and layout, and the bf16 decode of one
+// 16-code unit of row r, group g, for the tile consumer (the cast back
+// inlines the same decode; as a shared call it measured a few percent slower).
+struct ScaleView {
+    const void* p;
+    int32_t kind;               // ScaleKind
+    int32_t mn;                 // MN-major [G, ld] (UE8M0 packed 4 per word)
+    int64_t ld;
+    int32_t ngrp;               // groups per row
+};
+
+__device__ __forceinline__ void decode_unit(const ScaleView& sv, int64_t r, int g, const u32x4& q,
+                                            u32x4& o0, u32x4& o1) {
+    if (sv.kind == kScaleUe8m0) {
+        const uint32_t byte =
+            sv.mn ? (((const uint32_t*)sv.p)[(int64_t)(g >> 2) * sv.ld + r] >> (8 * (g & 3))) & 0xFFu
+                  : ((const uint8_t*)sv.p)[r * sv.ngrp + g];
+        const int e = (int)byte - 127;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t word = q[i];
+            const uint32_t lo = e4m3_to_bf16_fast(word & 0xFFu, e) |
+                                (e4m3_to_bf16_fast((word >> 8) & 0xFFu, e) << 16);
+            const uint32_t hi = e4m3_to_bf16_fast((word >> 16) & 0xFFu, e) |
+                                (e4m3_to_bf16_fast(word >> 24, e) << 16);
+            if (i < 2) { o0[2 * i] = lo; o0[2 * i + 1] = hi; }
+            else { o1[2 * (i - 2)] = lo; o1[2 * (i - 2) + 1] = hi; }
+        }
+    } else {
+        const float sc = sv.mn ? ((const float*)sv.p)[(int64_t)g * sv.ld + r]
+                               : ((const float*)sv.p)[r * sv.ngrp + g];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t word = q[i];
+            const uint32_t lo = e4m3_scaled_to_bf16(word & 0xFFu, sc) |
+                                (e4m3_scaled_to_bf16((word >> 8) & 0xFFu, sc) << 16);
+            const uint32_t hi = e4m3_scaled_to_bf16((word >> 16) & 0xFFu, sc) |
+                                (e4m3_scaled_to_bf16(word >> 24, sc) << 16);
+            if (i < 2) { o0[2 * i] = lo; o0[2 * i + 1] = hi; }
+            else { o1[2 * (i - 2)] = lo; o1[2 * (i - 2) + 1] = hi; }
+        }
+    }
+}
+
 __global__ __launch_bounds__(256) void k_tile_consume(ConsumeArgs a) {
     __shared__ int s_go;
+    const ScaleView sv{a.scales, a.scale_kind, a.scale_mn, a.scale_ld, a.H / 128};
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int w = uniform_i(tid / kWave);
@@ -1090,24 +1159,9 @@ __global__ __launch_bounds__(256) void k_tile_consume(ConsumeArgs a) {
                 const u32x4* src = (const u32x4*)a.pool + (int64_t)r * nunit;
                 u32x4* dst = (u32x4*)a.out + (int64_t)r * (a.H / 8);
                 for (int c = lane; c < nunit; c += kWave) {
-                    const int e = (int)a.scales[(int64_t)r * (a.H / 128) + (c >> 3)] - 127;
                     const u32x4 q = src[c];
                     u32x4 o0, o1;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const uint32_t word = q[i];
-                        const uint32_t b0 = e4m3_to_bf16(word & 0xFFu, e);
-                        const uint32_t b1 = e4m3_to_bf16((word >> 8) & 0xFFu, e);
-                        const uint32_t b2 = e4m3_to_bf16((word >> 16) & 0xFFu, e);
-                        const uint32_t b3 = e4m3_to_bf16(word >> 24, e);
-                        if (i < 2) {
-                            o0[2 * i] = b0 | (b1 << 16);
-                            o0[2 * i + 1] = b2 | (b3 << 16);
-                        } else {
-                            o1[2 * (i - 2)] = b0 | (b1 << 16);
-                            o1[2 * (i - 2) + 1] = b2 | (b3 << 16);
-                        }
-                    }
+                    decode_unit(sv, r, c >> 3, q, o0, o1);
                     dst[2 * c] = o0;
                     dst[2 * c + 1] = o1;
                 }
@@ -1139,28 +1193,6 @@ __global__ __launch_bounds__(256) void k_tile_consume(ConsumeArgs a) {
 }
 
 // ------------------------------------------------------------ cast back ---
-
-#ifndef EP_CAST_UNROLL
-#define EP_CAST_UNROLL 2       // 16-channel units per lane per cast-back work item
-#endif
-
-// Exact float32 value of an e4m3fn code magnitude (0..0x7E).
-__device__ __forceinline__ float e4m3_value_f32(uint32_t mag) {
-    const uint32_t ef = mag >> 3, m = mag & 7u;
-    return ef ? __uint_as_float(((ef + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
-}
-
-// bf16 of value(code) * s in float32 (one rounded product, then RNE); NaN
-// codes and NaN products give a quiet NaN with the code's sign.
-__device__ __forceinline__ uint32_t e4m3_scaled_to_bf16(uint32_t code, float s) {
-    const uint32_t sign = (code & 0x80u) << 8;
-    const uint32_t mag = code & 0x7Fu;
-    if (mag == 0x7Fu) return sign | 0x7FC0u;
-    const float v = e4m3_value_f32(mag);
-    const float p = ((code & 0x80u) ? -v : v) * s;
-    if ((__float_as_uint(p) & 0x7FFFFFFFu) > 0x7F800000u) return sign | 0x7FC0u;
-    return f32_to_bf16_rne(p);
-}
 
 // per_token_cast_back (instagit DeepEP low-latency page, example usage):
 // bf16 rows from e4m3fn codes and their per-128-channel scales in any of the

@@ -324,16 +324,17 @@ ep_status ep_handle_sync_status(ep_handle* h, hipStream_t stream);
  * different stream).  A bounded grid of `workgroups` (1..65536) walks tiles in order,
  * waits until tile_ready[tile] has reached `seq` (wrap-safe), then writes
  * every real row of the tile to `out` (device bf16 [capacity_rows, hidden]):
- * a copy of a bf16 pool, or with EP_DISPATCH_FP8 the dequantised value
- * bf16(e4m3(q) * 2^(scale-127)).  With EP_CONSUME_GATHER, `pool` is a
+ * a copy of a bf16 pool, or with EP_DISPATCH_FP8 the dequantised value, as
+ * ep_fp8_cast_back computes it, with the scales in the flavour and layout the
+ * EP_SCALE_* flags name (as for the dispatch).  With EP_CONSUME_GATHER, `pool` is a
  * borrowed bf16 slab [num_tokens, hidden] and row r is read from slab row
  * pool_recv_token[r] (the indexed consumer of [BORROW]).  A wait longer than spin_limit_us gives up
  * on that tile and sets EP_ERR_TIMEOUT in the error word, so it always ends.
  * The caller orders it after ep_layout (e.g. with an event).  flags:
- * EP_DISPATCH_FP8 (row-major UE8M0 scales only; other EP_SCALE_* flags are
- * EP_ERR_UNSUPPORTED), EP_CONSUME_GATHER, EP_CONSUME_SIGNAL_DONE. */
+ * EP_DISPATCH_FP8 with any EP_SCALE_* flags, EP_CONSUME_GATHER (bf16 only),
+ * EP_CONSUME_SIGNAL_DONE. */
 ep_status ep_tile_consume(const ep_handle* h, uint32_t seq, const void* pool,
-                          const uint8_t* pool_scales, int32_t hidden, uint32_t flags,
+                          const void* pool_scales, int32_t hidden, uint32_t flags,
                           void* out, int32_t workgroups, uint32_t spin_limit_us,
                           hipStream_t stream);
 

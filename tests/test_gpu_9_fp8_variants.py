@@ -122,6 +122,41 @@ def test_scaled_dispatch_streaming_release(kind):
 
 @pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("mn", [False, True])
+def test_streaming_consumer_every_flavour(kind, mn):
+    """Streaming dispatch in each flavour and layout with the tile consumer on a
+    second stream: every real row it writes equals the oracle's cast back of
+    the oracle's quantised row."""
+    import combine_ep_layout_amd as ep
+    say(f"[fp8var] streaming consumer kind={kind} mn={mn}")
+    cfg, d = inputs("stream", 2000)
+    H = cfg.hidden
+    L = oracle.layout(d["topk_idx"], cfg.num_experts, cfg.block_m)
+    recv = L["pool_recv_token"]
+    real = np.flatnonzero(recv >= 0)
+    h = new_handle(cfg)
+    sa, sb = torch.cuda.current_stream(), torch.cuda.Stream()          # default priority
+    h.layout(*device_routing(d))
+    pool, scales = h.new_pool(H, fp8=True, scale_kind=kind, mn_major=mn)
+    out = torch.zeros(h.capacity_rows, H, dtype=torch.bfloat16, device=dev())
+    ev = torch.cuda.Event()
+    ev.record(sa)
+    sb.wait_event(ev)
+    seq = h.dispatch(to_dev_bf16(d["x"]), pool, scales, fp8=True, tile_ready=True,
+                     scale_kind=kind, mn_major=mn, stream=sa)
+    h.tile_consume(seq, pool, scales, H, out, fp8=True, workgroups=16, spin_limit_us=3_000_000,
+                   stream=sb, scale_kind=kind, mn_major=mn)
+    sa.synchronize()
+    sb.synchronize()
+    assert h.sync_status() == ep.EP_OK
+    op, osc = oracle.dispatch_fp8_scaled(d["x"][recv[real]], np.arange(real.size, dtype=np.int32), kind)
+    want = oracle.cast_back(op, osc, kind)
+    got = bits_of(out[torch.from_numpy(real).to(dev())])
+    assert np.array_equal(got, want)
+    h.close()
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("mn", [False, True])
 def test_scaled_dispatch_full_size_sampled(kind, mn):
     say(f"[fp8var] prefill full size kind={kind} mn={mn}, sampled rows")
     cfg, d = inputs("prefill")
@@ -207,10 +242,12 @@ def test_fp8_variant_rejections():
     assert lib.ep_dispatch(h.raw, P(x), H, P(pool), None, ep.EP_SCALE_F32, None, None) == ep.EP_ERR_INVALID_ARGUMENT
     assert lib.ep_dispatch(h.raw, P(x), H, P(pool), P(sc) + 2, F8 | ep.EP_SCALE_F32, None, None) == ep.EP_ERR_INVALID_ARGUMENT
     assert lib.ep_dispatch(h.raw, P(x), H, P(pool), P(sc) + 2, F8 | ep.EP_SCALE_MN_MAJOR, None, None) == ep.EP_ERR_INVALID_ARGUMENT
-    # the tile consumer reads row-major UE8M0 only
+    # the tile consumer: scale flags need FP8 and aligned float scales
     out = torch.empty(h.capacity_rows, H, dtype=torch.bfloat16, device=dev())
-    assert lib.ep_tile_consume(h.raw, 1, P(pool), P(sc), H, F8 | ep.EP_SCALE_F32, P(out), 4, 1000,
-                               None) == ep.EP_ERR_UNSUPPORTED
+    assert lib.ep_tile_consume(h.raw, 1, P(pool), P(sc), H, ep.EP_SCALE_F32, P(out), 4, 1000,
+                               None) == ep.EP_ERR_INVALID_ARGUMENT
+    assert lib.ep_tile_consume(h.raw, 1, P(pool), P(sc) + 2, H, F8 | ep.EP_SCALE_F32, P(out), 4, 1000,
+                               None) == ep.EP_ERR_INVALID_ARGUMENT
     # cast back: hidden not a multiple of 128, leading dimension below rows, unknown flag
     q = torch.zeros(8, 256, dtype=torch.uint8, device=dev())
     o = torch.empty(8, 256, dtype=torch.bfloat16, device=dev())
