@@ -38,6 +38,9 @@
 #ifndef EP_FP8_UNROLL
 #define EP_FP8_UNROLL 2        // 16-channel units per lane per FP8 dispatch work item
 #endif
+#ifndef EP_FP8_HW_ENCODE
+#define EP_FP8_HW_ENCODE 1     // UE8M0 codes through gfx950's scaled conversion
+#endif
 #ifndef EP_FP8_SMALL_SPLIT
 #define EP_FP8_SMALL_SPLIT 1   // one-unit FP8 items for batches too small to fill the SIMDs
 #endif
@@ -626,6 +629,23 @@ __device__ __forceinline__ uint32_t e4m3_code_scaled(uint32_t b, float f) {
     return sign | e4m3_code_f32(mag);
 }
 
+// Four bf16 values (two per word) to four e4m3fn codes with gfx950's scaled
+// conversion, the scale given as a power of two in a float's exponent field.
+typedef __bf16 bf16x2_in_t __attribute__((ext_vector_type(2)));
+typedef short shortx2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_fp8(uint32_t w0, uint32_t w1, float scale) {
+    bf16x2_in_t a, b;
+    __builtin_memcpy(&a, &w0, 4);
+    __builtin_memcpy(&b, &w1, 4);
+    shortx2_t r = {0, 0};
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, a, scale, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, b, scale, true);
+    uint32_t out;
+    __builtin_memcpy(&out, &r, 4);
+    return out;
+}
+
 __device__ __forceinline__ uint32_t mag_for_max(uint32_t b) {
     const uint32_t m = b & 0x7FFFu;
     return m > 0x7F80u ? 0u : m;                     // NaN does not take part
@@ -788,14 +808,34 @@ __global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg,
                 sbyte = (uint32_t)(e + 127);
                 // 2^e as a float32 pattern (2^-127 is the subnormal 0x00400000)
                 sval = __uint_as_float(e > -127 ? sbyte << 23 : 0x00400000u);
+                // gfx950's scaled bf16 -> fp8 conversion (scale = the UE8M0 byte in a
+                // float's exponent field) gives the integer encoder's codes for every
+                // finite input within 448 * 2^e, which is every finite input here
+                // (checked on the GPU for all bf16 patterns and scale bytes).  It differs
+                // on NaN and infinity, so a unit holding one takes the integer path.
+                uint32_t special = 0u;
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const uint32_t w0 = lo[u][2 * i], w1 = lo[u][2 * i + 1];
-                    q[i] = e4m3_code(w0 & 0xFFFFu, e) | (e4m3_code(w0 >> 16, e) << 8) |
-                           (e4m3_code(w1 & 0xFFFFu, e) << 16) | (e4m3_code(w1 >> 16, e) << 24);
-                    const uint32_t h0 = hi[u][2 * i], h1 = hi[u][2 * i + 1];
-                    q[2 + i] = e4m3_code(h0 & 0xFFFFu, e) | (e4m3_code(h0 >> 16, e) << 8) |
-                               (e4m3_code(h1 & 0xFFFFu, e) << 16) | (e4m3_code(h1 >> 16, e) << 24);
+                for (int i = 0; i < 4; ++i) {
+                    special |= ((lo[u][i] & 0x7F80u) == 0x7F80u) | ((lo[u][i] & 0x7F800000u) == 0x7F800000u);
+                    special |= ((hi[u][i] & 0x7F80u) == 0x7F80u) | ((hi[u][i] & 0x7F800000u) == 0x7F800000u);
+                }
+                if (EP_FP8_HW_ENCODE && !special) {
+                    const float hs = __uint_as_float(sbyte << 23);
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        q[i] = pk_fp8(lo[u][2 * i], lo[u][2 * i + 1], hs);
+                        q[2 + i] = pk_fp8(hi[u][2 * i], hi[u][2 * i + 1], hs);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        const uint32_t w0 = lo[u][2 * i], w1 = lo[u][2 * i + 1];
+                        q[i] = e4m3_code(w0 & 0xFFFFu, e) | (e4m3_code(w0 >> 16, e) << 8) |
+                               (e4m3_code(w1 & 0xFFFFu, e) << 16) | (e4m3_code(w1 >> 16, e) << 24);
+                        const uint32_t h0 = hi[u][2 * i], h1 = hi[u][2 * i + 1];
+                        q[2 + i] = e4m3_code(h0 & 0xFFFFu, e) | (e4m3_code(h0 >> 16, e) << 8) |
+                                   (e4m3_code(h1 & 0xFFFFu, e) << 16) | (e4m3_code(h1 >> 16, e) << 24);
+                    }
                 }
             }
             if (c < nunit) {
