@@ -123,3 +123,37 @@ def test_fp8_nonfinite_inputs():
     cfg = _one_row_per_token(x)
     d = {"x": x, "topk_idx": np.zeros((6, 1), np.int32), "topk_weights": np.ones((6, 1), np.float32)}
     full_path_check(cfg, d, fp8=True)
+
+
+def test_fp8_every_scale_exponent():
+    """Every UE8M0 exponent a finite group can take (e = -127 ... 120): for each,
+    groups whose amax is 448 * 2^e (the largest finite bf16 for e = 120)
+    holding every finite bf16 magnitude that fits under it, with random signs.
+    The codes come from the hardware conversion where it applies, so this
+    covers it over every (pattern, scale) pair the dispatch can meet."""
+    say("[dispatch fp8] every scale exponent x every fitting magnitude")
+    H = 4096
+    rng = np.random.default_rng(11)
+    mags = np.arange(1, 0x7F80, dtype=np.uint32)                 # every finite nonzero magnitude
+    rows = []
+    for e in range(-127, 121):
+        # amax 448 * 2^e; e = 120 is reached only by magnitudes above 448 * 2^119
+        top = np.uint32(0x43E0 + (e << 7)) if e <= 119 else np.uint32(0x7F7F)
+        fit = mags[mags <= top]
+        fit = fit[fit != top]
+        sgn = rng.integers(0, 2, size=fit.size, dtype=np.uint32) << 15
+        probes = (fit | sgn).astype(np.uint16)
+        ngroups = (probes.size + 126) // 127
+        probes = np.resize(probes, ngroups * 127).reshape(ngroups, 127)
+        groups = np.concatenate([np.full((ngroups, 1), top, np.uint16), probes], axis=1)
+        flat = groups.reshape(-1)
+        pad = (-flat.size) % H
+        flat = np.concatenate([flat, np.zeros(pad, np.uint16)])
+        rows.append(flat.reshape(-1, H))
+    x_bits = np.ascontiguousarray(np.concatenate(rows, axis=0))
+    T = x_bits.shape[0]
+    say(f"  {T} tokens of hidden {H}")
+    cfg = _one_row_per_token(x_bits)
+    d = {"x": x_bits, "topk_idx": np.zeros((T, 1), np.int32),
+         "topk_weights": np.ones((T, 1), np.float32)}
+    full_path_check(cfg, d, fp8=True)

@@ -259,3 +259,22 @@ def test_fp8_variant_rejections():
     torch.cuda.synchronize()
     assert h.sync_status() == ep.EP_OK
     h.close()
+
+
+@pytest.mark.parametrize("kind", ["ue8m0", "pow2_f32"])
+def test_cast_back_every_code_every_scale(kind):
+    """Every code against every power-of-two scale (UE8M0 bytes 0..255; float
+    2^e for e = -127..127), the range where the hardware conversion decodes:
+    bit-identical to the oracle, NaN codes keeping their sign."""
+    import combine_ep_layout_amd as ep
+    say(f"[fp8var] cast back: every code x every scale, {kind}")
+    H = 256
+    nb = 256 if kind == "ue8m0" else 255
+    q = np.tile(np.arange(256, dtype=np.uint8), (nb, 1))            # row b: codes 0..255
+    b = np.arange(nb, dtype=np.uint8)
+    rm = np.stack([b, b], axis=1)                                     # both groups of row b
+    if kind == "pow2_f32":
+        rm = oracle.pow2_scales_from_ue8m0(rm)
+    out = ep.cast_back(torch.from_numpy(q).to(dev()), torch.from_numpy(np.ascontiguousarray(rm)).to(dev()),
+                       kind, False)
+    assert np.array_equal(bits_of(out), oracle.cast_back(q, rm, kind))
