@@ -66,12 +66,19 @@ def algorithmic_bytes(cfg, idx: np.ndarray, counts: np.ndarray, fp8: bool):
 
 
 def kernel_source_sha() -> str:
+    """Hash of the library sources with comments and blank space removed, so
+    that a comment edit does not orphan counters taken on the same code."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "combine_ep_layout_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode())
-            h.update(f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        text = " ".join(text.split())
+        h.update(name.encode())
+        h.update(text.encode())
     return h.hexdigest()[:16]
 
 

@@ -14,15 +14,22 @@
 //
 // Dispatch is token-major: a wave reads one segment of a token's row of x
 // once and writes it, as 16-byte vectors, to each of the token's pool rows
-// (bf16), or quantises it once to e4m3fn with UE8M0 scales per 128 channels
-// and writes the codes (FP8).  With the streaming release, each workgroup
-// covers whole tokens, makes its rows visible at device scope and then raises
-// the arrival count of every tile it wrote; the workgroup that completes a
-// tile release-stores the sequence number into tile_ready[tile].
+// (bf16), or quantises it once to e4m3fn with a scale per 128 channels and
+// writes the codes (FP8; instagit DeepEP low-latency page, "FP8 and
+// Quantization Support").  UE8M0 codes come from gfx950's scaled conversion
+// instruction wherever it equals the exact integer encoder, which is kept for
+// the rest.  With the streaming release, resident workgroups take chunks of
+// whole tokens in global order, make each chunk's rows visible at device
+// scope and then raise the arrival count of every tile it wrote; the
+// workgroup that completes a tile release-stores the sequence number into
+// tile_ready[tile].
 //
 // Combine is token-major too: a wave gathers one segment of the token's k
 // expert rows, accumulates w * o in fp32 with one fused multiply-add per slot
-// in slot order, and rounds once to bf16 (blog, router-weight section).
+// in slot order, and rounds once to bf16 (blog, router-weight section).  The
+// gated variant waits per token on y_done_per_token (StreamEP README,
+// opening paragraph).  The backward kernels, the FP8 cast back and the
+// consumer stand-in (tests and benchmarks) follow.
 //
 // Nothing here is a dense contraction, so no matrix-core instructions are
 // used; dispatch and combine are HBM-bound streaming kernels.
