@@ -152,3 +152,33 @@ def test_gate_rejections():
     torch.cuda.synchronize()
     assert h.sync_status() == ep.EP_OK
     h.close()
+
+
+@pytest.mark.parametrize("T,H,K,E,BM", [(1, 128, 1, 1, 1), (37, 256, 3, 5, 1), (64, 512, 2, 1, 7)])
+def test_gate_small_shapes(T, H, K, E, BM):
+    """One token, one expert, BLOCK_M 1, odd top-k: the gate's batch and
+    stride arithmetic at the smallest shapes (some tokens have no slot)."""
+    import combine_ep_layout_amd as ep
+    from synth import Config, generate
+    say(f"[gate] small shape T={T} H={H} K={K} E={E} BM={BM}")
+    cfg = Config("gate_edge", T, H, K, E, E, BM)
+    d = generate(cfg, 4)
+    if E == 1:
+        idx = np.zeros((T, K), np.int32)
+        idx[::3, -1] = -1
+        d["topk_idx"] = idx
+    L = oracle.layout(d["topk_idx"], E, BM)
+    want = _expected_y(d, L, False)
+    h = new_handle(cfg)
+    epoch = h.layout(*device_routing(d))
+    pool, _ = h.new_pool(H)
+    eo = torch.zeros(h.capacity_rows, H, dtype=torch.bfloat16, device=dev())
+    seq = h.dispatch(to_dev_bf16(d["x"]), pool, tile_ready=True)
+    h.tile_consume(seq, pool, None, H, eo, workgroups=3, spin_limit_us=SPIN_US, signal_done=True)
+    y = h.combine_gated(epoch, eo, round=1, spin_limit_us=SPIN_US)
+    torch.cuda.synchronize()
+    assert h.sync_status() == ep.EP_OK
+    assert np.array_equal(bits_of(y), want)
+    done = h.array("y_done_per_token").cpu().numpy().view(np.uint32)
+    assert np.array_equal(done, _slots_per_token(L, T, K))
+    h.close()

@@ -278,3 +278,28 @@ def test_cast_back_every_code_every_scale(kind):
     out = ep.cast_back(torch.from_numpy(q).to(dev()), torch.from_numpy(np.ascontiguousarray(rm)).to(dev()),
                        kind, False)
     assert np.array_equal(bits_of(out), oracle.cast_back(q, rm, kind))
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("mn", [False, True])
+def test_fp8_variants_one_group_rows(kind, mn):
+    """hidden 128 (one group, a packed word with three zero bytes), top-1,
+    BLOCK_M 1, one-unit items: dispatch, streaming dispatch and cast back of
+    a single row."""
+    import combine_ep_layout_amd as ep
+    from synth import Config, generate
+    say(f"[fp8var] hidden 128 kind={kind} mn={mn}")
+    cfg = Config("one_group", 9, 128, 1, 3, 3, 1)
+    d = generate(cfg, 5)
+    for ready in (False, True):
+        h, pool, scales, L = _dispatch_check(cfg, d, kind, mn, tile_ready=ready)
+        h.close()
+    # one row cast back, MN-major with ld == rows
+    q = pool[:1].contiguous()
+    if mn:
+        s1 = scales[:, :1].contiguous()
+    else:
+        s1 = scales[:1].contiguous()
+    out = ep.cast_back(q, s1, kind, mn, rows=1)
+    s_host = _scales_host(s1, np.zeros(1, np.uint32 if (mn and kind == "ue8m0") else np.uint8))
+    assert np.array_equal(bits_of(out), oracle.cast_back(q.cpu().numpy(), s_host, kind, mn))
