@@ -230,6 +230,12 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
     int key[kSlotsPerLane];
     bool bad = false;
     load_keys(a.topk_idx, base, a.S, E, key, bad);
+    float wv[kSlotsPerLane];                            // weights copied at the end, loaded now
+#pragma unroll
+    for (int j = 0; j < kSlotsPerLane; ++j) {
+        const int s = base + j * kWave + lane;
+        wv[j] = (s < a.S) ? a.topk_w[s] : 0.0f;
+    }
     for (int i = tid; i < kLayoutWaves * E; i += kLayoutThreads) wc[i] = 0;
 
     int total = 0;
@@ -382,10 +388,13 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
             if (r - j * BM >= s_tt[j - jc]) a.recv_token[r] = -1;
         }
     }
-    // ... and of the weights
+    // ... and of the weights (this wave's slots, as the keys)
+#pragma unroll
+    for (int j = 0; j < kSlotsPerLane; ++j) {
+        const int s = base + j * kWave + lane;
+        if (s < a.S) a.weights[s] = wv[j];
+    }
     const int s1 = min(a.S, (b + 1) * kLayoutSlotsPerBlock);
-    for (int s = b * kLayoutSlotsPerBlock + tid; s < s1; s += kLayoutThreads)
-        a.weights[s] = a.topk_w[s];
     // ... and of the per-token done counts of the tokens whose first slot is here
     const int T = a.S / a.K;
     const int tb0 = (b * kLayoutSlotsPerBlock + a.K - 1) / a.K;
