@@ -87,8 +87,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kLayoutThreads = 1024;                          // 16 waves
 constexpr int kLayoutWaves = kLayoutThreads / kWave;
-constexpr int kSlotsPerLane = kLayoutSlotsPerBlock / kLayoutThreads;   // 8
-constexpr int kWaveSlots = kLayoutSlotsPerBlock / kLayoutWaves;       // 512
+constexpr int kSlotsPerLane = kLayoutSlotsPerBlock / kLayoutThreads;   // EP_LAYOUT_SLOTS_PER_LANE
+constexpr int kWaveSlots = kLayoutSlotsPerBlock / kLayoutWaves;       // slots per wave
 
 __device__ __forceinline__ int uniform_i(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -161,7 +161,7 @@ __device__ __forceinline__ int expert_of_tile(const int* s_off, int E, int j) {
     return lo;
 }
 
-// Keys of this wave's 512 slots, slot = base + i*64 + lane: the expert id, or
+// Keys of this wave's kWaveSlots slots, slot = base + i*64 + lane: the expert id, or
 // E for masked, invalid and past-the-end slots.  All loads are issued first.
 __device__ __forceinline__ void load_keys(const int32_t* idx, int base, int S, int E,
                                           int (&key)[kSlotsPerLane], bool& bad) {
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_count(LayoutArgs a) {
 // Layout ranks.  FUSED: the whole layout in this one workgroup (nb == 1, no
 // histogram launch).  Otherwise launch 2 of the multi-workgroup layout: the
 // workgroup sums the histograms of the workgroups before it and of all of
-// them, scans tiles over experts, and ranks its own 8192 slots.  Every
+// them, scans tiles over experts, and ranks its own kLayoutSlotsPerBlock slots.  Every
 // workgroup writes its share of the tile metadata and of the padding rows.
 template <bool FUSED>
 __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, int nb, int lg_tpe) {
