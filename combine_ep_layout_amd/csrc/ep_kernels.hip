@@ -150,15 +150,17 @@ __device__ int block_exclusive_scan(int v, int* s_tmp, int& total) {
     return before + x - v;
 }
 
-// Expert owning tile j: the last e whose first tile is <= j (s_off has E+1
-// non-decreasing entries; requires j < s_off[E]).
-__device__ __forceinline__ int expert_of_tile(const int* s_off, int E, int j) {
-    int lo = 0, hi = E - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_off[mid] <= j) lo = mid; else hi = mid - 1;
+// Exclusive scan over one wave; returns this lane's prefix and the wave total.
+__device__ __forceinline__ int wave_exclusive_scan(int v, int& total) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int x = v;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int y = __shfl_up(x, d, kWave);
+        if (lane >= d) x += y;
     }
-    return lo;
+    total = __shfl(x, kWave - 1, kWave);
+    return x - v;
 }
 
 // Keys of this wave's kWaveSlots slots, slot = base + i*64 + lane: the expert id, or
@@ -219,8 +221,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
     int* s_cnt = s_base + E;                            // [E]   rows of expert e
     int* s_off = s_cnt + E;                             // [E+1] first tile of expert e
     int* s_tmp = s_off + E + 1;                         // [16]
-    int* s_tt = s_tmp + kLayoutWaves;                   // [1024] real rows of a chunk of tiles
-    uint16_t* wc = (uint16_t*)(s_tt + kLayoutThreads);  // [16][E] per-wave counts, then next ranks
+    uint16_t* wc = (uint16_t*)(s_tmp + kLayoutWaves);   // [16][E] per-wave counts, then next ranks
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int w = uniform_i(tid / kWave);
     const int b = (int)blockIdx.x;
@@ -271,10 +272,6 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
             s_cnt[e] = tot;
             s_off[e] = off;
             s_base[e] = off * BM + pre;
-            if (b == 0) {
-                a.counts[e] = tot;
-                a.offsets[e] = off;
-            }
         }
     }
     __syncthreads();
@@ -289,39 +286,42 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
         if (key[i] < E && lane == __ffsll((unsigned long long)m[i]) - 1)
             wc[w * E + key[i]] += (uint16_t)__popcll(m[i]);
     }
+    // The handle's copy of the weights (this wave's slots, as the keys).  On
+    // gfx9 a wait for a load also waits for every store issued before it, so
+    // global stores are kept after the last global load is consumed.
+#pragma unroll
+    for (int j = 0; j < kSlotsPerLane; ++j) {
+        const int s = base + j * kWave + lane;
+        if (s < a.S) a.weights[s] = wv[j];
+    }
     __syncthreads();
 
+    // exclusive prefix of the per-wave counts over waves; the last running sum
+    // is the expert's count in this workgroup (E <= kLayoutThreads)
+    int run = 0;
+    if (tid < E) {
+        int c[kLayoutWaves];                            // every load issued before the stores
+#pragma unroll
+        for (int v = 0; v < kLayoutWaves; ++v) c[v] = wc[v * E + tid];
+#pragma unroll
+        for (int v = 0; v < kLayoutWaves; ++v) {
+            wc[v * E + tid] = (uint16_t)run;
+            run += c[v];
+        }
+    }
     if constexpr (FUSED) {
         if (__ballot(bad) && lane == 0) atomicOr(a.error, 1u);
-        int tot = 0;
-        if (tid < E)
-            for (int v = 0; v < kLayoutWaves; ++v) tot += wc[v * E + tid];
-        const int tiles = (tid < E) ? (tot + BM - 1) / BM : 0;
-        const int off = block_exclusive_scan<kLayoutThreads>(tiles, s_tmp, total);
+        const int tiles = (tid < E) ? (run + BM - 1) / BM : 0;
+        // with E <= 64 wave 0 holds every expert and scans without a barrier
+        const int off = E <= kWave ? wave_exclusive_scan(tiles, total)
+                                   : block_exclusive_scan<kLayoutThreads>(tiles, s_tmp, total);
         if (tid < E) {
-            s_cnt[tid] = tot;
+            s_cnt[tid] = run;
             s_off[tid] = off;
             s_base[tid] = off * BM;
-            a.counts[tid] = tot;
-            a.offsets[tid] = off;
         }
     }
-    // exclusive prefix of the per-wave counts over waves
-    for (int e = tid; e < E; e += kLayoutThreads) {
-        int run = 0;
-        for (int v = 0; v < kLayoutWaves; ++v) {
-            const int c = wc[v * E + e];
-            wc[v * E + e] = (uint16_t)run;
-            run += c;
-        }
-    }
-    if (tid == 0) {
-        s_off[E] = total;
-        if (b == 0) {
-            a.offsets[E] = total;
-            *a.num_tiles = total;
-        }
-    }
+    if (tid == 0) s_off[E] = total;
     __syncthreads();
 
     // pool row of every slot of this wave
@@ -348,58 +348,56 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
         }
     }
 
-    // this workgroup's share of the tile metadata
-    const int tpb = (a.max_tiles + nb - 1) / nb;
-    const int j1 = min(a.max_tiles, (b + 1) * tpb);
-    for (int j = b * tpb + tid; j < j1; j += kLayoutThreads) {
-        if (j < total) {
-            const int e = expert_of_tile(s_off, E, j);
-            const int left = s_cnt[e] - (j - s_off[e]) * BM;
-            a.tile_expert[j] = e;
-            a.tile_target[j] = left < BM ? left : BM;
-            a.arrival[j] = 0u;
-        } else {
-            a.tile_expert[j] = -1;
-            a.tile_target[j] = 0;
-        }
+    // Tile metadata and padding rows, expert by expert (expert e's tiles are
+    // [s_off[e], s_off[e+1]) and its padding rows follow its s_cnt[e] real
+    // rows): workgroup b takes experts b, b + nb, ..., one wave per expert.
+    // (the next expert's bounds are read before this one's stores)
+    const int estep = nb * kLayoutWaves;
+    int e_n = b + nb * w;
+    int j0_n = 0, j1_n = 0, cnt_n = 0;
+    if (e_n < E) {
+        j0_n = s_off[e_n];
+        j1_n = s_off[e_n + 1];
+        cnt_n = s_cnt[e_n];
     }
-    // ... of the rows that receive no slot (padding, and everything past the
-    // tiles), with the real-row count of each tile looked up once per tile
-    const int rpb = (a.cap + nb - 1) / nb;
-    const int r0 = min(a.cap, b * rpb), r1 = min(a.cap, (b + 1) * rpb);
-    const int jt0 = r0 / BM, jt1 = (r1 + BM - 1) / BM;
-    for (int jc = jt0; jc < jt1; jc += kLayoutThreads) {
-        const int jn = min(jt1, jc + kLayoutThreads);
-        __syncthreads();
-        if (jc + tid < jn) {
-            const int j = jc + tid;
-            int real = 0;
-            if (j < total) {
-                const int e = expert_of_tile(s_off, E, j);
-                const int left = s_cnt[e] - (j - s_off[e]) * BM;
-                real = left < BM ? left : BM;
-            }
-            s_tt[tid] = real;
+    for (int e = e_n; e < E; e += estep) {
+        const int j0 = j0_n, nt = j1_n - j0_n, cnt = cnt_n;
+        e_n = e + estep;
+        if (e_n < E) {
+            j0_n = s_off[e_n];
+            j1_n = s_off[e_n + 1];
+            cnt_n = s_cnt[e_n];
         }
-        __syncthreads();
-        const int ra = max(r0, jc * BM), rb = min(r1, jn * BM);
-        for (int r = ra + tid; r < rb; r += kLayoutThreads) {
-            const int j = r / BM;
-            if (r - j * BM >= s_tt[j - jc]) a.recv_token[r] = -1;
+        for (int i = lane; i < nt; i += kWave) {
+            const int left = cnt - i * BM;
+            a.tile_expert[j0 + i] = e;
+            a.tile_target[j0 + i] = left < BM ? left : BM;
+            a.arrival[j0 + i] = 0u;
         }
+        for (int r = j0 * BM + cnt + lane; r < (j0 + nt) * BM; r += kWave) a.recv_token[r] = -1;
     }
-    // ... and of the weights (this wave's slots, as the keys)
-#pragma unroll
-    for (int j = 0; j < kSlotsPerLane; ++j) {
-        const int s = base + j * kWave + lane;
-        if (s < a.S) a.weights[s] = wv[j];
+    // ... then the tiles and rows past the last tile, spread over all workgroups
+    const int total_t = s_off[E];
+    for (int j = total_t + b * kLayoutThreads + tid; j < a.max_tiles; j += nb * kLayoutThreads) {
+        a.tile_expert[j] = -1;
+        a.tile_target[j] = 0;
     }
+    for (int r = total_t * BM + b * kLayoutThreads + tid; r < a.cap; r += nb * kLayoutThreads)
+        a.recv_token[r] = -1;
     const int s1 = min(a.S, (b + 1) * kLayoutSlotsPerBlock);
-    // ... and of the per-token done counts of the tokens whose first slot is here
+    // and the per-token done counts of the tokens whose first slot is here
     const int T = a.S / a.K;
     const int tb0 = (b * kLayoutSlotsPerBlock + a.K - 1) / a.K;
     const int tb1 = min(T, (s1 + a.K - 1) / a.K);
     for (int t = tb0 + tid; t < tb1; t += kLayoutThreads) a.y_done[t] = 0u;
+    // counts, first tiles and the tile total (workgroup 0)
+    if (b == 0) {
+        for (int e = tid; e <= E; e += kLayoutThreads) {
+            if (e < E) a.counts[e] = s_cnt[e];
+            a.offsets[e] = s_off[e];
+        }
+        if (tid == 0) *a.num_tiles = s_off[E];
+    }
 }
 
 // ------------------------------------------------------------- dispatch ---
@@ -1444,7 +1442,7 @@ hipError_t combine_bwd_kt(const CombineBwdArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
-    const size_t lds_rank = sizeof(int) * (size_t)(3 * a.E + 1 + kLayoutWaves + kLayoutThreads) +
+    const size_t lds_rank = sizeof(int) * (size_t)(3 * a.E + 1 + kLayoutWaves) +
                             sizeof(uint16_t) * (size_t)kLayoutWaves * a.E;
     if (a.S <= kLayoutSlotsPerBlock) {
         hipLaunchKernelGGL((k_layout_rank<true>), dim3(1), dim3(kLayoutThreads), lds_rank, stream,
