@@ -350,6 +350,7 @@ ep_status ep_combine_gated(const ep_handle* h, uint32_t epoch, const void* exper
     a.round = round;
     a.limit_ticks = (uint64_t)spin_limit_us * (uint64_t)h->wall_khz / 1000u;
     a.error = h->error;
+    a.num_cu = h->num_cu;
     return hip_status(epk::launch_combine_gated(a, stream));
 }
 

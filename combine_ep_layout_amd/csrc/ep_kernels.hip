@@ -878,7 +878,8 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 // expert rows for that segment, accumulates w * o in fp32 with one fused
 // multiply-add per slot in slot order, and rounds once to bf16).
 template <int KT, bool UNIT>
-__device__ __forceinline__ void combine_item(const CombineArgs& a, int t, int seg, int lane) {
+__device__ __forceinline__ int combine_compute(const CombineArgs& a, int t, int seg, int lane,
+                                               u32x4 (&out)[EP_COMBINE_UNROLL]) {
     constexpr int U = EP_COMBINE_UNROLL;
     const int n16 = a.H / 8;
     const u32x4* eo = (const u32x4*)a.expert_out;
@@ -901,7 +902,6 @@ __device__ __forceinline__ void combine_item(const CombineArgs& a, int t, int se
             if (c < n16) v[k][u] = load_v<EP_COMBINE_NT_LOADS>(src + c);
         }
     }
-    u32x4* dst = (u32x4*)a.y + (int64_t)t * n16;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         float acc[8];
@@ -918,13 +918,35 @@ __device__ __forceinline__ void combine_item(const CombineArgs& a, int t, int se
                     __builtin_fmaf(wt[k], __uint_as_float(p & 0xFFFF0000u), acc[2 * i + 1]);
             }
         }
-        u32x4 o;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            o[i] = f32_to_bf16_rne(acc[2 * i]) | (f32_to_bf16_rne(acc[2 * i + 1]) << 16);
-        const int c = c0 + u * kWave;
-        if (c < n16) store_row<EP_COMBINE_STORE>(dst, a.H * 2, c, o);
+            out[u][i] = f32_to_bf16_rne(acc[2 * i]) | (f32_to_bf16_rne(acc[2 * i + 1]) << 16);
     }
+    int nrows = 0;
+#pragma unroll
+    for (int k = 0; k < KT; ++k) nrows += rows[k] >= 0 ? 1 : 0;
+    return nrows;
+}
+
+// Stores of one combine work item's outputs (row t of y, segment seg).
+__device__ __forceinline__ void combine_store(const CombineArgs& a, int t, int seg, int lane,
+                                              const u32x4 (&o)[EP_COMBINE_UNROLL]) {
+    constexpr int U = EP_COMBINE_UNROLL;
+    const int n16 = a.H / 8;
+    const int c0 = seg * (kWave * U) + lane;
+    u32x4* dst = (u32x4*)a.y + (int64_t)t * n16;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * kWave;
+        if (c < n16) store_row<EP_COMBINE_STORE>(dst, a.H * 2, c, o[u]);
+    }
+}
+
+template <int KT, bool UNIT>
+__device__ __forceinline__ void combine_item(const CombineArgs& a, int t, int seg, int lane) {
+    u32x4 o[EP_COMBINE_UNROLL];
+    combine_compute<KT, UNIT>(a, t, seg, lane, o);
+    combine_store(a, t, seg, lane, o);
 }
 
 template <int KT, bool UNIT>
@@ -940,15 +962,52 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a, int nseg, int ip
 }
 
 #ifndef EP_GATE_TOKENS
-#define EP_GATE_TOKENS 16      // tokens per workgroup of the gated combine (<= 64)
+#define EP_GATE_TOKENS 16      // most tokens per workgroup of the gated combine (<= 64)
 #endif
 static_assert(EP_GATE_TOKENS >= 1 && EP_GATE_TOKENS <= 64, "one wave lane per gated token");
 #ifndef EP_GATE_WAVES
-#define EP_GATE_WAVES 16       // waves per workgroup of the gated combine
+#define EP_GATE_WAVES 16       // most waves per workgroup of the gated combine
+#endif
+#ifndef EP_GATE_DEFER
+#define EP_GATE_DEFER 4        // gated combine items computed before their stores are issued
 #endif
 #ifndef EP_GATE_STRIDED
 #define EP_GATE_STRIDED 1      // 1: a workgroup's tokens are strided by the grid size
 #endif
+
+// The items of a gated batch (token slot j < gtok, segment): wave w takes
+// items w, w + nw, ...  On gfx9 a wait for a load also waits for every store
+// issued before it, so a wave that owns several items computes D of them
+// before issuing their stores: one store drain per D items, not per item.
+// With few rows per token (a latency-bound batch) holding stores back was
+// measured slower, so those batches use D = 1.
+template <int KT, int D>
+__device__ __forceinline__ void gated_items(const CombineArgs& a, int nseg, int gtok, uint64_t mask,
+                                            int w, int nw, int lane) {
+    const int b = (int)blockIdx.x, nb = (int)gridDim.x;
+    auto token_of = [&](int j) {
+        return EP_GATE_STRIDED ? b + j * nb : b * gtok + j;
+    };
+    const int nit = gtok * nseg;
+    for (int i0 = w; i0 < nit; i0 += D * nw) {
+        u32x4 o[D][EP_COMBINE_UNROLL];
+        int tt[D], sg[D];
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int i = i0 + d * nw;
+            const int j = i / nseg;
+            tt[d] = -1;
+            if (i < nit && token_of(j) < a.T && ((mask >> j) & 1ull)) {
+                tt[d] = token_of(j);
+                sg[d] = i - j * nseg;
+                combine_compute<KT, false>(a, tt[d], sg[d], lane, o[d]);
+            }
+        }
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            if (tt[d] >= 0) combine_store(a, tt[d], sg[d], lane, o[d]);
+    }
+}
 
 // Per-token gate (StreamEP README, y_done_per_token).  A workgroup takes
 // EP_GATE_TOKENS tokens, strided by the grid size so that the workgroups in
@@ -962,22 +1021,36 @@ static_assert(EP_GATE_TOKENS >= 1 && EP_GATE_TOKENS <= 64, "one wave lane per ga
 // (error bit 2), it gives up, sets bit 2, and the batch's tokens that were
 // not done are skipped (their y rows keep their contents).
 template <int KT>
-__global__ __launch_bounds__(64 * EP_GATE_WAVES) void k_combine_gated(CombineArgs a, int nseg) {
+__global__ __launch_bounds__(64 * EP_GATE_WAVES) void k_combine_gated(CombineArgs a, int nseg, int gtok) {
     __shared__ uint64_t s_done;
+    __shared__ int s_dense;
     const int lane = threadIdx.x & (kWave - 1);
     const int w = uniform_i(threadIdx.x / kWave);
+    const int nw = (int)blockDim.x / kWave;
     const int b = (int)blockIdx.x, nb = (int)gridDim.x;
-    // batch slot j holds token b + j * nb (strided: the workgroups in flight
-    // cover a compact window of tokens) or b * EP_GATE_TOKENS + j
+    // batch slot j < gtok holds token b + j * nb (strided: the workgroups in
+    // flight cover a compact window of tokens) or b * gtok + j
     auto token_of = [&](int j) {
-        return EP_GATE_STRIDED ? b + j * nb : b * EP_GATE_TOKENS + j;
+        return EP_GATE_STRIDED ? b + j * nb : b * gtok + j;
     };
     if (w == 0) {
         const int t = token_of(lane);
-        const bool mine = lane < EP_GATE_TOKENS && t < a.T;
+        const bool mine = lane < gtok && t < a.T;
         uint32_t target = 0;
-        if (mine)
-            for (int k = 0; k < a.K; ++k) target += a.slot_to_row[t * a.K + k] >= 0 ? 1u : 0u;
+        if (mine) {
+            int r[KT];                                  // every load issued before the first use
+#pragma unroll
+            for (int k = 0; k < KT; ++k) r[k] = k < a.K ? a.slot_to_row[t * a.K + k] : -1;
+#pragma unroll
+            for (int k = 0; k < KT; ++k) target += r[k] >= 0 ? 1u : 0u;
+        }
+        // rows and tokens of the batch: an average of 4 or more rows per token
+        // takes the path that holds stores back
+        int rows = (int)target, toks = mine ? 1 : 0;
+        for (int d = 1; d < kWave; d <<= 1) {
+            rows += __shfl_xor(rows, d, kWave);
+            toks += __shfl_xor(toks, d, kWave);
+        }
         target *= a.round;
         auto done = [&]() {
             return !mine || target == 0 ||
@@ -1000,15 +1073,15 @@ __global__ __launch_bounds__(64 * EP_GATE_WAVES) void k_combine_gated(CombineArg
             }
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        if (lane == 0) s_done = mask;
+        if (lane == 0) {
+            s_done = mask;
+            s_dense = rows >= 4 * toks;
+        }
     }
     __syncthreads();
     const uint64_t mask = s_done;
-    for (int i = w; i < EP_GATE_TOKENS * nseg; i += EP_GATE_WAVES) {
-        const int j = i / nseg;
-        const int t = token_of(j);
-        if (t < a.T && ((mask >> j) & 1ull)) combine_item<KT, false>(a, t, i - j * nseg, lane);
-    }
+    if (s_dense) gated_items<KT, EP_GATE_DEFER>(a, nseg, gtok, mask, w, nw, lane);
+    else gated_items<KT, 1>(a, nseg, gtok, mask, w, nw, lane);
 }
 
 // ----------------------------------------------------- combine backward ---
@@ -1410,8 +1483,13 @@ hipError_t combine_kt(const CombineArgs& a, hipStream_t st) {
     const int per_seg = kWave * EP_COMBINE_UNROLL * 8;
     const int nseg = (a.H + per_seg - 1) / per_seg;
     if constexpr (GATE) {
-        const int grid = (a.T + EP_GATE_TOKENS - 1) / EP_GATE_TOKENS;
-        hipLaunchKernelGGL((k_combine_gated<KT>), dim3(grid), dim3(64 * EP_GATE_WAVES), 0, st, a, nseg);
+        // fewer tokens per workgroup when the batch would not give every
+        // compute unit two workgroups; no more waves than the batch has items
+        int gtok = EP_GATE_TOKENS;
+        while (gtok > 1 && (a.T + gtok - 1) / gtok < 2 * a.num_cu) gtok >>= 1;
+        const int gw = gtok * nseg < EP_GATE_WAVES ? gtok * nseg : EP_GATE_WAVES;
+        const int grid = (a.T + gtok - 1) / gtok;
+        hipLaunchKernelGGL((k_combine_gated<KT>), dim3(grid), dim3(64 * gw), 0, st, a, nseg, gtok);
         return hipGetLastError();
     }
     const int ipb = items_per_block(nseg, false);
