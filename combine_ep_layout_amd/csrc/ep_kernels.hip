@@ -43,13 +43,13 @@
 #define EP_DISPATCH_UNROLL 7   // 16-byte chunks per lane per bf16 dispatch work item
 #endif
 #ifndef EP_FP8_UNROLL
-#define EP_FP8_UNROLL 2        // 16-channel units per lane per FP8 dispatch work item
+#define EP_FP8_UNROLL 1        // 16-channel units per lane per FP8 dispatch work item
+#endif
+#ifndef EP_FP8_STREAM_UNROLL
+#define EP_FP8_STREAM_UNROLL 2 // the same for the streaming (tile_ready) FP8 dispatch
 #endif
 #ifndef EP_FP8_HW_ENCODE
 #define EP_FP8_HW_ENCODE 1     // UE8M0 codes through gfx950's scaled conversion
-#endif
-#ifndef EP_FP8_SMALL_SPLIT
-#define EP_FP8_SMALL_SPLIT 1   // one-unit FP8 items for batches too small to fill the SIMDs
 #endif
 #ifndef EP_FP8_PACK8
 #define EP_FP8_PACK8 1         // UE8M0 scale bytes of a full step as one 64-bit store per row
@@ -1440,12 +1440,8 @@ inline int items_per_block(int nseg, bool stream) {
 
 template <int KT>
 hipError_t dispatch_kt(const DispatchArgs& a, bool fp8, bool stream, hipStream_t st) {
-    // FP8 items of one unit per lane when the batch is too small to give every
-    // SIMD two waves of EP_FP8_UNROLL-unit items (decode): the quantiser's ALU
-    // chain is then split over twice the waves
-    const int n2 = (a.H / 16 + kWave * EP_FP8_UNROLL - 1) / (kWave * EP_FP8_UNROLL);
-    const bool small = EP_FP8_SMALL_SPLIT && fp8 && !stream && (int64_t)a.T * n2 < (int64_t)a.num_cu * 8;
-    const int fu = small ? 1 : EP_FP8_UNROLL;
+    constexpr int FU = EP_FP8_UNROLL, FS = EP_FP8_STREAM_UNROLL;
+    const int fu = stream ? FS : FU;
     const int per_seg = fp8 ? kWave * fu * 16 : kWave * EP_DISPATCH_UNROLL * 8;  // channels
     const int nseg = (a.H + per_seg - 1) / per_seg;
     const int ipb = items_per_block(nseg, stream);
@@ -1455,18 +1451,13 @@ hipError_t dispatch_kt(const DispatchArgs& a, bool fp8, bool stream, hipStream_t
     const size_t lds = stream ? 2 * sizeof(int) * (size_t)a.E : 0;
     const dim3 block(stream ? EP_STREAM_THREADS : 256);
     if (fp8) {
-        constexpr int FU = EP_FP8_UNROLL;
         const bool f32q = a.scale_kind == kScaleF32;
         if (stream && f32q)
-            hipLaunchKernelGGL((k_dispatch_fp8<KT, true, true, FU>), dim3(grid), block, lds, st, a, nseg, ipb);
+            hipLaunchKernelGGL((k_dispatch_fp8<KT, true, true, FS>), dim3(grid), block, lds, st, a, nseg, ipb);
         else if (stream)
-            hipLaunchKernelGGL((k_dispatch_fp8<KT, true, false, FU>), dim3(grid), block, lds, st, a, nseg, ipb);
-        else if (f32q && small)
-            hipLaunchKernelGGL((k_dispatch_fp8<KT, false, true, 1>), dim3(grid), block, lds, st, a, nseg, ipb);
+            hipLaunchKernelGGL((k_dispatch_fp8<KT, true, false, FS>), dim3(grid), block, lds, st, a, nseg, ipb);
         else if (f32q)
             hipLaunchKernelGGL((k_dispatch_fp8<KT, false, true, FU>), dim3(grid), block, lds, st, a, nseg, ipb);
-        else if (small)
-            hipLaunchKernelGGL((k_dispatch_fp8<KT, false, false, 1>), dim3(grid), block, lds, st, a, nseg, ipb);
         else
             hipLaunchKernelGGL((k_dispatch_fp8<KT, false, false, FU>), dim3(grid), block, lds, st, a, nseg, ipb);
     } else {
