@@ -32,7 +32,6 @@ struct ep_handle {
     float* weights;
     uint32_t* error;
     int32_t* ws;
-    uint32_t* done;
     uint32_t* y_done;         // per-token done counts of the combine gate
     // host state of the current layout
     int32_t T;                // tokens of the current layout, -1 before the first
@@ -159,7 +158,6 @@ ep_status ep_handle_create(const ep_config* cfg, ep_handle** out) {
         {(void**)&h->weights, sizeof(float) * ms},
         {(void**)&h->error, sizeof(uint32_t)},
         {(void**)&h->ws, sizeof(int32_t) * (size_t)h->ws_blocks * E},
-        {(void**)&h->done, sizeof(uint32_t)},
         {(void**)&h->y_done, sizeof(uint32_t) * (size_t)cfg->max_tokens},
     };
     size_t total = 0;
@@ -237,7 +235,6 @@ ep_status ep_layout(ep_handle* h, const int32_t* topk_idx, const float* topk_wei
     a.weights = h->weights;
     a.error = h->error;
     a.ws = h->ws;
-    a.done = h->done;
     a.y_done = h->y_done;
     ep_status st = hip_status(epk::launch_layout(a, stream));
     if (st != EP_OK) return st;
@@ -295,11 +292,7 @@ ep_status ep_dispatch(ep_handle* h, const void* x, int32_t hidden, void* pool,
     a.scale_ld = scale_ld_of(h->cap);
     a.arrival = h->arrival;
     a.tile_ready = h->tile_ready;
-    a.max_tiles = h->max_tiles;
-    a.tile_bits = 1;
-    while ((1 << a.tile_bits) <= h->max_tiles) ++a.tile_bits;
     a.stream_grid = h->num_cu * EP_STREAM_WG_PER_CU;
-    a.num_cu = h->num_cu;
     a.seq = h->seq + 1;
     a.round = h->round + (ready ? 1u : 0u);
     ep_status st = hip_status(epk::launch_dispatch(a, fp8, ready, stream));

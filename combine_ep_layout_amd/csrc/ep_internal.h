@@ -39,7 +39,6 @@ struct LayoutArgs {
     float* weights;             // [S]
     uint32_t* error;            // [1]
     int32_t* ws;                // [blocks * E] per-workgroup counts, then bases
-    uint32_t* done;             // [1] last-workgroup counter (self-resetting)
     uint32_t* y_done;           // [T] per-token done counts, zeroed here
 };
 
@@ -70,10 +69,7 @@ struct DispatchArgs {
     uint32_t* tile_ready;
     uint32_t seq;
     uint32_t round;             // TILE_READY dispatches since the layout (1, 2, ...)
-    int32_t max_tiles;
-    int32_t tile_bits;          // bits of a tile id, max_tiles included
     int32_t stream_grid;        // workgroups of a streaming dispatch (resident)
-    int32_t num_cu;             // compute units of the device
 };
 
 struct CombineArgs {
