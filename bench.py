@@ -9,7 +9,7 @@ resident in HBM when the timed region starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
                     [--no-cpu-baseline] [--copy-calibration]
-                    [--borrow-compare | --backward | --gate | --fp8-variants | --ceiling]
+                    [--borrow-compare | --backward | --gate | --fp8-variants | --graph | --ceiling]
 
 Prints one JSON line.  "value" is algorithmic bytes moved per step / step
 time, over exactly K steps with nothing else on the stream.  Per-kernel times
@@ -277,6 +277,66 @@ def _time_us(fn, steps: int, warmup: int, stream) -> float:
     return a.elapsed_time(b) / steps * 1e3
 
 
+def graph_bench(cfg, steps: int, warmup: int, per_replay: int = 4) -> dict:
+    """The layout -> dispatch -> combine step launched eagerly vs captured in
+    a HIP graph of `per_replay` steps (torch's graph capture on the library's
+    stream).  Small batches are launch-bound, and a graph replay removes the
+    gaps between launches.  The graph's output is checked against the eager
+    step's."""
+    import torch
+    import combine_ep_layout_amd as ep
+    from synth import generate
+    dev = torch.device("cuda", 0)
+    d = generate(cfg, 0)
+    T, K, H = cfg.tokens, cfg.top_k, cfg.hidden
+    fp8, ready = cfg.fp8, cfg.tile_ready
+    idx = torch.from_numpy(d["topk_idx"]).to(dev)
+    w = torch.from_numpy(d["topk_weights"]).to(dev)
+    x = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    h = ep.EpHandle(T, K, cfg.num_experts, cfg.block_m)
+    pool, scales = h.new_pool(H, fp8=fp8)
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    eo = torch.randn(h.capacity_rows, H, generator=g, device=dev).to(torch.bfloat16)
+    y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+
+    def step():
+        e = h.layout(idx, w)
+        h.dispatch(x, pool, scales, fp8=fp8, tile_ready=ready)
+        h.combine(e, eo, y)
+
+    s = torch.cuda.Stream()                              # default priority
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        eager = _time_us(step, steps, warmup, s)
+        want = y.clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            for _ in range(per_replay):
+                step()
+        torch.cuda.synchronize()
+        y.zero_()
+        n = max(1, steps // per_replay)
+        replay = _time_us(graph.replay, n, max(1, warmup // per_replay), s) / per_replay
+    torch.cuda.synchronize()
+    same = bool(torch.equal(y.view(torch.int16), want.view(torch.int16)))
+    status = h.sync_status()
+    del graph
+    h.close()
+    if not same or status != ep.EP_OK:
+        raise RuntimeError("graph replay differs from the eager step")
+    return {"metric": "layout+dispatch+combine step, eager vs captured in a HIP graph",
+            "unit": "us", "higher_is_better": False, "data": "synthetic",
+            "dtype": "fp8" if fp8 else "bf16",
+            "config": {"workload": f"{cfg.name}: {T} tokens, hidden {H}, {cfg.num_experts} experts "
+                                   f"{cfg.routing} top-{K}, BLOCK_M {cfg.block_m}, "
+                                   f"{'fp8' if fp8 else 'bf16'}" + (", tile_ready" if ready else ""),
+                       "steps_per_replay": per_replay},
+            "eager_us_per_step": round(eager, 2), "graph_us_per_step": round(replay, 2),
+            "change_pct": round(100.0 * (replay - eager) / eager, 1),
+            "graph_output_equals_eager": same}
+
+
 def gate_bench(cfg, steps: int, warmup: int) -> dict:
     """Per-token combine gate.  (1) The gate's own cost: the gated combine
     with every token already done vs the plain combine.  (2) A forward pass
@@ -455,6 +515,8 @@ def main() -> int:
                     help="print the per-token combine gate measurement instead")
     ap.add_argument("--fp8-variants", action="store_true",
                     help="print the FP8 scale flavour / cast back measurement instead")
+    ap.add_argument("--graph", action="store_true",
+                    help="print the eager vs HIP-graph step time instead")
     ap.add_argument("--ceiling", action="store_true",
                     help="print the bandwidth of plain torch fill / read / copy kernels instead")
     args = ap.parse_args()
@@ -479,6 +541,10 @@ def main() -> int:
     if args.gate:
         torch.cuda.set_device(0)
         print(json.dumps(gate_bench(CONFIGS[args.config], args.steps, args.warmup)), flush=True)
+        return 0
+    if args.graph:
+        torch.cuda.set_device(0)
+        print(json.dumps(graph_bench(CONFIGS[args.config], args.steps, args.warmup)), flush=True)
         return 0
     if args.ceiling:
         torch.cuda.set_device(0)
