@@ -319,6 +319,7 @@ ep_status ep_combine(const ep_handle* h, uint32_t epoch, const void* expert_out,
     a.slot_to_row = h->slot_to_row;
     a.weights = h->weights;
     a.y = y;
+    a.num_cu = h->num_cu;
     return hip_status(epk::launch_combine(a, stream));
 }
 
@@ -408,6 +409,7 @@ ep_status ep_dispatch_backward(const ep_handle* h, uint32_t epoch, const void* g
     a.slot_to_row = h->slot_to_row;
     a.weights = nullptr;
     a.y = grad_x;
+    a.num_cu = h->num_cu;
     return hip_status(epk::launch_combine_unit(a, stream));
 }
 

@@ -85,7 +85,7 @@ struct CombineArgs {
     uint32_t round;
     uint64_t limit_ticks;
     uint32_t* error;
-    int32_t num_cu;             // compute units of the device (gated launch shape)
+    int32_t num_cu;             // compute units of the device (launch shapes)
 };
 
 struct CombineBwdArgs {

@@ -72,6 +72,9 @@
 #ifndef EP_COMBINE_STORE
 #define EP_COMBINE_STORE 1     // y stores: see store_row
 #endif
+#ifndef EP_COMBINE_SCALAR_WAVES
+#define EP_COMBINE_SCALAR_WAVES 8  // grids up to this many waves per compute unit read slots as scalars
+#endif
 #ifndef EP_COMBINE_NT_LOADS
 #define EP_COMBINE_NT_LOADS 1  // non-temporal loads of expert rows
 #endif
@@ -874,10 +877,29 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// A token's K slot values (pool rows, weights) for a wave that works on one
+// token: the address is the same in every lane and the arrays are read-only
+// while the kernel runs, so the reads go to the scalar unit, all issued before
+// the first use.  Slots k >= K get `fill`.
+template <int KT, typename V>
+__device__ __forceinline__ void load_slots(const V* p, int t, int K, V fill, V (&out)[KT]) {
+    typedef __attribute__((address_space(4))) const V CV;
+    CV* q = (CV*)(p + (int64_t)t * K);
+#pragma unroll
+    for (int k = 0; k < KT; ++k) out[k] = q[k < K ? k : 0];
+#pragma unroll
+    for (int k = 0; k < KT; ++k)
+        if (k >= K) out[k] = fill;
+}
+
 // One combine work item: segment `seg` of token t (a wave gathers the token's
 // expert rows for that segment, accumulates w * o in fp32 with one fused
-// multiply-add per slot in slot order, and rounds once to bf16).
-template <int KT, bool UNIT>
+// multiply-add per slot in slot order, and rounds once to bf16).  SCALAR: the
+// slot values are read in one batch through the scalar unit, which shortens
+// a wave's start; it is used when the whole grid is resident at once, since
+// at large batches the faster start of every wave was measured slower (more
+// rows in flight at once).
+template <int KT, bool UNIT, bool SCALAR>
 __device__ __forceinline__ int combine_compute(const CombineArgs& a, int t, int seg, int lane,
                                                u32x4 (&out)[EP_COMBINE_UNROLL]) {
     constexpr int U = EP_COMBINE_UNROLL;
@@ -885,10 +907,20 @@ __device__ __forceinline__ int combine_compute(const CombineArgs& a, int t, int 
     const u32x4* eo = (const u32x4*)a.expert_out;
     int rows[KT];
     float wt[KT];
+    if constexpr (SCALAR) {
+        load_slots<KT>(a.slot_to_row, t, a.K, -1, rows);
+        if constexpr (UNIT) {
 #pragma unroll
-    for (int k = 0; k < KT; ++k) {
-        rows[k] = (k < a.K) ? a.slot_to_row[t * a.K + k] : -1;
-        wt[k] = UNIT ? 1.0f : ((k < a.K) ? a.weights[t * a.K + k] : 0.0f);
+            for (int k = 0; k < KT; ++k) wt[k] = 1.0f;
+        } else {
+            load_slots<KT>(a.weights, t, a.K, 0.0f, wt);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+            rows[k] = (k < a.K) ? a.slot_to_row[t * a.K + k] : -1;
+            wt[k] = UNIT ? 1.0f : ((k < a.K) ? a.weights[t * a.K + k] : 0.0f);
+        }
     }
     const int c0 = seg * (kWave * U) + lane;
     u32x4 v[KT][U];
@@ -942,14 +974,14 @@ __device__ __forceinline__ void combine_store(const CombineArgs& a, int t, int s
     }
 }
 
-template <int KT, bool UNIT>
+template <int KT, bool UNIT, bool SCALAR>
 __device__ __forceinline__ void combine_item(const CombineArgs& a, int t, int seg, int lane) {
     u32x4 o[EP_COMBINE_UNROLL];
-    combine_compute<KT, UNIT>(a, t, seg, lane, o);
+    combine_compute<KT, UNIT, SCALAR>(a, t, seg, lane, o);
     combine_store(a, t, seg, lane, o);
 }
 
-template <int KT, bool UNIT>
+template <int KT, bool UNIT, bool SCALAR>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a, int nseg, int ipb) {
     const int lane = threadIdx.x & (kWave - 1);
     const int w = uniform_i(threadIdx.x / kWave);
@@ -957,7 +989,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a, int nseg, int ip
     const int i1 = min(a.T * nseg, i0 + ipb);
     for (int it = i0 + w; it < i1; it += 4) {
         const int t = it / nseg;
-        combine_item<KT, UNIT>(a, t, it - t * nseg, lane);
+        combine_item<KT, UNIT, SCALAR>(a, t, it - t * nseg, lane);
     }
 }
 
@@ -1000,7 +1032,7 @@ __device__ __forceinline__ void gated_items(const CombineArgs& a, int nseg, int 
             if (i < nit && token_of(j) < a.T && ((mask >> j) & 1ull)) {
                 tt[d] = token_of(j);
                 sg[d] = i - j * nseg;
-                combine_compute<KT, false>(a, tt[d], sg[d], lane, o[d]);
+                combine_compute<KT, false, false>(a, tt[d], sg[d], lane, o[d]);
             }
         }
 #pragma unroll
@@ -1486,7 +1518,11 @@ hipError_t combine_kt(const CombineArgs& a, hipStream_t st) {
     const int ipb = items_per_block(nseg, false);
     const int64_t items = (int64_t)a.T * nseg;
     const int grid = (int)((items + ipb - 1) / ipb);
-    hipLaunchKernelGGL((k_combine<KT, UNIT>), dim3(grid), dim3(256), 0, st, a, nseg, ipb);
+    // the whole grid resident at once (one wave per item): scalar slot reads
+    if (items <= (int64_t)a.num_cu * EP_COMBINE_SCALAR_WAVES)
+        hipLaunchKernelGGL((k_combine<KT, UNIT, true>), dim3(grid), dim3(256), 0, st, a, nseg, ipb);
+    else
+        hipLaunchKernelGGL((k_combine<KT, UNIT, false>), dim3(grid), dim3(256), 0, st, a, nseg, ipb);
     return hipGetLastError();
 }
 
