@@ -1219,6 +1219,12 @@ __device__ __forceinline__ uint32_t e4m3_to_bf16_fast(uint32_t code, int e) {
 
 // ---------------------------------------------------- FP8 decode helpers ---
 
+#ifndef EP_CAST_LDS
+#define EP_CAST_LDS 32768      // unused LDS per cast-back workgroup for power-of-two scales
+#endif
+#ifndef EP_CAST_LDS_MIN_GRID
+#define EP_CAST_LDS_MIN_GRID 16384  // ... on grids of at least this many workgroups
+#endif
 #ifndef EP_CAST_UNROLL
 #define EP_CAST_UNROLL 2       // 16-channel units per lane per cast-back work item
 #endif
@@ -1609,7 +1615,14 @@ hipError_t launch_cast_back(const CastBackArgs& a, hipStream_t stream) {
     const int64_t items = a.rows * nseg;
     int64_t grid = (items + 3) / 4;
     if (grid > (1 << 20)) grid = 1 << 20;          // grid-stride beyond a million workgroups
-    hipLaunchKernelGGL(k_cast_back, dim3((uint32_t)grid), dim3(256), 0, stream, a, nseg);
+    // Power-of-two scales decode through the hardware conversion and a large
+    // cast back is memory-bound: unused LDS caps it at five workgroups per
+    // compute unit (160 KB each), so fewer rows are in flight at once, which
+    // measured 6-11 % faster from 16384 rows up.  Small grids are
+    // latency-bound and arbitrary float32 scales take the ALU-heavy software
+    // decode; both keep every wave they can get.
+    const size_t lds = a.scale_kind != kScaleF32 && grid >= EP_CAST_LDS_MIN_GRID ? EP_CAST_LDS : 0;
+    hipLaunchKernelGGL(k_cast_back, dim3((uint32_t)grid), dim3(256), lds, stream, a, nseg);
     return hipGetLastError();
 }
 
