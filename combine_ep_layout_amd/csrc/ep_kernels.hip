@@ -67,7 +67,7 @@
 #define EP_STREAM_THREADS 1024 // threads per streaming workgroup
 #endif
 #ifndef EP_DISPATCH_STORE
-#define EP_DISPATCH_STORE 1    // pool stores outside streaming: see store_row
+#define EP_DISPATCH_STORE 4    // pool stores outside streaming: see store_row
 #endif
 #ifndef EP_COMBINE_STORE
 #define EP_COMBINE_STORE 1     // y stores: see store_row
