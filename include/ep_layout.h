@@ -63,7 +63,7 @@ extern "C" {
 typedef enum ep_status {
     EP_OK = 0,
     EP_ERR_INVALID_ARGUMENT = 1, /* bad pointer, size or flag                      */
-    EP_ERR_UNSUPPORTED = 2,      /* valid request outside what this build handles  */
+    EP_ERR_UNSUPPORTED = 2,      /* valid request outside what the library supports */
     EP_ERR_OUT_OF_MEMORY = 3,    /* device allocation failed in ep_handle_create   */
     EP_ERR_HANDLE_STATE = 4,     /* no layout yet, or epoch does not match         */
     EP_ERR_BAD_ROUTING = 5,      /* device saw expert ids outside [-1, E)          */
