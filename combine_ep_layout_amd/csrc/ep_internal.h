@@ -38,7 +38,7 @@ struct LayoutArgs {
     int32_t* recv_token;        // [cap]
     float* weights;             // [S]
     uint32_t* error;            // [1]
-    int32_t* ws;                // [blocks * E] per-workgroup counts, then bases
+    int32_t* ws;                // [blocks * E] per-workgroup expert counts
     uint32_t* y_done;           // [T] per-token done counts, zeroed here
 };
 

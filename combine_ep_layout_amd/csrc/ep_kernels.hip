@@ -669,8 +669,10 @@ __device__ __forceinline__ uint32_t mag_for_max(uint32_t b) {
 }
 
 // Scale stores of one 64-lane step (8 groups): every lane of a group holds
-// its group's byte (UE8M0) and float (the other flavours).  Device-coherent
-// atomic stores when streaming, so the release stays cheap.
+// its group's byte (UE8M0) and float (the other flavours).  Packed MN-major
+// words and float scales are device-coherent atomic stores when streaming, so
+// the release stays cheap; row-major UE8M0 bytes are plain stores in every
+// mode (when streaming, the release fence writes them back).
 template <bool STREAM, typename V>
 __device__ __forceinline__ void put_scale(V* p, V v) {
     if constexpr (STREAM)
@@ -1617,8 +1619,9 @@ hipError_t launch_cast_back(const CastBackArgs& a, hipStream_t stream) {
     if (grid > (1 << 20)) grid = 1 << 20;          // grid-stride beyond a million workgroups
     // Power-of-two scales decode through the hardware conversion and a large
     // cast back is memory-bound: unused LDS caps it at five workgroups per
-    // compute unit (160 KB each), so fewer rows are in flight at once, which
-    // measured 6-11 % faster from 16384 rows up.  Small grids are
+    // compute unit (160 KB of LDS each), so fewer rows are in flight at once,
+    // which measured 6-11 % faster on grids of 16384 workgroups and up (16384
+    // rows at hidden 7168).  Small grids are
     // latency-bound and arbitrary float32 scales take the ALU-heavy software
     // decode; both keep every wave they can get.
     const size_t lds = a.scale_kind != kScaleF32 && grid >= EP_CAST_LDS_MIN_GRID ? EP_CAST_LDS : 0;

@@ -213,9 +213,10 @@ ep_status ep_combine(const ep_handle* h, uint32_t epoch, const void* expert_out,
  * of that row's token, e.g. ep_tile_consume with EP_CONSUME_SIGNAL_DONE.
  *   round          >= 1: producer passes since ep_layout this call waits for.
  *   spin_limit_us  bound on one token's wait; past it, or once any wait of
- *                  this handle has timed out, the remaining waiting tokens are
- *                  skipped (their y rows are left as they were) and
- *                  EP_ERR_TIMEOUT is set in the error word.
+ *                  this handle has timed out (in this call or an earlier one,
+ *                  until ep_handle_sync_status clears the error word), the
+ *                  remaining waiting tokens are skipped (their y rows are left
+ *                  as they were) and EP_ERR_TIMEOUT is set in the error word.
  * Everything else as ep_combine: the result equals ep_combine's bit for bit. */
 ep_status ep_combine_gated(const ep_handle* h, uint32_t epoch, const void* expert_out,
                            int32_t hidden, void* y, uint32_t round, uint32_t spin_limit_us,
