@@ -277,6 +277,27 @@ def _time_us(fn, steps: int, warmup: int, stream) -> float:
     return a.elapsed_time(b) / steps * 1e3
 
 
+def _time_in_step_us(before, fn, after, steps: int, warmup: int, stream) -> float:
+    """Mean duration of fn's launches when each one runs between `before` and
+    `after` (the kernels around it in a step), from HIP events on `stream`."""
+    import torch
+    for _ in range(warmup):
+        before()
+        fn()
+        after()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        before()
+        a.record(stream)
+        fn()
+        b.record(stream)
+        after()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+
+
 def graph_bench(cfg, steps: int, warmup: int, per_replay: int = 4) -> dict:
     """The layout -> dispatch -> combine step launched eagerly vs captured in
     a HIP graph of `per_replay` steps (torch's graph capture on the library's
@@ -422,7 +443,11 @@ def fp8_variants_bench(cfg, steps: int, warmup: int) -> dict:
     """FP8 dispatch in every scale flavour and layout, and the cast back of
     the used pool rows.  Dispatch bytes as in the main benchmark (scale bytes
     1 per group for UE8M0, 4 for float32); cast back reads P rows of codes and
-    their scales and writes P bf16 rows (P = used pool rows)."""
+    their scales and writes P bf16 rows (P = used pool rows).  The dispatch is
+    timed inside the layout -> dispatch -> combine step, as in the main
+    benchmark: timed back to back on its own, the scale array would stay in
+    the caches between calls, which hides what partial-line scale writes cost
+    in a pipeline.  The cast back is timed back to back."""
     import torch
     import combine_ep_layout_amd as ep
     from synth import generate
@@ -442,14 +467,27 @@ def fp8_variants_bench(cfg, steps: int, warmup: int) -> dict:
     n_a = int(valid.sum())
     t_act = int(valid.any(1).sum())
     out = torch.empty(P, H, dtype=torch.bfloat16, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1)
+    eo = torch.randn(h.capacity_rows, H, generator=g, device=dev).to(torch.bfloat16)
+    y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    state = {}
+
+    def before():
+        state["epoch"] = h.layout(idx, w)
+
+    def after():
+        h.combine(state["epoch"], eo, y)
+
     combos = [(kind, mn) for kind in ("ue8m0", "f32", "pow2_f32") for mn in (False, True)]
     pools = {c: h.new_pool(H, fp8=True, scale_kind=c[0], mn_major=c[1]) for c in combos}
     best = {}
     for rep in range(2):                  # two passes over every combination, best of each
         for kind, mn in combos:
             pool, scales = pools[(kind, mn)]
-            t_d = _time_us(lambda: h.dispatch(x, pool, scales, fp8=True, scale_kind=kind,
-                                              mn_major=mn), steps, warmup, stream)
+            t_d = _time_in_step_us(before, lambda: h.dispatch(x, pool, scales, fp8=True,
+                                                              scale_kind=kind, mn_major=mn),
+                                   after, steps, warmup, stream)
             t_c = _time_us(lambda: ep.cast_back(pool, scales, kind, mn, rows=P, out=out),
                            steps, warmup, stream)
             o = best.get((kind, mn), (1e18, 1e18))

@@ -95,6 +95,16 @@ constexpr int kWaveSlots = kLayoutSlotsPerBlock / kLayoutWaves;       // slots p
 
 __device__ __forceinline__ int uniform_i(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// The hardware hands workgroup b to XCD b mod 8.  This bijection of [0, G)
+// gives XCD x the contiguous blocks [x*G/8, (x+1)*G/8) instead (the first
+// G mod 8 XCDs take one block more), so the tokens one XCD works on are
+// consecutive.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_contiguous_block(int b, int G) {
+    const int q = G / kXcds, r = G % kXcds, x = b % kXcds, j = b / kXcds;
+    return x * q + (x < r ? x : r) + j;
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
     const int lane = threadIdx.x & (kWave - 1);
     return (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
@@ -747,7 +757,15 @@ __global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg,
     const int nw = (int)blockDim.x / kWave;
     const int nchunk = STREAM ? (a.T + EP_STREAM_TOKENS - 1) / EP_STREAM_TOKENS : 1;
     for (int ch = STREAM ? (int)blockIdx.x : 0; ch < nchunk; ch += STREAM ? (int)gridDim.x : 1) {
-    const int i0 = STREAM ? ch * EP_STREAM_TOKENS * nseg : (int)blockIdx.x * ipb;
+    // Float32 scales are 4-byte entries whose cache lines are shared by
+    // consecutive pool rows of an expert, i.e. by consecutive tokens.  With
+    // each XCD on a contiguous token range those lines are completed in one
+    // L2 before they are written back, instead of in pieces from all eight
+    // (measured 1-11 % faster for the float flavours at 16384 tokens; bf16
+    // and UE8M0 keep the round-robin, which measured slightly faster there).
+    const int blk = a.scale_kind != kScaleUe8m0 ? xcd_contiguous_block((int)blockIdx.x, (int)gridDim.x)
+                                                : (int)blockIdx.x;
+    const int i0 = STREAM ? ch * EP_STREAM_TOKENS * nseg : blk * ipb;
     const int i1 = min(a.T * nseg, STREAM ? i0 + EP_STREAM_TOKENS * nseg : i0 + ipb);
     // a wave's items are software-pipelined: the next item's rows and x
     // segment are loaded before the current one is quantised and stored
