@@ -9,6 +9,8 @@ other than itself): layout, bf16 dispatch, FP8 quantisation (scale exponent and
 e4m3fn codes) in the UE8M0, float32 and power-of-two float32 scale flavours,
 the MN-major and packed scale layouts, dequantisation (cast back), combine,
 combine and dispatch backward.  Nothing here is "parity unpinned".
+tests/test_oracle_mutants.py plants plausible mistakes in a copy of the C
+source and checks that the pins reject every one.
 """
 from __future__ import annotations
 

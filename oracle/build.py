@@ -13,15 +13,16 @@ SRC = os.path.join(HERE, "ep_oracle.c")
 LIB = os.path.join(HERE, "libep_oracle.so")
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
+def build(verbose: bool = False, src: str = SRC, out: str = LIB) -> str:
+    """Compile `src` (the oracle's C source, or a copy of it) into `out`."""
+    tmp = out + ".tmp"
     cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
-           "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, SRC, "-lm"]
+           "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, src, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -11,6 +11,7 @@ closed forms: identity experts with weights summing to one return x
 bit-exactly, and the tiny workload's scaled experts give x * sum_k w_k (e_k+1)/8.
 """
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -155,3 +156,53 @@ def test_single_slot_weight_one_is_copy_and_zero_weight_is_zero():
     assert np.array_equal(bf16_to_f32(y0), np.zeros((3, 64), np.float32))
     yh = oracle.combine(o, s2r, np.full((3, 1), 0.5, np.float32))
     assert np.array_equal(bf16_to_f32(yh), bf16_to_f32(o[[2, 0, 1]]) * np.float32(0.5))
+
+
+def test_nan_rounds_to_the_quiet_nan_with_its_sign():
+    """NaN of any payload rounds to the quiet NaN 0x7FC0 with its sign kept
+    (reading 10's final rounding).  Patterns with low payload bits only are
+    the ones a truncating conversion would turn into infinity.  (Not compared
+    with torch: its vectorised CPU cast writes other NaN patterns.)"""
+    pos = np.array([0x7F800001, 0x7F80FFFF, 0x7FA00000, 0x7FC00000, 0x7FFFFFFF], np.uint32)
+    got = oracle.f32_to_bf16_n(np.concatenate([pos, pos | 0x80000000]).view(np.float32))
+    assert np.array_equal(got[:5], np.full(5, 0x7FC0, np.uint16))
+    assert np.array_equal(got[5:], np.full(5, 0xFFC0, np.uint16))
+
+
+def test_fp32_fma_chain_in_ascending_slot_order():
+    """Reading 10 fixes the accumulation: fp32 from +0, one fused
+    multiply-add per unmasked slot in ascending k, one rounding to bf16.  Two
+    hand-worked tokens sit on bf16 rounding midpoints, where any other
+    accumulation rounds the other way.
+    Token 0, slots (w, o) = (1 + 2^-8, 1), (1, 2^-24), (1, 2^-24): in
+    ascending order each 2^-24 lands on an fp32 tie and rounds back (to even)
+    to 1 + 2^-8, a bf16 tie that rounds to even: 1.0 (0x3F80).  Descending
+    slots, or an exact sum, reach 1 + 2^-8 + 2^-23, which rounds up to 0x3F81.
+    Token 1, slots (1, 1), (w2, 3) with w2 = 0x3AAAAB56, so that w2 * 3 =
+    2^-8 + 2^-24 + 2^-32 exactly: the fused step rounds 1 + w2 * 3 once, up
+    to 1 + 2^-8 + 2^-23: 0x3F81.  A separate multiply first rounds the product
+    to 2^-8 + 2^-24 (an fp32 tie, to even), and the add then ties to even at
+    1 + 2^-8: 0x3F80."""
+    w2 = float(np.array([0x3AAAAB56], np.uint32).view(np.float32)[0])
+    assert Fraction(w2) * 3 == Fraction(1, 2**8) + Fraction(1, 2**24) + Fraction(1, 2**32)
+    H = 8
+    # rows: 1.0, 2^-24, 2^-24, 1.0, 3.0 as bf16 patterns
+    eo = np.repeat(np.array([0x3F80, 0x3380, 0x3380, 0x3F80, 0x4040], np.uint16)[:, None], H, 1)
+    s2r = np.array([0, 1, 2, 3, 4, -1], np.int32)
+    w = np.array([[1 + 2.0 ** -8, 1.0, 1.0], [1.0, w2, 0.0]], np.float32)
+    assert float(w[0, 0]) == 1 + 2.0 ** -8 and float(w[1, 1]) == w2
+    y = oracle.combine(eo, s2r, w)
+    assert np.array_equal(y, np.array([[0x3F80] * H, [0x3F81] * H], np.uint16))
+    valid = (s2r >= 0).reshape(2, 3)
+    y2 = oracle.combine_gathered(eo[np.where(s2r >= 0, s2r, 0)].reshape(2, 3, H), valid, w)
+    assert np.array_equal(y2, y)
+
+
+def test_gathered_combine_skips_masked_slots():
+    """A masked slot takes no part even when its gathered row is NaN and its
+    weight is not zero: y = bf16(1 * x) = x."""
+    rng = np.random.default_rng(3)
+    x = bf16_from_f32(rng.standard_normal(64, dtype=np.float32))
+    rows = np.stack([x, np.full(64, 0x7FC0, np.uint16)])[None]
+    y = oracle.combine_gathered(rows, np.array([[True, False]]), np.array([[1.0, 0.5]], np.float32))
+    assert np.array_equal(y[0], x)
