@@ -143,19 +143,22 @@ def test_quantize_row_error_bound_and_scale_rule():
 
 
 def test_dequant_is_exact():
+    """value(code) * 2^e for every non-NaN code; one row per exponent, all
+    rows decoded in one call, so each row must take its own scales."""
     codes = np.arange(256, dtype=np.uint8)
     codes = codes[(codes & 0x7F) != 0x7F]
     _, vals = _table()
-    for e in (-127, -100, -9, 0, 7, 100):
-        n = len(codes)
-        H = 128 * ((n + 127) // 128)
-        q = np.zeros(H, np.uint8)
-        q[:n] = codes
-        s = np.full(H // 128, e + 127, np.uint8)
-        got = oracle.dequant_rows(q[None, :], s[None, :])[0][:n]
+    exps = (-127, -100, -9, 0, 7, 100)
+    n = len(codes)
+    H = 128 * ((n + 127) // 128)
+    q = np.zeros((len(exps), H), np.uint8)
+    q[:, :n] = codes
+    s = np.array([[e + 127] * (H // 128) for e in exps], np.uint8)
+    got = oracle.dequant_rows(q, s)
+    for i, e in enumerate(exps):
         mag = vals[codes & 0x7F] * 2.0 ** e
         want = bf16_from_f32(np.where(codes & 0x80, -mag, mag).astype(np.float32))
-        assert np.array_equal(got, want), e
+        assert np.array_equal(got[i][:n], want), e
 
 
 def test_quantize_roundtrip_on_e4m3_grid():

@@ -1,16 +1,19 @@
 """Planted mistakes: the oracle's pins must reject a wrong oracle (CPU only).
 
-Each case copies oracle/ep_oracle.c, plants one plausible mistake by a
-textual substitution (a wrong tie rule, an off-by-one exponent, a dropped
-weight, a sign error, a transposed index, another accumulation order ...),
-compiles the copy with the oracle's own build flags into a temporary library,
-points the oracle package at it, and runs the pins of tests/test_oracle_*.py
-until one fails.  A mistake that no pin notices fails this test.  The
-committed source is never modified; the baseline case runs every pin against
-an unmodified copy built the same way, so a harness that always fails would be
-caught too.
+Each case copies oracle/ep_oracle.c, or oracle/__init__.py for the scale
+layouts, packing, capacity and decode glue written in Python, and plants one
+plausible mistake by a textual substitution: a wrong tie rule, an off-by-one
+exponent, a dropped weight, a sign error, a transposed index, another
+accumulation order.  A C copy is compiled with the oracle's own build flags
+into a temporary library and the oracle package is pointed at it; a Python
+copy is executed as a module and handed to the pins in place of the package.
+The pins of tests/test_oracle_*.py then run until one fails.  A mistake that
+no pin notices fails this test.  The committed sources are never modified,
+and the baseline cases run every pin against unmodified copies handled the
+same way, so a harness that always fails would be caught too.
 """
 import os
+import types
 
 import pytest
 
@@ -150,6 +153,39 @@ MUTANTS = [
 ]
 
 
+# the same for the Python half of the oracle (oracle/__init__.py)
+PY_MUTANTS = [
+    ("capacity without the -1",
+     "return tokens * top_k + num_experts * (block_m - 1)", "return tokens * top_k + num_experts * block_m"),
+    ("power-of-two scale with bias 128",
+     "e = scale_bytes.astype(np.int64) - 127", "e = scale_bytes.astype(np.int64) - 128"),
+    ("packed UE8M0 words in the wrong byte order",
+     "word |= int(scales[r, g]) << (8 * j)", "word |= int(scales[r, g]) << (8 * (3 - j))"),
+    ("packed words per row rounded down",
+     "return (groups + 3) // 4", "return groups // 4 if groups >= 4 else 1"),
+    ("MN-major float32 groups reversed",
+     "out[:, r] = scales[r, :]", "out[:, r] = scales[r, ::-1]"),
+    ("MN-major unpacking in the wrong byte order",
+     "(int(mn[g // 4, r]) >> (8 * (g % 4)))", "(int(mn[g // 4, r]) >> (8 * (3 - g % 4)))"),
+    ("power-of-two flavour stores the UE8M0 byte",
+     "rm[r] = b if kind == SCALE_UE8M0 else pow2_scales_from_ue8m0(b)", "rm[r] = b"),
+    ("scaled dispatch overwrites the padding rows' scales",
+     "scales[real] = rm[real]", "scales[:] = rm"),
+    ("cast back decodes power-of-two floats as UE8M0 bytes",
+     "    if kind == SCALE_UE8M0:\n        return dequant_rows(q, rm)",
+     "    if kind != SCALE_F32:\n        return dequant_rows(q, rm)"),
+    ("float32 dequantisation takes row 0's scales for every row",
+     "lib.eo_dequant_row_f32scale(_p(q[i]), _p(scales[i]), H, _p(out[i]))",
+     "lib.eo_dequant_row_f32scale(_p(q[i]), _p(scales[0]), H, _p(out[i]))"),
+    ("UE8M0 dequantisation takes row 0's scales for every row",
+     "lib.eo_dequant_row(_p(q[i]), _p(scales[i]), H, _p(out[i]))",
+     "lib.eo_dequant_row(_p(q[i]), _p(scales[0]), H, _p(out[i]))"),
+]
+
+PIN_MODULES = [tl, tc, td, tf, tb]
+PY_SOURCE = os.path.join(os.path.dirname(oracle_build.SRC), "__init__.py")
+
+
 def _source() -> str:
     with open(oracle_build.SRC) as f:
         return f.read()
@@ -163,12 +199,28 @@ def _first_failing_pin(text: str, tmp_path, monkeypatch):
     lib = oracle_build.build(src=str(src), out=str(tmp_path / "libep_oracle_variant.so"))
     monkeypatch.setattr(oracle, "_LIB_PATH", lib)
     monkeypatch.setattr(oracle, "_lib", None)
+    return _run_pins()
+
+
+def _run_pins():
     for name, pin in PINS:
         try:
             pin()
         except Exception:                   # an assertion, or an error the mistake causes
             return name
     return None
+
+
+def _first_failing_pin_py(text: str, monkeypatch):
+    """Execute `text` as the oracle's Python half (loading the real C
+    library) and hand it to the pins in place of the package."""
+    oracle._load()                          # builds the C library if it is missing
+    mod = types.ModuleType("oracle_variant")
+    mod.__file__ = PY_SOURCE
+    exec(compile(text, PY_SOURCE, "exec"), mod.__dict__)
+    for m in PIN_MODULES:
+        monkeypatch.setattr(m, "oracle", mod)
+    return _run_pins()
 
 
 def test_unmodified_copy_passes_every_pin(tmp_path, monkeypatch):
@@ -181,3 +233,16 @@ def test_planted_mistake_is_caught(what, old, new, tmp_path, monkeypatch):
     assert text.count(old) == 1, "the planted text must replace exactly one place"
     caught_by = _first_failing_pin(text.replace(old, new), tmp_path, monkeypatch)
     assert caught_by is not None, f"no pin notices: {what}"
+
+
+def test_unmodified_python_copy_passes_every_pin(monkeypatch):
+    with open(PY_SOURCE) as f:
+        assert _first_failing_pin_py(f.read(), monkeypatch) is None
+
+
+@pytest.mark.parametrize("what,old,new", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
+def test_planted_python_mistake_is_caught(what, old, new, monkeypatch):
+    with open(PY_SOURCE) as f:
+        text = f.read()
+    assert text.count(old) == 1, "the planted text must replace exactly one place"
+    assert _first_failing_pin_py(text.replace(old, new), monkeypatch) is not None, f"no pin notices: {what}"
