@@ -49,6 +49,20 @@
  *     it has completed.
  *   - Arrays: x, pool, expert_out and y are row-major; bf16 values are passed
  *     as their 16-bit patterns.
+ *   - HIP graph capture: ep_layout, ep_dispatch, ep_combine, ep_combine_gated,
+ *     the backward calls and ep_fp8_cast_back only launch kernels (nothing is
+ *     allocated and no memory is set through the runtime), so they can be
+ *     captured and replayed.  The host-side counters advance when a call is
+ *     captured, not when it is replayed: a replay repeats the captured epoch,
+ *     sequence number and streaming round.  A replayed ep_layout re-zeroes the
+ *     arrival counts and the per-token done counts, so the captured rounds
+ *     stay right when the layout is in the same graph.  tile_ready is never
+ *     reset, though: a replayed EP_DISPATCH_TILE_READY dispatch stamps the same
+ *     sequence number as the replay before it, so a consumer in that graph
+ *     would see the old stamp and could read a tile before it is rewritten.
+ *     Streaming dispatches and their consumers are therefore issued outside
+ *     graphs.  The BLOCKING calls and ep_borrow_release (which records an
+ *     event) are not for capture either.
  */
 #ifndef EP_LAYOUT_H
 #define EP_LAYOUT_H
