@@ -230,6 +230,8 @@ ep_status ep_layout(ep_handle* h, const int32_t* topk_idx, const float* topk_wei
     a.tile_expert = h->tile_expert;
     a.tile_target = h->tile_target;
     a.arrival = h->arrival;
+    a.tile_ready = h->tile_ready;
+    a.seq_base = h->seq;
     a.slot_to_row = h->slot_to_row;
     a.recv_token = h->recv_token;
     a.weights = h->weights;

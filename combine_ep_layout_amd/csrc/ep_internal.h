@@ -34,6 +34,8 @@ struct LayoutArgs {
     int32_t* tile_expert;       // [max_tiles]
     int32_t* tile_target;       // [max_tiles]
     uint32_t* arrival;          // [max_tiles]
+    uint32_t* tile_ready;       // [max_tiles], used tiles set to seq_base
+    uint32_t seq_base;          // sequence number of the handle's last dispatch
     int32_t* slot_to_row;       // [S]
     int32_t* recv_token;        // [cap]
     float* weights;             // [S]

@@ -386,6 +386,9 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
             a.tile_expert[j0 + i] = e;
             a.tile_target[j0 + i] = left < BM ? left : BM;
             a.arrival[j0 + i] = 0u;
+            // not ready for any dispatch after this layout (whose sequence
+            // numbers come after seq_base), also when a graph replays both
+            a.tile_ready[j0 + i] = a.seq_base;
         }
         for (int r = j0 * BM + cnt + lane; r < (j0 + nt) * BM; r += kWave) a.recv_token[r] = -1;
     }

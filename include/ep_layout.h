@@ -55,14 +55,13 @@
  *     captured and replayed.  The host-side counters advance when a call is
  *     captured, not when it is replayed: a replay repeats the captured epoch,
  *     sequence number and streaming round.  A replayed ep_layout re-zeroes the
- *     arrival counts and the per-token done counts, so the captured rounds
- *     stay right when the layout is in the same graph.  tile_ready is never
- *     reset, though: a replayed EP_DISPATCH_TILE_READY dispatch stamps the same
- *     sequence number as the replay before it, so a consumer in that graph
- *     would see the old stamp and could read a tile before it is rewritten.
- *     Streaming dispatches and their consumers are therefore issued outside
- *     graphs.  The BLOCKING calls and ep_borrow_release (which records an
- *     event) are not for capture either.
+ *     arrival counts and the per-token done counts and re-stamps its tiles'
+ *     tile_ready with the captured base (the sequence number before the
+ *     captured dispatches), so a streaming dispatch and its consumer captured
+ *     after the layout wait for that replay's stamps, not the last replay's.
+ *     A streaming dispatch replayed without its layout would repeat the last
+ *     replay's stamp, and its consumer could pass early.  The BLOCKING calls
+ *     and ep_borrow_release (which records an event) are not for capture.
  */
 #ifndef EP_LAYOUT_H
 #define EP_LAYOUT_H
@@ -173,7 +172,10 @@ int64_t ep_scale_ld(const ep_handle* h);
  *   slot_to_pool_row[t*K+k]      pool row of slot (t,k), -1 if masked
  *   pool_recv_token[r]           source token of pool row r, -1 for padding
  * Rows of one expert are in ascending slot order t*K+k.  pool_arrival_count is
- * zeroed for the layout's tiles and y_done_per_token for its tokens.  Ids outside [-1, E) are treated as masked and
+ * zeroed for the layout's tiles and y_done_per_token for its tokens, and the
+ * layout's tiles get tile_ready = the sequence number of the handle's last
+ * dispatch (0 before the first), so no tile reads as ready for a dispatch
+ * that comes after the layout.  Ids outside [-1, E) are treated as masked and
  * set EP_ERR_BAD_ROUTING in the error word.  Invalidates earlier epochs. */
 ep_status ep_layout(ep_handle* h, const int32_t* topk_idx, const float* topk_weights,
                     int32_t num_tokens, hipStream_t stream, uint32_t* epoch_out);

@@ -106,3 +106,35 @@ def test_streaming_dispatch_pool_bytes(name, tokens, fp8):
     say(f"[stream] pool bytes with tile_ready: {name} tokens={tokens} fp8={fp8}")
     cfg, d = inputs(name, tokens)
     full_path_check(cfg, d, fp8=fp8, tile_ready=True)
+
+
+def test_layout_stamps_its_tiles_with_the_last_sequence_number():
+    """ep_layout sets its tiles' tile_ready to the sequence number of the
+    handle's last dispatch, so no tile reads as ready for a dispatch issued
+    after the layout.  (A HIP graph replays layout and dispatch with the
+    sequence numbers captured, so without this stamp a replayed streaming
+    dispatch would find the previous replay's stamps already in place.)"""
+    import combine_ep_layout_amd as ep
+    say("[stream] layout stamps tile_ready with the last sequence number")
+    cfg, d = inputs("stream", 2000)
+    _, d2 = inputs("stream", 2000, seed=5)             # a second routing of the same size
+    L = oracle.layout(d["topk_idx"], cfg.num_experts, cfg.block_m)
+    L2 = oracle.layout(d2["topk_idx"], cfg.num_experts, cfg.block_m)
+    h = new_handle(cfg)
+
+    def ready(n):
+        return h.array("tile_ready").cpu().numpy().view(np.uint32)[:n]
+
+    h.layout(*device_routing(d))
+    assert (ready(L["num_tiles"]) == 0).all()          # no dispatch yet
+    pool, scales = h.new_pool(cfg.hidden, fp8=True)
+    s1 = h.dispatch(to_dev_bf16(d["x"]), pool, scales, fp8=True, tile_ready=True)
+    assert (ready(L["num_tiles"]) == s1).all()
+    s2 = h.dispatch(to_dev_bf16(d["x"]), pool, scales, fp8=True)   # not streaming: no stamps
+    assert s2 == s1 + 1 and (ready(L["num_tiles"]) == s1).all()
+    h.layout(*device_routing(d2))
+    assert (ready(L2["num_tiles"]) == s2).all()        # below the next dispatch's number
+    s3 = h.dispatch(to_dev_bf16(d2["x"]), pool, scales, fp8=True, tile_ready=True)
+    assert s3 == s2 + 1 and (ready(L2["num_tiles"]) == s3).all()
+    assert h.sync_status() == ep.EP_OK
+    h.close()
