@@ -33,6 +33,11 @@ struct ep_handle {
     uint32_t* error;
     int32_t* ws;
     uint32_t* y_done;         // per-token done counts of the combine gate
+    // routing density of the last completed layout (epk::Density), written by
+    // the layout kernel into pinned host memory and read by ep_combine for
+    // its launch shape; density_dev is the device's address of the word
+    int32_t* density_host;
+    int32_t* density_dev;
     // host state of the current layout
     int32_t T;                // tokens of the current layout, -1 before the first
     uint32_t epoch;
@@ -178,6 +183,22 @@ ep_status ep_handle_create(const ep_config* cfg, ep_handle** out) {
         delete h;
         return EP_ERR_HIP;
     }
+    if (hipHostMalloc((void**)&h->density_host, 64, hipHostMallocDefault) != hipSuccess) {
+        (void)hipGetLastError();
+        (void)hipEventDestroy(h->lease_event);
+        (void)hipFree(h->block);
+        delete h;
+        return EP_ERR_OUT_OF_MEMORY;
+    }
+    __atomic_store_n(h->density_host, (int32_t)epk::kDensityUnknown, __ATOMIC_RELAXED);
+    if (hipHostGetDevicePointer((void**)&h->density_dev, h->density_host, 0) != hipSuccess ||
+        !h->density_dev) {
+        (void)hipHostFree(h->density_host);
+        (void)hipEventDestroy(h->lease_event);
+        (void)hipFree(h->block);
+        delete h;
+        return EP_ERR_HIP;
+    }
     h->lease = false;
     h->lease_wait = false;
     *out = h;
@@ -192,6 +213,8 @@ ep_status ep_handle_destroy(ep_handle* h) {
     if (e == hipSuccess && cur != h->device) e = hipSetDevice(h->device);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     hipError_t f = hipFree(h->block);
+    if (f == hipSuccess) f = hipHostFree(h->density_host);
+    else (void)hipHostFree(h->density_host);
     (void)hipEventDestroy(h->lease_event);
     if (cur != h->device) (void)hipSetDevice(cur);
     delete h;
@@ -238,6 +261,7 @@ ep_status ep_layout(ep_handle* h, const int32_t* topk_idx, const float* topk_wei
     a.error = h->error;
     a.ws = h->ws;
     a.y_done = h->y_done;
+    a.density = h->density_dev;
     ep_status st = hip_status(epk::launch_layout(a, stream));
     if (st != EP_OK) return st;
     h->T = num_tokens;
@@ -322,6 +346,9 @@ ep_status ep_combine(const ep_handle* h, uint32_t epoch, const void* expert_out,
     a.weights = h->weights;
     a.y = y;
     a.num_cu = h->num_cu;
+    // the density of the latest layout whose kernel has finished (the one
+    // just enqueued may not have run yet): it chooses the launch shape only
+    a.density = __atomic_load_n(h->density_host, __ATOMIC_RELAXED);
     return hip_status(epk::launch_combine(a, stream));
 }
 
@@ -412,6 +439,7 @@ ep_status ep_dispatch_backward(const ep_handle* h, uint32_t epoch, const void* g
     a.weights = nullptr;
     a.y = grad_x;
     a.num_cu = h->num_cu;
+    a.density = __atomic_load_n(h->density_host, __ATOMIC_RELAXED);   // launch shape, as ep_combine
     return hip_status(epk::launch_combine_unit(a, stream));
 }
 

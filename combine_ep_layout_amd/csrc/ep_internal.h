@@ -42,6 +42,15 @@ struct LayoutArgs {
     uint32_t* error;            // [1]
     int32_t* ws;                // [blocks * E] per-workgroup expert counts
     uint32_t* y_done;           // [T] per-token done counts, zeroed here
+    int32_t* density;           // host-mapped word: kDensitySparse / kDensityDense
+};
+
+// Routing density of a layout, as the layout reports it for the next combine's
+// launch shape (results never depend on it).
+enum Density : int32_t {
+    kDensityUnknown = 0,        // no layout reported yet
+    kDensitySparse = 1,         // fewer than 4 real rows per token on average
+    kDensityDense = 2,          // 4 or more
 };
 
 // Scale flavours of the FP8 dispatch and the cast back.
@@ -88,6 +97,7 @@ struct CombineArgs {
     uint64_t limit_ticks;
     uint32_t* error;
     int32_t num_cu;             // compute units of the device (launch shapes)
+    int32_t density;            // Density of the last layout that reported one (launch shape)
 };
 
 struct CombineBwdArgs {

@@ -72,8 +72,11 @@
 #ifndef EP_COMBINE_STORE
 #define EP_COMBINE_STORE 1     // y stores: see store_row
 #endif
-#ifndef EP_COMBINE_SCALAR_WAVES
-#define EP_COMBINE_SCALAR_WAVES 8  // grids up to this many waves per compute unit read slots as scalars
+#ifndef EP_COMBINE_RESIDENT_WAVES
+#define EP_COMBINE_RESIDENT_WAVES 8  // combine grids up to this many waves per CU run at full occupancy
+#endif
+#ifndef EP_COMBINE_DENSE_LDS
+#define EP_COMBINE_DENSE_LDS 55296  // unused LDS per combine workgroup for dense routing: 2 per CU
 #endif
 #ifndef EP_COMBINE_NT_LOADS
 #define EP_COMBINE_NT_LOADS 1  // non-temporal loads of expert rows
@@ -408,11 +411,26 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
     for (int t = tb0 + tid; t < tb1; t += kLayoutThreads) a.y_done[t] = 0u;
     // counts, first tiles and the tile total (workgroup 0)
     if (b == 0) {
+        int rows = 0;
         for (int e = tid; e <= E; e += kLayoutThreads) {
-            if (e < E) a.counts[e] = s_cnt[e];
+            if (e < E) {
+                a.counts[e] = s_cnt[e];
+                rows += s_cnt[e];
+            }
             a.offsets[e] = s_off[e];
         }
         if (tid == 0) *a.num_tiles = s_off[E];
+        // the layout's density for the next combine's launch shape: real rows
+        // summed over the experts (s_tmp is free once the scans are done)
+        for (int d = kWave / 2; d > 0; d >>= 1) rows += __shfl_xor(rows, d, kWave);
+        if (lane == 0) s_tmp[w] = rows;
+        __syncthreads();
+        if (tid == 0 && a.density) {
+            int total_rows = 0;
+            for (int i = 0; i < kLayoutWaves; ++i) total_rows += s_tmp[i];
+            __hip_atomic_store(a.density, (int64_t)total_rows >= 4 * (int64_t)T ? kDensityDense : kDensitySparse,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
     }
 }
 
@@ -918,10 +936,10 @@ __device__ __forceinline__ void load_slots(const V* p, int t, int K, V fill, V (
 // One combine work item: segment `seg` of token t (a wave gathers the token's
 // expert rows for that segment, accumulates w * o in fp32 with one fused
 // multiply-add per slot in slot order, and rounds once to bf16).  SCALAR: the
-// slot values are read in one batch through the scalar unit, which shortens
-// a wave's start; it is used when the whole grid is resident at once, since
-// at large batches the faster start of every wave was measured slower (more
-// rows in flight at once).
+// slot values are read in one batch through the scalar unit, so a wave issues
+// all its row loads at once (the plain combine; its launcher sets how many
+// waves run at a time).  Otherwise they are read as vector loads, one slot
+// after another (the gated combine).
 template <int KT, bool UNIT, bool SCALAR>
 __device__ __forceinline__ int combine_compute(const CombineArgs& a, int t, int seg, int lane,
                                                u32x4 (&out)[EP_COMBINE_UNROLL]) {
@@ -997,14 +1015,7 @@ __device__ __forceinline__ void combine_store(const CombineArgs& a, int t, int s
     }
 }
 
-template <int KT, bool UNIT, bool SCALAR>
-__device__ __forceinline__ void combine_item(const CombineArgs& a, int t, int seg, int lane) {
-    u32x4 o[EP_COMBINE_UNROLL];
-    combine_compute<KT, UNIT, SCALAR>(a, t, seg, lane, o);
-    combine_store(a, t, seg, lane, o);
-}
-
-template <int KT, bool UNIT, bool SCALAR>
+template <int KT, bool UNIT>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a, int nseg, int ipb) {
     const int lane = threadIdx.x & (kWave - 1);
     const int w = uniform_i(threadIdx.x / kWave);
@@ -1012,7 +1023,10 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a, int nseg, int ip
     const int i1 = min(a.T * nseg, i0 + ipb);
     for (int it = i0 + w; it < i1; it += 4) {
         const int t = it / nseg;
-        combine_item<KT, UNIT, SCALAR>(a, t, it - t * nseg, lane);
+        const int seg = it - t * nseg;
+        u32x4 o[EP_COMBINE_UNROLL];
+        combine_compute<KT, UNIT, true>(a, t, seg, lane, o);
+        combine_store(a, t, seg, lane, o);
     }
 }
 
@@ -1547,11 +1561,19 @@ hipError_t combine_kt(const CombineArgs& a, hipStream_t st) {
     const int ipb = items_per_block(nseg, false);
     const int64_t items = (int64_t)a.T * nseg;
     const int grid = (int)((items + ipb - 1) / ipb);
-    // the whole grid resident at once (one wave per item): scalar slot reads
-    if (items <= (int64_t)a.num_cu * EP_COMBINE_SCALAR_WAVES)
-        hipLaunchKernelGGL((k_combine<KT, UNIT, true>), dim3(grid), dim3(256), 0, st, a, nseg, ipb);
-    else
-        hipLaunchKernelGGL((k_combine<KT, UNIT, false>), dim3(grid), dim3(256), 0, st, a, nseg, ipb);
+    // Launch shape; the kernel and its results are the same in every shape.
+    // A resident grid (one wave per item), or sparse routing, runs at full
+    // occupancy.  Dense routing (4 or more rows per token) is capped at two
+    // 4-wave workgroups per compute unit by unused LDS: with every wave
+    // issuing all its row loads at once, that was the fastest shape for it
+    // (345 against 375 us at full occupancy, 16384 tokens x top-8), while
+    // sparse routing is latency-bound and wants every wave (23 against 38 us).
+    // The density is the one the last completed layout on the handle
+    // reported; before any has, the dense shape is taken, where a wrong guess
+    // costs least.
+    const bool resident = items <= (int64_t)a.num_cu * EP_COMBINE_RESIDENT_WAVES;
+    const size_t lds = (resident || a.density == kDensitySparse) ? 0 : EP_COMBINE_DENSE_LDS;
+    hipLaunchKernelGGL((k_combine<KT, UNIT>), dim3(grid), dim3(256), lds, st, a, nseg, ipb);
     return hipGetLastError();
 }
 

@@ -158,3 +158,36 @@ def test_nan_padding_is_never_read():
     assert not torch.isnan(y1).any()
     assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
     h.close()
+
+
+def test_combine_after_dense_and_sparse_layouts():
+    """The plain combine and the dispatch backward take their launch shape
+    from the density the last completed layout on the handle reported (two
+    workgroups per compute unit for 4 or more rows per token, full occupancy
+    below); the results do not depend on it.  One handle alternates a dense
+    and a sparse routing of the same size, with the stream synchronised after
+    each layout so that its density is the one in force, and every combine
+    and dispatch backward is compared with the oracle."""
+    say("[combine] alternating dense / sparse layouts on one handle, 6000 tokens")
+    dense = CONFIGS["stream"].replace(tokens=6000, hidden=1024, mask_frac=0.0, fp8=False,
+                                      tile_ready=False)
+    sparse = CONFIGS["share"].replace(tokens=6000, hidden=1024, num_experts=128, experts_global=128,
+                                      local_keep=16)
+    h = new_handle(dense)
+    rng = np.random.default_rng(41)
+    for it, cfg in enumerate([dense, sparse, dense, sparse]):
+        d = generate(cfg, 50 + it)
+        L = oracle.layout(d["topk_idx"], cfg.num_experts, cfg.block_m, cap=h.capacity_rows)
+        epoch = h.layout(*device_routing(d))
+        torch.cuda.synchronize()
+        rows = int((d["topk_idx"] >= 0).sum())
+        eo = bf16_from_f32(rng.standard_normal((h.capacity_rows, cfg.hidden), dtype=np.float32))
+        y = h.combine(epoch, to_dev_bf16(eo))
+        y_or = oracle.combine(eo, L["slot_to_pool_row"], d["topk_weights"])
+        assert ulp_diff(bits_of(y), y_or).max(initial=0) <= 1
+        gx = h.dispatch_backward(epoch, to_dev_bf16(eo))
+        assert np.array_equal(bits_of(gx), oracle.dispatch_backward(eo, L["slot_to_pool_row"],
+                                                                      cfg.tokens, cfg.top_k))
+        say(f"  layout {it}: {rows / cfg.tokens:.2f} rows per token, combine and dispatch backward match")
+    assert h.sync_status() == 0
+    h.close()
