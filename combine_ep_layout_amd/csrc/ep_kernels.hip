@@ -224,6 +224,17 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_count(LayoutArgs a) {
         a.ws[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
+// The layout's routing density for the next combine's launch shape: 4 or more
+// real rows per token on average is dense.  The word lives in pinned host
+// memory; the store is issued as early as the total is known, so that its
+// trip to the host overlaps the rest of the kernel.
+__device__ __forceinline__ void report_density(const LayoutArgs& a, int rows) {
+    if (!a.density) return;
+    const int64_t T = a.S / a.K;
+    __hip_atomic_store(a.density, (int64_t)rows >= 4 * T ? (int32_t)kDensityDense : (int32_t)kDensitySparse,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // Layout ranks.  FUSED: the whole layout in this one workgroup (nb == 1, no
 // histogram launch).  Otherwise launch 2 of the multi-workgroup layout: the
 // workgroup sums the histograms of the workgroups before it and of all of
@@ -232,6 +243,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_count(LayoutArgs a) {
 template <bool FUSED>
 __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, int nb, int lg_tpe) {
     extern __shared__ int smem[];
+    __shared__ int s_rows;                              // real rows (density report)
     const int E = a.E, BM = a.BM;
     int* s_base = smem;                                 // [E]   first row of e for this workgroup
     int* s_cnt = s_base + E;                            // [E]   rows of expert e
@@ -243,6 +255,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
     const int b = (int)blockIdx.x;
     const int nbits = key_bits(E);
     const int base = b * kLayoutSlotsPerBlock + w * kWaveSlots;
+    if (tid == 0) s_rows = 0;                           // ordered before the adds by the barriers below
 
     int key[kSlotsPerLane];
     bool bad = false;
@@ -289,11 +302,18 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
             s_off[e] = off;
             s_base[e] = off * BM + pre;
         }
+        if (b == 0) {                                   // all real rows, for the density report
+            int v = owner ? tot : 0;
+            for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
+            if (lane == 0 && v) atomicAdd(&s_rows, v);
+        }
     }
     __syncthreads();
+    if (!FUSED && b == 0 && tid == 0) report_density(a, s_rows);
 
     // per-wave counts; each iteration's match mask is kept for the ranking pass
     uint64_t m[kSlotsPerLane];
+    int nvalid = 0;
 #pragma unroll
     for (int i = 0; i < kSlotsPerLane; ++i) {
         m[i] = 0;
@@ -301,7 +321,9 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
         m[i] = match_any(key[i], nbits);
         if (key[i] < E && lane == __ffsll((unsigned long long)m[i]) - 1)
             wc[w * E + key[i]] += (uint16_t)__popcll(m[i]);
+        if constexpr (FUSED) nvalid += __popcll(__ballot(key[i] < E));
     }
+    if (FUSED && lane == 0 && nvalid) atomicAdd(&s_rows, nvalid);
     // The handle's copy of the weights (this wave's slots, as the keys).  On
     // gfx9 a wait for a load also waits for every store issued before it, so
     // global stores are kept after the last global load is consumed.
@@ -311,6 +333,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
         if (s < a.S) a.weights[s] = wv[j];
     }
     __syncthreads();
+    if (FUSED && tid == 0) report_density(a, s_rows);
 
     // exclusive prefix of the per-wave counts over waves; the last running sum
     // is the expert's count in this workgroup (E <= kLayoutThreads)
@@ -411,26 +434,11 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
     for (int t = tb0 + tid; t < tb1; t += kLayoutThreads) a.y_done[t] = 0u;
     // counts, first tiles and the tile total (workgroup 0)
     if (b == 0) {
-        int rows = 0;
         for (int e = tid; e <= E; e += kLayoutThreads) {
-            if (e < E) {
-                a.counts[e] = s_cnt[e];
-                rows += s_cnt[e];
-            }
+            if (e < E) a.counts[e] = s_cnt[e];
             a.offsets[e] = s_off[e];
         }
         if (tid == 0) *a.num_tiles = s_off[E];
-        // the layout's density for the next combine's launch shape: real rows
-        // summed over the experts (s_tmp is free once the scans are done)
-        for (int d = kWave / 2; d > 0; d >>= 1) rows += __shfl_xor(rows, d, kWave);
-        if (lane == 0) s_tmp[w] = rows;
-        __syncthreads();
-        if (tid == 0 && a.density) {
-            int total_rows = 0;
-            for (int i = 0; i < kLayoutWaves; ++i) total_rows += s_tmp[i];
-            __hip_atomic_store(a.density, (int64_t)total_rows >= 4 * (int64_t)T ? kDensityDense : kDensitySparse,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        }
     }
 }
 
