@@ -1057,7 +1057,9 @@ static_assert(EP_GATE_TOKENS >= 1 && EP_GATE_TOKENS <= 64, "one wave lane per ga
 // issued before it, so a wave that owns several items computes D of them
 // before issuing their stores: one store drain per D items, not per item.
 // With few rows per token (a latency-bound batch) holding stores back was
-// measured slower, so those batches use D = 1.
+// measured slower, so those batches use D = 1, and read a token's slots in
+// one batch through the scalar unit, which measured faster there (and slower
+// for dense batches, as in the plain combine at full occupancy).
 template <int KT, int D>
 __device__ __forceinline__ void gated_items(const CombineArgs& a, int nseg, int gtok, uint64_t mask,
                                             int w, int nw, int lane) {
@@ -1077,7 +1079,7 @@ __device__ __forceinline__ void gated_items(const CombineArgs& a, int nseg, int 
             if (i < nit && token_of(j) < a.T && ((mask >> j) & 1ull)) {
                 tt[d] = token_of(j);
                 sg[d] = i - j * nseg;
-                combine_compute<KT, false, false>(a, tt[d], sg[d], lane, o[d]);
+                combine_compute<KT, false, D == 1>(a, tt[d], sg[d], lane, o[d]);
             }
         }
 #pragma unroll
