@@ -217,7 +217,13 @@ ep_status ep_dispatch(ep_handle* h, const void* x, int32_t hidden, void* pool,
  *   expert_out  device bf16 [capacity_rows, hidden]; only real rows are read.
  *   y           device bf16 [num_tokens, hidden], fully written.
  * y[t,c] = bf16_rne( fp32 fma chain over k ascending of w[t,k] * o[row(t,k),c] )
- * starting from +0 and skipping masked slots; a token with no slot gets +0. */
+ * starting from +0 and skipping masked slots; a token with no slot gets +0.
+ * Launch shape: ep_layout reports whether its routing averages 4 or more real
+ * rows per token into a word of pinned host memory that the handle owns; this
+ * call (and ep_dispatch_backward) reads the word when it launches and runs
+ * fewer waves per compute unit for dense routing.  The word holds the latest
+ * layout whose kernel has finished, normally the current one; y is the same in
+ * every shape, only the timing depends on it. */
 ep_status ep_combine(const ep_handle* h, uint32_t epoch, const void* expert_out,
                      int32_t hidden, void* y, hipStream_t stream);
 
