@@ -374,6 +374,7 @@ ep_status ep_combine_gated(const ep_handle* h, uint32_t epoch, const void* exper
     a.limit_ticks = (uint64_t)spin_limit_us * (uint64_t)h->wall_khz / 1000u;
     a.error = h->error;
     a.num_cu = h->num_cu;
+    a.density = __atomic_load_n(h->density_host, __ATOMIC_RELAXED);   // launch shape, as ep_combine
     return hip_status(epk::launch_combine_gated(a, stream));
 }
 

@@ -1559,9 +1559,17 @@ hipError_t combine_kt(const CombineArgs& a, hipStream_t st) {
     const int per_seg = kWave * EP_COMBINE_UNROLL * 8;
     const int nseg = (a.H + per_seg - 1) / per_seg;
     if constexpr (GATE) {
-        // fewer tokens per workgroup when the batch would not give every
-        // compute unit two workgroups; no more waves than the batch has items
+        // Tokens per workgroup.  Dense routing (or density not reported yet):
+        // halved until every wave has at most EP_GATE_DEFER items, so that
+        // each wave issues its stores in one batch (prefill's 7 segments per
+        // token: 16 -> 8 tokens, 371 -> 355 us; at 4 segments 16 tokens
+        // already fit, and halving only adds polls and acquires).  Sparse
+        // batches keep 16 (fewer measured slower).  Then fewer when the batch
+        // would not give every compute unit two workgroups; no more waves
+        // than the batch has items.
         int gtok = EP_GATE_TOKENS;
+        if (a.density != kDensitySparse)
+            while (gtok > 1 && gtok * nseg > EP_GATE_WAVES * EP_GATE_DEFER) gtok >>= 1;
         while (gtok > 1 && (a.T + gtok - 1) / gtok < 2 * a.num_cu) gtok >>= 1;
         const int gw = gtok * nseg < EP_GATE_WAVES ? gtok * nseg : EP_GATE_WAVES;
         const int grid = (a.T + gtok - 1) / gtok;
