@@ -521,12 +521,25 @@ __device__ __forceinline__ void store_pool(u32x4* row, int row_bytes, int c, con
     store_row<STREAM ? EP_STREAM_STORE : EP_DISPATCH_STORE>(row, row_bytes, c, v);
 }
 
+// Slot groups.  A kernel holds the pool rows (and weights) of at most KT <= 8
+// slots of a token in registers.  With MANY (top_k above 8) it walks the
+// token's slots in groups of KT, in ascending slot order, so the registers a
+// wave needs do not grow with top_k and the fp32 sums keep their slot order.
+constexpr int kSlotGroup = 8;
+
+template <bool MANY, int KT>
+__device__ __forceinline__ int slot_groups(int K) {
+    return MANY ? (K + KT - 1) / KT : 1;
+}
+
+// Pool rows of slots k0 .. k0+KT-1 of token t (-1 past top_k); true when one
+// of them is a real row.
 template <int KT>
-__device__ __forceinline__ bool load_rows(const int32_t* s2r, int t, int K, int (&rows)[KT]) {
+__device__ __forceinline__ bool load_rows(const int32_t* s2r, int t, int K, int k0, int (&rows)[KT]) {
     bool any = false;
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
-        rows[k] = (k < K) ? s2r[t * K + k] : -1;
+        rows[k] = (k0 + k < K) ? s2r[t * K + k0 + k] : -1;
         any |= rows[k] >= 0;
     }
     return any;
@@ -534,8 +547,10 @@ __device__ __forceinline__ bool load_rows(const int32_t* s2r, int t, int K, int 
 
 // Work items are (token, segment) pairs, item = t * nseg + seg, handed out in
 // order: workgroup b owns items [b * ipb, (b+1) * ipb) and its waves take them
-// round-robin.  In streaming mode ipb is a whole number of tokens.
-template <int KT, bool STREAM>
+// round-robin.  In streaming mode ipb is a whole number of tokens.  With MANY
+// an item's first slot group is loaded ahead and the later groups' rows are
+// read as they are stored (an item is never skipped).
+template <int KT, bool STREAM, bool MANY>
 __global__ __launch_bounds__(1024) void k_dispatch_bf16(DispatchArgs a, int nseg, int ipb) {
     extern __shared__ int smem[];
     constexpr int U = EP_DISPATCH_UNROLL;
@@ -556,7 +571,7 @@ __global__ __launch_bounds__(1024) void k_dispatch_bf16(DispatchArgs a, int nseg
     auto fetch = [&](int it_, int (&r)[KT], u32x4 (&v_)[U]) -> bool {
         const int t_ = it_ / nseg;
         const int seg_ = it_ - t_ * nseg;
-        if (!load_rows<KT>(a.slot_to_row, t_, a.K, r)) return false;
+        if (!load_rows<KT>(a.slot_to_row, t_, a.K, 0, r) && !MANY) return false;
         const int c0_ = seg_ * (kWave * U) + lane;
         const u32x4* src_ = x + (int64_t)t_ * n16;
 #pragma unroll
@@ -582,14 +597,18 @@ __global__ __launch_bounds__(1024) void k_dispatch_bf16(DispatchArgs a, int nseg
         any_n = (it + nw < i1) && fetch(it + nw, rows_n, v_n);
         if (!any) continue;
         const int c0 = seg * (kWave * U) + lane;
+        const int ngroups = slot_groups<MANY, KT>(a.K);
+        for (int g = 0; g < ngroups; ++g) {
+            if (MANY && g > 0) load_rows<KT>(a.slot_to_row, t, a.K, g * KT, rows);
 #pragma unroll
-        for (int k = 0; k < KT; ++k) {
-            if (rows[k] < 0) continue;
-            u32x4* dst = pool + (int64_t)rows[k] * n16;
+            for (int k = 0; k < KT; ++k) {
+                if (rows[k] < 0) continue;
+                u32x4* dst = pool + (int64_t)rows[k] * n16;
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int c = c0 + u * kWave;
-                if (c < n16) store_pool<STREAM>(dst, a.H * 2, c, v[u]);
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + u * kWave;
+                    if (c < n16) store_pool<STREAM>(dst, a.H * 2, c, v[u]);
+                }
             }
         }
     }
@@ -772,7 +791,7 @@ __device__ __forceinline__ void store_scales(const DispatchArgs& a, const int (&
 // F32Q: float32 scale amax / 448 and codes of x * (448 / amax); otherwise the
 // UE8M0 exponent (stored as a byte, or as the float 2^e).  U: 16-channel
 // units per lane per work item.
-template <int KT, bool STREAM, bool F32Q, int U>
+template <int KT, bool STREAM, bool F32Q, int U, bool MANY>
 __global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg, int ipb) {
     extern __shared__ int smem[];
     const int lane = threadIdx.x & (kWave - 1);
@@ -801,7 +820,7 @@ __global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg,
     auto fetch = [&](int it_, int (&r)[KT], u32x4 (&l)[U], u32x4 (&h)[U]) -> bool {
         const int t_ = it_ / nseg;
         const int seg_ = it_ - t_ * nseg;
-        if (!load_rows<KT>(a.slot_to_row, t_, a.K, r)) return false;
+        if (!load_rows<KT>(a.slot_to_row, t_, a.K, 0, r) && !MANY) return false;
         const int u0_ = seg_ * (kWave * U) + lane;
         const u32x4* src_ = x + (int64_t)t_ * (a.H / 8);
 #pragma unroll
@@ -904,14 +923,21 @@ __global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg,
                     }
                 }
             }
-            if (c < nunit) {
+            const int ngroups = slot_groups<MANY, KT>(a.K);
+            for (int g = 0; g < ngroups; ++g) {
+                int rg[KT];
 #pragma unroll
-                for (int k = 0; k < KT; ++k) {
-                    if (rows[k] < 0) continue;
-                    store_pool<STREAM>(pool + (int64_t)rows[k] * nunit, a.H, c, q);
+                for (int k = 0; k < KT; ++k) rg[k] = rows[k];
+                if (MANY && g > 0) load_rows<KT>(a.slot_to_row, t, a.K, g * KT, rg);
+                if (c < nunit) {
+#pragma unroll
+                    for (int k = 0; k < KT; ++k) {
+                        if (rg[k] < 0) continue;
+                        store_pool<STREAM>(pool + (int64_t)rg[k] * nunit, a.H, c, q);
+                    }
                 }
+                store_scales<KT, STREAM>(a, rg, c, nunit, ngrp, pack8, sbyte, sval);
             }
-            store_scales<KT, STREAM>(a, rows, c, nunit, ngrp, pack8, sbyte, sval);
         }
     }
     if constexpr (STREAM) release_chunk(a, i0 / nseg, i1 / nseg, smem, smem + a.E);
@@ -926,19 +952,19 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// A token's K slot values (pool rows, weights) for a wave that works on one
-// token: the address is the same in every lane and the arrays are read-only
-// while the kernel runs, so the reads go to the scalar unit, all issued before
-// the first use.  Slots k >= K get `fill`.
+// A token's slot values (pool rows, weights) k0 .. k0+KT-1 for a wave that
+// works on one token: the address is the same in every lane and the arrays
+// are read-only while the kernel runs, so the reads go to the scalar unit, all
+// issued before the first use.  Slots past top_k get `fill`.
 template <int KT, typename V>
-__device__ __forceinline__ void load_slots(const V* p, int t, int K, V fill, V (&out)[KT]) {
+__device__ __forceinline__ void load_slots(const V* p, int t, int K, int k0, V fill, V (&out)[KT]) {
     typedef __attribute__((address_space(4))) const V CV;
-    CV* q = (CV*)(p + (int64_t)t * K);
+    CV* q = (CV*)(p + (int64_t)t * K + k0);
 #pragma unroll
-    for (int k = 0; k < KT; ++k) out[k] = q[k < K ? k : 0];
+    for (int k = 0; k < KT; ++k) out[k] = q[k0 + k < K ? k : 0];
 #pragma unroll
     for (int k = 0; k < KT; ++k)
-        if (k >= K) out[k] = fill;
+        if (k0 + k >= K) out[k] = fill;
 }
 
 // One combine work item: segment `seg` of token t (a wave gathers the token's
@@ -947,65 +973,75 @@ __device__ __forceinline__ void load_slots(const V* p, int t, int K, V fill, V (
 // slot values are read in one batch through the scalar unit, so a wave issues
 // all its row loads at once (the plain combine; its launcher sets how many
 // waves run at a time).  Otherwise they are read as vector loads, one slot
-// after another (the gated combine).
-template <int KT, bool UNIT, bool SCALAR>
+// after another (the gated combine).  With MANY the slots are taken in groups
+// of KT, each group's rows loaded together, the accumulators carried over.
+template <int KT, bool UNIT, bool SCALAR, bool MANY>
 __device__ __forceinline__ int combine_compute(const CombineArgs& a, int t, int seg, int lane,
                                                u32x4 (&out)[EP_COMBINE_UNROLL]) {
     constexpr int U = EP_COMBINE_UNROLL;
     const int n16 = a.H / 8;
     const u32x4* eo = (const u32x4*)a.expert_out;
-    int rows[KT];
-    float wt[KT];
-    if constexpr (SCALAR) {
-        load_slots<KT>(a.slot_to_row, t, a.K, -1, rows);
-        if constexpr (UNIT) {
-#pragma unroll
-            for (int k = 0; k < KT; ++k) wt[k] = 1.0f;
-        } else {
-            load_slots<KT>(a.weights, t, a.K, 0.0f, wt);
-        }
-    } else {
-#pragma unroll
-        for (int k = 0; k < KT; ++k) {
-            rows[k] = (k < a.K) ? a.slot_to_row[t * a.K + k] : -1;
-            wt[k] = UNIT ? 1.0f : ((k < a.K) ? a.weights[t * a.K + k] : 0.0f);
-        }
-    }
     const int c0 = seg * (kWave * U) + lane;
-    u32x4 v[KT][U];
+    float acc[U][8];
 #pragma unroll
-    for (int k = 0; k < KT; ++k) {
-        if (rows[k] < 0) continue;
-        const u32x4* src = eo + (int64_t)rows[k] * n16;
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int c = c0 + u * kWave;
-            if (c < n16) v[k][u] = load_v<EP_COMBINE_NT_LOADS>(src + c);
+        for (int i = 0; i < 8; ++i) acc[u][i] = 0.0f;
+    int nrows = 0;
+    const int ngroups = slot_groups<MANY, KT>(a.K);
+    for (int g = 0; g < ngroups; ++g) {
+        const int k0 = g * KT;
+        int rows[KT];
+        float wt[KT];
+        if constexpr (SCALAR) {
+            load_slots<KT>(a.slot_to_row, t, a.K, k0, -1, rows);
+            if constexpr (UNIT) {
+#pragma unroll
+                for (int k = 0; k < KT; ++k) wt[k] = 1.0f;
+            } else {
+                load_slots<KT>(a.weights, t, a.K, k0, 0.0f, wt);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < KT; ++k) {
+                const bool in = k0 + k < a.K;
+                rows[k] = in ? a.slot_to_row[t * a.K + k0 + k] : -1;
+                wt[k] = UNIT ? 1.0f : (in ? a.weights[t * a.K + k0 + k] : 0.0f);
+            }
         }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        float acc[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+        u32x4 v[KT][U];
 #pragma unroll
         for (int k = 0; k < KT; ++k) {
             if (rows[k] < 0) continue;
+            const u32x4* src = eo + (int64_t)rows[k] * n16;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t p = v[k][u][i];
-                acc[2 * i] = __builtin_fmaf(wt[k], __uint_as_float(p << 16), acc[2 * i]);
-                acc[2 * i + 1] =
-                    __builtin_fmaf(wt[k], __uint_as_float(p & 0xFFFF0000u), acc[2 * i + 1]);
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + u * kWave;
+                if (c < n16) v[k][u] = load_v<EP_COMBINE_NT_LOADS>(src + c);
             }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            out[u][i] = f32_to_bf16_rne(acc[2 * i]) | (f32_to_bf16_rne(acc[2 * i + 1]) << 16);
-    }
-    int nrows = 0;
+        for (int u = 0; u < U; ++u) {
 #pragma unroll
-    for (int k = 0; k < KT; ++k) nrows += rows[k] >= 0 ? 1 : 0;
+            for (int k = 0; k < KT; ++k) {
+                if (rows[k] < 0) continue;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t p = v[k][u][i];
+                    acc[u][2 * i] = __builtin_fmaf(wt[k], __uint_as_float(p << 16), acc[u][2 * i]);
+                    acc[u][2 * i + 1] =
+                        __builtin_fmaf(wt[k], __uint_as_float(p & 0xFFFF0000u), acc[u][2 * i + 1]);
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < KT; ++k) nrows += rows[k] >= 0 ? 1 : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            out[u][i] = f32_to_bf16_rne(acc[u][2 * i]) | (f32_to_bf16_rne(acc[u][2 * i + 1]) << 16);
     return nrows;
 }
 
@@ -1023,7 +1059,7 @@ __device__ __forceinline__ void combine_store(const CombineArgs& a, int t, int s
     }
 }
 
-template <int KT, bool UNIT>
+template <int KT, bool UNIT, bool MANY>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a, int nseg, int ipb) {
     const int lane = threadIdx.x & (kWave - 1);
     const int w = uniform_i(threadIdx.x / kWave);
@@ -1033,7 +1069,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a, int nseg, int ip
         const int t = it / nseg;
         const int seg = it - t * nseg;
         u32x4 o[EP_COMBINE_UNROLL];
-        combine_compute<KT, UNIT, true>(a, t, seg, lane, o);
+        combine_compute<KT, UNIT, true, MANY>(a, t, seg, lane, o);
         combine_store(a, t, seg, lane, o);
     }
 }
@@ -1060,7 +1096,7 @@ static_assert(EP_GATE_TOKENS >= 1 && EP_GATE_TOKENS <= 64, "one wave lane per ga
 // measured slower, so those batches use D = 1, and read a token's slots in
 // one batch through the scalar unit, which measured faster there (and slower
 // for dense batches, as in the plain combine at full occupancy).
-template <int KT, int D>
+template <int KT, int D, bool MANY>
 __device__ __forceinline__ void gated_items(const CombineArgs& a, int nseg, int gtok, uint64_t mask,
                                             int w, int nw, int lane) {
     const int b = (int)blockIdx.x, nb = (int)gridDim.x;
@@ -1079,7 +1115,7 @@ __device__ __forceinline__ void gated_items(const CombineArgs& a, int nseg, int 
             if (i < nit && token_of(j) < a.T && ((mask >> j) & 1ull)) {
                 tt[d] = token_of(j);
                 sg[d] = i - j * nseg;
-                combine_compute<KT, false, D == 1>(a, tt[d], sg[d], lane, o[d]);
+                combine_compute<KT, false, D == 1, MANY>(a, tt[d], sg[d], lane, o[d]);
             }
         }
 #pragma unroll
@@ -1099,7 +1135,7 @@ __device__ __forceinline__ void gated_items(const CombineArgs& a, int nseg, int 
 // wait is bounded: past limit_ticks, or once another workgroup has timed out
 // (error bit 2), it gives up, sets bit 2, and the batch's tokens that were
 // not done are skipped (their y rows keep their contents).
-template <int KT>
+template <int KT, bool MANY>
 __global__ __launch_bounds__(64 * EP_GATE_WAVES) void k_combine_gated(CombineArgs a, int nseg, int gtok) {
     __shared__ uint64_t s_done;
     __shared__ int s_dense;
@@ -1117,11 +1153,12 @@ __global__ __launch_bounds__(64 * EP_GATE_WAVES) void k_combine_gated(CombineArg
         const bool mine = lane < gtok && t < a.T;
         uint32_t target = 0;
         if (mine) {
-            int r[KT];                                  // every load issued before the first use
+            for (int g = 0; g < slot_groups<MANY, KT>(a.K); ++g) {
+                int r[KT];                              // every load issued before the first use
+                load_rows<KT>(a.slot_to_row, t, a.K, g * KT, r);
 #pragma unroll
-            for (int k = 0; k < KT; ++k) r[k] = k < a.K ? a.slot_to_row[t * a.K + k] : -1;
-#pragma unroll
-            for (int k = 0; k < KT; ++k) target += r[k] >= 0 ? 1u : 0u;
+                for (int k = 0; k < KT; ++k) target += r[k] >= 0 ? 1u : 0u;
+            }
         }
         // rows and tokens of the batch: an average of 4 or more rows per token
         // takes the path that holds stores back
@@ -1159,8 +1196,8 @@ __global__ __launch_bounds__(64 * EP_GATE_WAVES) void k_combine_gated(CombineArg
     }
     __syncthreads();
     const uint64_t mask = s_done;
-    if (s_dense) gated_items<KT, EP_GATE_DEFER>(a, nseg, gtok, mask, w, nw, lane);
-    else gated_items<KT, 1>(a, nseg, gtok, mask, w, nw, lane);
+    if (s_dense) gated_items<KT, MANY ? 1 : EP_GATE_DEFER, MANY>(a, nseg, gtok, mask, w, nw, lane);
+    else gated_items<KT, 1, MANY>(a, nseg, gtok, mask, w, nw, lane);
 }
 
 // ----------------------------------------------------- combine backward ---
@@ -1169,12 +1206,13 @@ __global__ __launch_bounds__(64 * EP_GATE_WAVES) void k_combine_gated(CombineArg
 #define EP_BWD_UNROLL 2        // 16-byte chunks per lane in flight in combine backward
 #endif
 
-// Backward of the combine, one wave per token: grad_y[t] is read once; for
-// each unmasked slot the gradient row bf16(fp32(w * g)) is stored and the
-// exact bf16 x bf16 products are accumulated in double, per lane in ascending
-// chunk order and then across lanes by a fixed butterfly (lane 0's sum is
-// kept), then rounded once to float.
-template <int KT>
+// Backward of the combine, one wave per token: grad_y[t] is read once (once
+// per slot group with MANY); for each unmasked slot the gradient row
+// bf16(fp32(w * g)) is stored and the exact bf16 x bf16 products are
+// accumulated in double, per lane in ascending chunk order and then across
+// lanes by a fixed butterfly (lane 0's sum is kept), then rounded once to
+// float.
+template <int KT, bool MANY>
 __global__ __launch_bounds__(256) void k_combine_bwd(CombineBwdArgs a) {
     constexpr int U = EP_BWD_UNROLL;
     const int lane = threadIdx.x & (kWave - 1);
@@ -1182,59 +1220,64 @@ __global__ __launch_bounds__(256) void k_combine_bwd(CombineBwdArgs a) {
     const int t = (int)blockIdx.x * 4 + w;
     if (t >= a.T) return;
     const int n16 = a.H / 8;
-    int rows[KT];
-    float wt[KT];
-    double acc[KT];
-#pragma unroll
-    for (int k = 0; k < KT; ++k) {
-        rows[k] = (k < a.K) ? a.slot_to_row[t * a.K + k] : -1;
-        wt[k] = (k < a.K) ? a.weights[t * a.K + k] : 0.0f;
-        acc[k] = 0.0;
-    }
     const u32x4* gy = (const u32x4*)a.grad_y + (int64_t)t * n16;
     const u32x4* eo = (const u32x4*)a.expert_out;
     u32x4* geo = (u32x4*)a.grad_eo;
-    for (int c0 = lane; c0 < n16; c0 += kWave * U) {
-        u32x4 g[U];
+    const int ngroups = slot_groups<MANY, KT>(a.K);
+    for (int gi = 0; gi < ngroups; ++gi) {
+        const int k0 = gi * KT;
+        int rows[KT];
+        float wt[KT];
+        double acc[KT];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int c = c0 + u * kWave;
-            if (c < n16) g[u] = gy[c];
+        for (int k = 0; k < KT; ++k) {
+            const bool in = k0 + k < a.K;
+            rows[k] = in ? a.slot_to_row[t * a.K + k0 + k] : -1;
+            wt[k] = in ? a.weights[t * a.K + k0 + k] : 0.0f;
+            acc[k] = 0.0;
+        }
+        for (int c0 = lane; c0 < n16; c0 += kWave * U) {
+            u32x4 g[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + u * kWave;
+                if (c < n16) g[u] = gy[c];
+            }
+#pragma unroll
+            for (int k = 0; k < KT; ++k) {
+                if (rows[k] < 0) continue;
+                u32x4 o[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + u * kWave;
+                    if (c < n16) o[u] = load_v<EP_COMBINE_NT_LOADS>(eo + (int64_t)rows[k] * n16 + c);
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + u * kWave;
+                    if (c >= n16) continue;
+                    u32x4 q;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float g0 = __uint_as_float(g[u][i] << 16);
+                        const float g1 = __uint_as_float(g[u][i] & 0xFFFF0000u);
+                        const float o0 = __uint_as_float(o[u][i] << 16);
+                        const float o1 = __uint_as_float(o[u][i] & 0xFFFF0000u);
+                        q[i] = f32_to_bf16_rne(wt[k] * g0) | (f32_to_bf16_rne(wt[k] * g1) << 16);
+                        acc[k] = __builtin_fma((double)g0, (double)o0, acc[k]);
+                        acc[k] = __builtin_fma((double)g1, (double)o1, acc[k]);
+                    }
+                    store_row<EP_DISPATCH_STORE>(geo + (int64_t)rows[k] * n16, a.H * 2, c, q);
+                }
+            }
         }
 #pragma unroll
         for (int k = 0; k < KT; ++k) {
-            if (rows[k] < 0) continue;
-            u32x4 o[U];
+            double v = acc[k];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int c = c0 + u * kWave;
-                if (c < n16) o[u] = load_v<EP_COMBINE_NT_LOADS>(eo + (int64_t)rows[k] * n16 + c);
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int c = c0 + u * kWave;
-                if (c >= n16) continue;
-                u32x4 q;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float g0 = __uint_as_float(g[u][i] << 16);
-                    const float g1 = __uint_as_float(g[u][i] & 0xFFFF0000u);
-                    const float o0 = __uint_as_float(o[u][i] << 16);
-                    const float o1 = __uint_as_float(o[u][i] & 0xFFFF0000u);
-                    q[i] = f32_to_bf16_rne(wt[k] * g0) | (f32_to_bf16_rne(wt[k] * g1) << 16);
-                    acc[k] = __builtin_fma((double)g0, (double)o0, acc[k]);
-                    acc[k] = __builtin_fma((double)g1, (double)o1, acc[k]);
-                }
-                store_row<EP_DISPATCH_STORE>(geo + (int64_t)rows[k] * n16, a.H * 2, c, q);
-            }
+            for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
+            if (lane == 0 && k0 + k < a.K) a.grad_w[t * a.K + k0 + k] = rows[k] >= 0 ? (float)v : 0.0f;
         }
-    }
-#pragma unroll
-    for (int k = 0; k < KT; ++k) {
-        double v = acc[k];
-#pragma unroll
-        for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
-        if (lane == 0 && k < a.K) a.grad_w[t * a.K + k] = rows[k] >= 0 ? (float)v : 0.0f;
     }
 }
 
@@ -1523,7 +1566,7 @@ inline int items_per_block(int nseg, bool stream) {
     return stream ? EP_STREAM_TOKENS * nseg : 4 * EP_ITEMS_PER_WAVE;
 }
 
-template <int KT>
+template <int KT, bool MANY>
 hipError_t dispatch_kt(const DispatchArgs& a, bool fp8, bool stream, hipStream_t st) {
     constexpr int FU = EP_FP8_UNROLL, FS = EP_FP8_STREAM_UNROLL;
     const int fu = stream ? FS : FU;
@@ -1538,23 +1581,23 @@ hipError_t dispatch_kt(const DispatchArgs& a, bool fp8, bool stream, hipStream_t
     if (fp8) {
         const bool f32q = a.scale_kind == kScaleF32;
         if (stream && f32q)
-            hipLaunchKernelGGL((k_dispatch_fp8<KT, true, true, FS>), dim3(grid), block, lds, st, a, nseg, ipb);
+            hipLaunchKernelGGL((k_dispatch_fp8<KT, true, true, FS, MANY>), dim3(grid), block, lds, st, a, nseg, ipb);
         else if (stream)
-            hipLaunchKernelGGL((k_dispatch_fp8<KT, true, false, FS>), dim3(grid), block, lds, st, a, nseg, ipb);
+            hipLaunchKernelGGL((k_dispatch_fp8<KT, true, false, FS, MANY>), dim3(grid), block, lds, st, a, nseg, ipb);
         else if (f32q)
-            hipLaunchKernelGGL((k_dispatch_fp8<KT, false, true, FU>), dim3(grid), block, lds, st, a, nseg, ipb);
+            hipLaunchKernelGGL((k_dispatch_fp8<KT, false, true, FU, MANY>), dim3(grid), block, lds, st, a, nseg, ipb);
         else
-            hipLaunchKernelGGL((k_dispatch_fp8<KT, false, false, FU>), dim3(grid), block, lds, st, a, nseg, ipb);
+            hipLaunchKernelGGL((k_dispatch_fp8<KT, false, false, FU, MANY>), dim3(grid), block, lds, st, a, nseg, ipb);
     } else {
         if (stream)
-            hipLaunchKernelGGL((k_dispatch_bf16<KT, true>), dim3(grid), block, lds, st, a, nseg, ipb);
+            hipLaunchKernelGGL((k_dispatch_bf16<KT, true, MANY>), dim3(grid), block, lds, st, a, nseg, ipb);
         else
-            hipLaunchKernelGGL((k_dispatch_bf16<KT, false>), dim3(grid), block, lds, st, a, nseg, ipb);
+            hipLaunchKernelGGL((k_dispatch_bf16<KT, false, MANY>), dim3(grid), block, lds, st, a, nseg, ipb);
     }
     return hipGetLastError();
 }
 
-template <int KT, bool UNIT, bool GATE>
+template <int KT, bool UNIT, bool GATE, bool MANY>
 hipError_t combine_kt(const CombineArgs& a, hipStream_t st) {
     const int per_seg = kWave * EP_COMBINE_UNROLL * 8;
     const int nseg = (a.H + per_seg - 1) / per_seg;
@@ -1573,7 +1616,7 @@ hipError_t combine_kt(const CombineArgs& a, hipStream_t st) {
         while (gtok > 1 && (a.T + gtok - 1) / gtok < 2 * a.num_cu) gtok >>= 1;
         const int gw = gtok * nseg < EP_GATE_WAVES ? gtok * nseg : EP_GATE_WAVES;
         const int grid = (a.T + gtok - 1) / gtok;
-        hipLaunchKernelGGL((k_combine_gated<KT>), dim3(grid), dim3(64 * gw), 0, st, a, nseg, gtok);
+        hipLaunchKernelGGL((k_combine_gated<KT, MANY>), dim3(grid), dim3(64 * gw), 0, st, a, nseg, gtok);
         return hipGetLastError();
     }
     const int ipb = items_per_block(nseg, false);
@@ -1591,25 +1634,24 @@ hipError_t combine_kt(const CombineArgs& a, hipStream_t st) {
     // costs least.
     const bool resident = items <= (int64_t)a.num_cu * EP_COMBINE_RESIDENT_WAVES;
     const size_t lds = (resident || a.density == kDensitySparse) ? 0 : EP_COMBINE_DENSE_LDS;
-    hipLaunchKernelGGL((k_combine<KT, UNIT>), dim3(grid), dim3(256), lds, st, a, nseg, ipb);
+    hipLaunchKernelGGL((k_combine<KT, UNIT, MANY>), dim3(grid), dim3(256), lds, st, a, nseg, ipb);
     return hipGetLastError();
 }
 
 template <bool UNIT, bool GATE>
 hipError_t combine_any(const CombineArgs& a, hipStream_t stream) {
     if (a.T == 0) return hipSuccess;
-    if (a.K <= 1) return combine_kt<1, UNIT, GATE>(a, stream);
-    if (a.K <= 2) return combine_kt<2, UNIT, GATE>(a, stream);
-    if (a.K <= 4) return combine_kt<4, UNIT, GATE>(a, stream);
-    if (a.K <= 8) return combine_kt<8, UNIT, GATE>(a, stream);
-    if (a.K <= 16) return combine_kt<16, UNIT, GATE>(a, stream);
-    return combine_kt<32, UNIT, GATE>(a, stream);
+    if (a.K <= 1) return combine_kt<1, UNIT, GATE, false>(a, stream);
+    if (a.K <= 2) return combine_kt<2, UNIT, GATE, false>(a, stream);
+    if (a.K <= 4) return combine_kt<4, UNIT, GATE, false>(a, stream);
+    if (a.K <= kSlotGroup) return combine_kt<kSlotGroup, UNIT, GATE, false>(a, stream);
+    return combine_kt<kSlotGroup, UNIT, GATE, true>(a, stream);
 }
 
-template <int KT>
+template <int KT, bool MANY>
 hipError_t combine_bwd_kt(const CombineBwdArgs& a, hipStream_t st) {
     const int grid = (a.T + 3) / 4;
-    hipLaunchKernelGGL((k_combine_bwd<KT>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_combine_bwd<KT, MANY>), dim3(grid), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
@@ -1641,12 +1683,11 @@ hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
 
 hipError_t launch_dispatch(const DispatchArgs& a, bool fp8, bool tile_ready, hipStream_t stream) {
     if (a.T == 0) return hipSuccess;
-    if (a.K <= 1) return dispatch_kt<1>(a, fp8, tile_ready, stream);
-    if (a.K <= 2) return dispatch_kt<2>(a, fp8, tile_ready, stream);
-    if (a.K <= 4) return dispatch_kt<4>(a, fp8, tile_ready, stream);
-    if (a.K <= 8) return dispatch_kt<8>(a, fp8, tile_ready, stream);
-    if (a.K <= 16) return dispatch_kt<16>(a, fp8, tile_ready, stream);
-    return dispatch_kt<32>(a, fp8, tile_ready, stream);
+    if (a.K <= 1) return dispatch_kt<1, false>(a, fp8, tile_ready, stream);
+    if (a.K <= 2) return dispatch_kt<2, false>(a, fp8, tile_ready, stream);
+    if (a.K <= 4) return dispatch_kt<4, false>(a, fp8, tile_ready, stream);
+    if (a.K <= kSlotGroup) return dispatch_kt<kSlotGroup, false>(a, fp8, tile_ready, stream);
+    return dispatch_kt<kSlotGroup, true>(a, fp8, tile_ready, stream);
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
@@ -1663,12 +1704,11 @@ hipError_t launch_combine_unit(const CombineArgs& a, hipStream_t stream) {
 
 hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t stream) {
     if (a.T == 0) return hipSuccess;
-    if (a.K <= 1) return combine_bwd_kt<1>(a, stream);
-    if (a.K <= 2) return combine_bwd_kt<2>(a, stream);
-    if (a.K <= 4) return combine_bwd_kt<4>(a, stream);
-    if (a.K <= 8) return combine_bwd_kt<8>(a, stream);
-    if (a.K <= 16) return combine_bwd_kt<16>(a, stream);
-    return combine_bwd_kt<32>(a, stream);
+    if (a.K <= 1) return combine_bwd_kt<1, false>(a, stream);
+    if (a.K <= 2) return combine_bwd_kt<2, false>(a, stream);
+    if (a.K <= 4) return combine_bwd_kt<4, false>(a, stream);
+    if (a.K <= kSlotGroup) return combine_bwd_kt<kSlotGroup, false>(a, stream);
+    return combine_bwd_kt<kSlotGroup, true>(a, stream);
 }
 
 hipError_t launch_cast_back(const CastBackArgs& a, hipStream_t stream) {

@@ -367,16 +367,25 @@ def combine_gathered(rows: np.ndarray, valid: np.ndarray, weights: np.ndarray) -
 # ---------------------------------------------------------------- backward --
 
 def combine_backward(grad_y: np.ndarray, expert_out: np.ndarray, slot_to_row: np.ndarray,
-                     weights: np.ndarray, grad_eo_init: Optional[np.ndarray] = None):
-    """Returns (grad_expert_out [cap, H] bf16 bits, grad_weights [T, K] float32)."""
+                     weights: np.ndarray, grad_eo_init: Optional[np.ndarray] = None,
+                     grad_eo_out: Optional[np.ndarray] = None):
+    """Returns (grad_expert_out [cap, H] bf16 bits, grad_weights [T, K] float32).
+    With grad_eo_out (a C-contiguous uint16 [cap, H] array) the gradient rows
+    are written into it in place and it is returned; other rows keep its
+    contents."""
     gy = np.ascontiguousarray(grad_y, dtype=np.uint16)
     eo = np.ascontiguousarray(expert_out, dtype=np.uint16)
     w = np.ascontiguousarray(weights, dtype=np.float32)
     T, K = w.shape
     H = gy.shape[1]
     s2r = np.ascontiguousarray(slot_to_row, dtype=np.int32)
-    geo = (np.zeros_like(eo) if grad_eo_init is None
-           else np.array(grad_eo_init, dtype=np.uint16, copy=True, order="C"))
+    if grad_eo_out is not None:
+        assert grad_eo_out.dtype == np.uint16 and grad_eo_out.flags["C_CONTIGUOUS"]
+        assert grad_eo_out.shape == eo.shape
+        geo = grad_eo_out
+    else:
+        geo = (np.zeros_like(eo) if grad_eo_init is None
+               else np.array(grad_eo_init, dtype=np.uint16, copy=True, order="C"))
     gw = np.empty((T, K), np.float32)
     _load().eo_combine_backward(_p(gy), _p(eo), _p(s2r), _p(w), T, K, H, _p(geo), _p(gw))
     return geo, gw

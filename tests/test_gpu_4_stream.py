@@ -23,17 +23,6 @@ pytestmark = pytest.mark.gpu
 SPIN_US = 3_000_000
 
 
-def _expected_consumer_rows(d, L, fp8, rows):
-    recv = L["pool_recv_token"]
-    if fp8:
-        out = []
-        for r in rows:
-            q, s = oracle.quantize_row(d["x"][recv[r]])
-            out.append(oracle.dequant_rows(q[None, :], s[None, :])[0])
-        return np.stack(out)
-    return d["x"][recv[rows]]
-
-
 def _check_end_state(h, L, seq, rounds):
     nt = L["num_tiles"]
     cnt = h.array("pool_arrival_count").cpu().numpy().view(np.uint32)[:nt]
@@ -43,10 +32,41 @@ def _check_end_state(h, L, seq, rounds):
     assert (ready[:nt] == seq).all()
 
 
-def _run(name, tokens, fp8, replays=1, sample=None):
+def _check_rows(d, L, fp8, out, pool, scales, per_token):
+    """Every real row: the consumer's output against the oracle (a copy of x,
+    or the dequantised codes of its token), and the pool bytes and scales the
+    streaming dispatch left behind against the oracle's per-token
+    quantisation."""
+    recv = L["pool_recv_token"]
+    real = np.flatnonzero(recv >= 0)
+    step = 32768
+    for r0 in range(0, len(real), step):
+        rows = real[r0:r0 + step]
+        rt = torch.from_numpy(rows).to(dev())
+        toks = recv[rows]
+        if fp8:
+            q_tok, s_tok, deq_tok = per_token
+            assert np.array_equal(bits_of(out[rt]), deq_tok[toks]), r0
+            assert np.array_equal(pool[rt].cpu().numpy(), q_tok[toks]), r0
+            assert np.array_equal(scales[rt].cpu().numpy(), s_tok[toks]), r0
+        else:
+            assert np.array_equal(bits_of(out[rt]), d["x"][toks]), r0
+            assert np.array_equal(bits_of(pool[rt]), d["x"][toks]), r0
+
+
+def _run(name, tokens, fp8, replays=1, top_k=None):
     import combine_ep_layout_amd as ep
+    import oracle_par
     cfg, d = inputs(name, tokens)
+    if top_k is not None:                       # the same tokens, routed to top_k experts
+        cfg = cfg.replace(top_k=top_k)
+        from synth import generate
+        d = generate(cfg, 0)
     L = oracle.layout(d["topk_idx"], cfg.num_experts, cfg.block_m)
+    per_token = None
+    if fp8:
+        q_tok, s_tok = oracle_par.quantize_tokens(d["x"])
+        per_token = (q_tok, s_tok, oracle_par.dequant_tokens(q_tok, s_tok))
     h = new_handle(cfg)
     H = cfg.hidden
     sa = torch.cuda.current_stream()
@@ -68,11 +88,7 @@ def _run(name, tokens, fp8, replays=1, sample=None):
         sa.synchronize()
         assert h.sync_status() == ep.EP_OK, "a consumer wait timed out"
         _check_end_state(h, L, seq, rep)
-        real = np.flatnonzero(L["pool_recv_token"] >= 0)
-        if sample is not None:
-            real = np.sort(np.random.default_rng(rep).choice(real, size=sample, replace=False))
-        got = bits_of(out[torch.from_numpy(real).to(dev())])
-        assert np.array_equal(got, _expected_consumer_rows(d, L, fp8, real))
+        _check_rows(d, L, fp8, out, pool, scales, per_token)
     h.close()
 
 
@@ -88,8 +104,16 @@ def test_replays_without_reset():
 
 
 def test_stream_full_size():
-    say("[stream] full size, consumer on a second stream, sampled rows")
-    _run("stream", -1, True, sample=1024)
+    say("[stream] full size, consumer on a second stream, every row")
+    _run("stream", -1, True)
+
+
+@pytest.mark.parametrize("top_k,fp8", [(16, True), (32, True), (16, False), (32, False)])
+def test_streaming_dispatch_top_k_above_8(top_k, fp8):
+    """top_k 16 and 32: the dispatch walks a token's slots in groups of 8;
+    every pool row, scale row and consumer row against the oracle."""
+    say(f"[stream] top_k={top_k} fp8={fp8}, 700 tokens")
+    _run("stream", 700, fp8, top_k=top_k)
 
 
 def test_bf16_prefill_shape_streaming():

@@ -27,18 +27,23 @@ def _rows_and_grads(cfg, L, seed=3):
     return eo, gy, s2r, valid
 
 
-def _check_grad_w(got, want, gy, eo, s2r, valid):
+def _check_grad_w(got, want, gy, eo, s2r, valid, chunk=512):
     H = gy.shape[1]
     assert (got[~valid] == 0).all()
-    g64 = bf16_to_f32(gy).astype(np.float64)
-    ts, ks = np.nonzero(valid)
-    o64 = bf16_to_f32(eo[s2r[ts, ks]]).astype(np.float64)
-    absum = np.abs(g64[ts] * o64).sum(1)
-    w = want[ts, ks].astype(np.float64)
-    bound = np.spacing(np.abs(want[ts, ks])).astype(np.float64) + 2 * H * 2.0 ** -53 * absum
-    diff = np.abs(got[ts, ks].astype(np.float64) - w)
-    assert np.all(diff <= bound)
-    return int((diff > 0).sum())
+    differ = 0
+    for t0 in range(0, gy.shape[0], chunk):              # bounded host memory at full size
+        t1 = min(gy.shape[0], t0 + chunk)
+        ts, ks = np.nonzero(valid[t0:t1])
+        ts = ts + t0
+        g64 = bf16_to_f32(gy[ts]).astype(np.float64)
+        o64 = bf16_to_f32(eo[s2r[ts, ks]]).astype(np.float64)
+        absum = np.abs(g64 * o64).sum(1)
+        w = want[ts, ks].astype(np.float64)
+        bound = np.spacing(np.abs(want[ts, ks])).astype(np.float64) + 2 * H * 2.0 ** -53 * absum
+        diff = np.abs(got[ts, ks].astype(np.float64) - w)
+        assert np.all(diff <= bound), t0
+        differ += int((diff > 0).sum())
+    return differ
 
 
 @pytest.mark.parametrize("name,tokens", [("tiny", -1), ("decode", -1), ("share", -1),
@@ -76,36 +81,66 @@ def test_dispatch_backward_parity(name, tokens):
     h.close()
 
 
-def test_backward_full_size_sampled():
-    say("[backward] prefill full size, sampled tokens")
+def test_backward_full_size():
+    """The metric's workload at full size: every gradient row, every weight
+    gradient and every row of grad_x against the oracle."""
+    import oracle_par
+    say("[backward] prefill full size, every token")
     cfg, d = inputs("prefill")
     L = oracle.layout(d["topk_idx"], cfg.num_experts, cfg.block_m)
     T, K, H = cfg.tokens, cfg.top_k, cfg.hidden
     h = new_handle(cfg)
     epoch = h.layout(*device_routing(d))
+    cap = h.capacity_rows
     g = torch.Generator(device=dev())
     g.manual_seed(77)
-    eo = torch.randn(h.capacity_rows, H, generator=g, device=dev()).to(torch.bfloat16)
+    eo = torch.empty(cap, H, dtype=torch.bfloat16, device=dev())
+    for r0 in range(0, cap, 16384):
+        r1 = min(cap, r0 + 16384)
+        eo[r0:r1] = torch.randn(r1 - r0, H, generator=g, device=dev()).to(torch.bfloat16)
+    recv = torch.from_numpy(L["pool_recv_token"]).to(dev())
+    eo[recv < 0] = float("nan")                   # rows no slot owns are never read
     gy = torch.randn(T, H, generator=g, device=dev()).to(torch.bfloat16)
-    geo, gw = h.combine_backward(epoch, gy, eo)
+    geo = torch.full((cap, H), POISON_BF16 - 0x10000, dtype=torch.int16,
+                     device=dev()).view(torch.bfloat16)
+    _, gw = h.combine_backward(epoch, gy, eo, geo)
     gx = h.dispatch_backward(epoch, eo)
-    rng = np.random.default_rng(9)
-    toks = np.sort(rng.choice(T, size=256, replace=False))
+    eo_h, gy_h = bits_of(eo), bits_of(gy)
+    del eo
+    geo_or, gw_or = oracle_par.combine_backward(gy_h, eo_h, L["slot_to_pool_row"], d["topk_weights"],
+                                                np.full((cap, H), POISON_BF16, np.uint16))
+    assert np.array_equal(bits_of(geo), geo_or)           # rows bit-exact, the rest untouched
+    del geo, geo_or
     s2r = L["slot_to_pool_row"].reshape(T, K)
-    w = d["topk_weights"]
-    gy_h = bits_of(gy[torch.from_numpy(toks).to(dev())])
-    for i, t in enumerate(toks):
-        rows = s2r[t]
-        vr = rows[rows >= 0]
-        eo_rows = bits_of(eo[torch.from_numpy(vr.astype(np.int64)).to(dev())])
-        # single-token oracle calls on gathered rows
-        sub_s2r = np.where(rows >= 0, np.cumsum(rows >= 0) - 1, -1).astype(np.int32)
-        geo_or, gw_or = oracle.combine_backward(gy_h[i:i + 1], eo_rows, sub_s2r, w[t:t + 1])
-        assert np.array_equal(bits_of(geo[torch.from_numpy(vr.astype(np.int64)).to(dev())]), geo_or)
-        _check_grad_w(gw[t:t + 1].cpu().numpy(), gw_or, gy_h[i:i + 1], eo_rows,
-                      sub_s2r.reshape(1, K), (rows >= 0).reshape(1, K))
-        gx_or = oracle.dispatch_backward(eo_rows, sub_s2r, 1, K)
-        assert np.array_equal(bits_of(gx[t:t + 1]), gx_or)
+    n = _check_grad_w(gw.cpu().numpy(), gw_or, gy_h, eo_h, s2r, s2r >= 0)
+    say(f"  grad_w not bit-identical: {n} of {int((s2r >= 0).sum())}")
+    gx_or = oracle_par.dispatch_backward(eo_h, L["slot_to_pool_row"], T, K)
+    assert np.array_equal(bits_of(gx), gx_or)
+    h.close()
+
+
+@pytest.mark.parametrize("top_k", [16, 32])
+def test_backward_top_k_above_8(top_k):
+    """top_k 16 and 32: both backward kernels walk a token's slots in groups
+    of 8 (combine backward reads grad_y once per group)."""
+    say(f"[backward] top_k={top_k}")
+    cfg = CONFIGS["stream"].replace(tokens=600, hidden=1024, top_k=top_k, fp8=False,
+                                    tile_ready=False)
+    d = generate(cfg, 12)
+    L = oracle.layout(d["topk_idx"], cfg.num_experts, cfg.block_m)
+    eo, gy, s2r, valid = _rows_and_grads(cfg, L)
+    h = new_handle(cfg)
+    epoch = h.layout(*device_routing(d))
+    cap, H = h.capacity_rows, cfg.hidden
+    geo = torch.full((cap, H), POISON_BF16 - 0x10000, dtype=torch.int16, device=dev()).view(torch.bfloat16)
+    _, gw = h.combine_backward(epoch, to_dev_bf16(gy), to_dev_bf16(eo), geo)
+    geo_or, gw_or = oracle.combine_backward(gy, eo, L["slot_to_pool_row"], d["topk_weights"],
+                                            grad_eo_init=np.full((cap, H), POISON_BF16, np.uint16))
+    assert np.array_equal(bits_of(geo), geo_or)
+    _check_grad_w(gw.cpu().numpy(), gw_or, gy, eo, s2r, valid)
+    gx = h.dispatch_backward(epoch, to_dev_bf16(eo))
+    assert np.array_equal(bits_of(gx), oracle.dispatch_backward(eo, L["slot_to_pool_row"],
+                                                                 cfg.tokens, top_k))
     h.close()
 
 

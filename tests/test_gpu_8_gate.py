@@ -28,19 +28,20 @@ def _slots_per_token(L, T, K):
 def _expected_y(d, L, fp8):
     """Oracle combine of the producer's rows: copies of x (bf16) or the
     dequantised FP8 rows; padding rows are NaN and never read."""
+    import oracle_par
     recv = L["pool_recv_token"]
     H = d["x"].shape[1]
     eo = np.full((recv.size, H), 0x7FC0, np.uint16)
     real = np.flatnonzero(recv >= 0)
     if fp8:
-        q, s = oracle.dispatch_fp8(d["x"], recv)
-        eo[real] = oracle.dequant_rows(q[real], s[real])
+        q_tok, s_tok = oracle_par.quantize_tokens(d["x"])
+        eo[real] = oracle_par.dequant_tokens(q_tok, s_tok)[recv[real]]
     else:
         eo[real] = d["x"][recv[real]]
-    return oracle.combine(eo, L["slot_to_pool_row"], d["topk_weights"])
+    return oracle_par.combine(eo, L["slot_to_pool_row"], d["topk_weights"])
 
 
-def _pipeline(name, tokens, fp8, rounds=1, one_stream=False):
+def _pipeline(name, tokens, fp8, rounds=1, one_stream=False, top_k=None):
     """layout on A; then per round: dispatch (tile_ready) on A, the producer on
     B and the gated combine on C, enqueued in that order.  Streams may share a
     hardware queue, which runs their kernels one after another, so the
@@ -51,6 +52,10 @@ def _pipeline(name, tokens, fp8, rounds=1, one_stream=False):
     writing.  With one_stream everything runs in order on A."""
     import combine_ep_layout_amd as ep
     cfg, d = inputs(name, tokens)
+    if top_k is not None:                       # the same tokens, routed to top_k experts
+        from synth import generate
+        cfg = cfg.replace(top_k=top_k)
+        d = generate(cfg, 0)
     T, K, H = cfg.tokens, cfg.top_k, cfg.hidden
     L = oracle.layout(d["topk_idx"], cfg.num_experts, cfg.block_m)
     want = _expected_y(d, L, fp8)
@@ -100,6 +105,23 @@ def test_gate_concurrent_streams(name, tokens, fp8):
     being written."""
     say(f"[gate] concurrent: {name} tokens={tokens} fp8={fp8}")
     _pipeline(name, tokens, fp8)
+
+
+@pytest.mark.parametrize("name,fp8", [("prefill", False), ("stream", True)])
+def test_gate_full_size(name, fp8):
+    """The prefill and streaming workloads at full size, in order on one
+    stream: dense batches hold several items' stores, and every wave owns
+    several items.  Every element of y against the oracle."""
+    say(f"[gate] full size {name}, in order")
+    _pipeline(name, -1, fp8, one_stream=True)
+
+
+@pytest.mark.parametrize("top_k,one_stream", [(16, True), (32, True), (16, False), (32, False)])
+def test_gate_top_k_above_8(top_k, one_stream):
+    """top_k 16 and 32: the gated combine walks a token's slots in groups of
+    8, in order and with the producer and combine on their own streams."""
+    say(f"[gate] top_k={top_k} one_stream={one_stream}")
+    _pipeline("stream", 900, False, one_stream=one_stream, top_k=top_k)
 
 
 def test_gate_rounds_without_relayout():
@@ -181,4 +203,41 @@ def test_gate_small_shapes(T, H, K, E, BM):
     assert np.array_equal(bits_of(y), want)
     done = h.array("y_done_per_token").cpu().numpy().view(np.uint32)
     assert np.array_equal(done, _slots_per_token(L, T, K))
+    h.close()
+
+
+@pytest.mark.parametrize("sync", [True, False])
+def test_gate_after_dense_and_sparse_layouts(sync):
+    """The gated combine's batch shape follows the routing density the layout
+    reports (dense batches hold several items' stores); the results do not
+    depend on it.  One handle alternates a dense and a sparse routing of the
+    same size, with or without a synchronisation after each layout (without
+    it the density in force may still be the previous layout's), and every
+    gated combine is compared with the oracle."""
+    import combine_ep_layout_amd as ep
+    from synth import CONFIGS, generate
+    say(f"[gate] alternating dense / sparse layouts on one handle, sync={sync}")
+    dense = CONFIGS["stream"].replace(tokens=6000, hidden=1024, mask_frac=0.0, fp8=False,
+                                      tile_ready=False)
+    sparse = CONFIGS["share"].replace(tokens=6000, hidden=1024, num_experts=128, experts_global=128,
+                                      local_keep=16)
+    h = new_handle(dense)
+    H = dense.hidden
+    pool, _ = h.new_pool(H)
+    for it, cfg in enumerate([dense, sparse, dense, sparse]):
+        d = generate(cfg, 60 + it)
+        L = oracle.layout(d["topk_idx"], cfg.num_experts, cfg.block_m, cap=h.capacity_rows)
+        want = _expected_y(d, L, False)
+        epoch = h.layout(*device_routing(d))
+        if sync:
+            torch.cuda.synchronize()
+        eo = torch.zeros(h.capacity_rows, H, dtype=torch.bfloat16, device=dev())
+        seq = h.dispatch(to_dev_bf16(d["x"]), pool, tile_ready=True)
+        h.tile_consume(seq, pool, None, H, eo, workgroups=64, spin_limit_us=SPIN_US,
+                       signal_done=True)
+        y = h.combine_gated(epoch, eo, round=1, spin_limit_us=SPIN_US)
+        torch.cuda.synchronize()
+        assert h.sync_status() == ep.EP_OK
+        assert np.array_equal(bits_of(y), want), it
+        say(f"  layout {it}: {(d['topk_idx'] >= 0).sum() / cfg.tokens:.2f} rows per token, match")
     h.close()

@@ -37,7 +37,7 @@ def _scales_host(t, host_like):
     return a.view(np.uint32) if host_like.dtype == np.uint32 else a
 
 
-def _dispatch_check(cfg, d, kind, mn, tile_ready=False, sample=None):
+def _dispatch_check(cfg, d, kind, mn, tile_ready=False, per_token=None):
     """Dispatch on the GPU and compare pool bytes and scales with the oracle.
     Returns the handle, pool, scales and the oracle layout for further use."""
     H = cfg.hidden
@@ -52,7 +52,7 @@ def _dispatch_check(cfg, d, kind, mn, tile_ready=False, sample=None):
                scale_kind=kind, mn_major=mn)
     got_p = pool.cpu().numpy()
     got_s = _scales_host(scales, s_init)
-    if sample is None:
+    if per_token is None:
         op, osc = oracle.dispatch_fp8_scaled(d["x"], recv, kind, mn, ld=h.scale_ld,
                                              pool_init=np.full((cap, H), POISON_U8, np.uint8),
                                              scales_init=s_init)
@@ -62,28 +62,38 @@ def _dispatch_check(cfg, d, kind, mn, tile_ready=False, sample=None):
         else:
             assert np.array_equal(got_s, osc)
     else:
-        # full size: sampled real rows against the oracle's per-row quantisation,
-        # and every padding row untouched
+        # full size: every real row against the oracle's quantisation of its
+        # token (computed once per token), every padding row untouched
+        import oracle_par
         real = np.flatnonzero(recv >= 0)
-        pick = np.sort(np.random.default_rng(4).choice(real, size=sample, replace=False))
-        op, osc = oracle.dispatch_fp8_scaled(d["x"][recv[pick]], np.arange(pick.size, dtype=np.int32),
-                                             kind)
-        assert np.array_equal(got_p[pick], op)
+        q_tok, s_tok = per_token
         G = H // 128
-        if mn and kind == "ue8m0":
-            # picked columns of the packed words, read back as little-endian bytes
-            cols = np.ascontiguousarray(got_s[:, pick].T).astype("<u4")
-            rm = cols.view(np.uint8).reshape(pick.size, -1)[:, :G]
-        elif mn:
-            rm = got_s[:, pick].T
-        else:
-            rm = got_s[pick]
-        if kind == "ue8m0":
-            assert np.array_equal(rm, osc)
-        else:
-            assert np.array_equal(np.ascontiguousarray(rm).view(np.uint32), osc.view(np.uint32))
-        pad = recv < 0
+        step = 16384
+        for r0 in range(0, real.size, step):
+            rows = real[r0:r0 + step]
+            toks = recv[rows]
+            assert np.array_equal(got_p[rows], q_tok[toks]), r0
+            if mn and kind == "ue8m0":
+                # the rows' columns of the packed words, read back as little-endian bytes
+                cols = np.ascontiguousarray(got_s[:, rows].T).astype("<u4")
+                rm = cols.view(np.uint8).reshape(rows.size, -1)[:, :G]
+            elif mn:
+                rm = got_s[:, rows].T
+            else:
+                rm = got_s[rows]
+            if kind == "ue8m0":
+                assert np.array_equal(rm, s_tok[toks]), r0
+            else:
+                assert np.array_equal(np.ascontiguousarray(rm).view(np.uint32),
+                                      s_tok[toks].view(np.uint32)), r0
+        pad = np.flatnonzero(recv < 0)
         assert (got_p[pad] == POISON_U8).all()
+        if mn:
+            unused = np.ones(got_s.shape[1], bool)
+            unused[real] = False
+            assert np.array_equal(got_s[:, unused], s_init[:, unused])
+        else:
+            assert np.array_equal(got_s[pad], s_init[pad])
     return h, pool, scales, L
 
 
@@ -156,12 +166,17 @@ def test_streaming_consumer_every_flavour(kind, mn):
 
 
 @pytest.mark.parametrize("kind", KINDS)
-@pytest.mark.parametrize("mn", [False, True])
-def test_scaled_dispatch_full_size_sampled(kind, mn):
-    say(f"[fp8var] prefill full size kind={kind} mn={mn}, sampled rows")
+def test_scaled_dispatch_full_size(kind):
+    """The prefill workload at full size in each flavour and both scale
+    layouts: every pool row and scale against the oracle."""
+    import oracle_par
     cfg, d = inputs("prefill")
-    h, pool, scales, L = _dispatch_check(cfg, d, kind, mn, sample=512)
-    h.close()
+    per_token = oracle_par.quantize_tokens(d["x"], kind=kind)
+    for mn in (False, True):
+        say(f"[fp8var] prefill full size kind={kind} mn={mn}, every row")
+        h, pool, scales, L = _dispatch_check(cfg, d, kind, mn, per_token=per_token)
+        del pool, scales
+        h.close()
 
 
 def test_special_values_all_flavours():
