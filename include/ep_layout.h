@@ -28,11 +28,11 @@
  *          combine (y_done_per_token) lets combine start on a token as soon
  *          as that token's expert compute has drained.
  *   [BORROW] DeepEP PR #769, "Add opt-in borrowed receive storage for compact
- *          BF16 dispatch", Description: dispatch may skip the activation copy
- *          and hand an indexed consumer a view (slab, row indices) instead; the
- *          view is an exclusive lease that is released on the consumer
- *          streams, calls that would disturb it are rejected while it is held,
- *          and unsupported modes are rejected up front.
+ *          BF16 dispatch", Description: instead of copying activations,
+ *          dispatch may give an indexed consumer a view made of a slab and row
+ *          indices; the view is held exclusively until the consumer streams
+ *          hand it back, calls that would change it fail meanwhile, and a mode
+ *          the borrow cannot serve fails before any work is queued.
  *
  * Conventions for every call:
  *   - Pointers marked "device" are device memory on the handle's GPU, 16-byte

@@ -1,9 +1,12 @@
-"""Borrowed receive view (DeepEP PR #769, Description): a borrowing dispatch
-copies nothing and lends x through the row map; an indexed consumer gathers
-rows from it; the view is an exclusive lease released on the consumer streams;
-unsupported modes are rejected up front.  Test patterns follow the PR's test
-description: bitwise payload and metadata against the gathered inputs,
-replay after release, delayed cross-stream readers, invalid-mode rejection."""
+"""Borrowed receive view (DeepEP PR #769, Description).  A borrowing
+dispatch writes no pool: x itself is the slab and the layout's
+pool_recv_token is the row map.  The tests gather rows through that map and
+compare them, and the metadata, with the oracle bit for bit; check that the
+handle refuses the calls that would disturb a lent view until it is handed
+back, and refuses modes a borrow cannot serve before enqueueing anything;
+reuse the handle once the view is returned; and keep a reader on another
+stream, held back behind other work, reading the old map while a new layout
+waits for it."""
 import numpy as np
 import pytest
 import torch
