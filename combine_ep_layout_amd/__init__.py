@@ -67,6 +67,7 @@ EXPORTS = [
     "ep_array_bytes", "ep_copy_array", "ep_counts_to_host", "ep_handle_sync_status",
     "ep_tile_consume", "ep_status_string", "ep_borrow_release", "ep_combine_backward",
     "ep_dispatch_backward", "ep_combine_gated", "ep_fp8_cast_back", "ep_scale_ld",
+    "ep_layout_noalloc",
 ]
 
 
@@ -110,6 +111,7 @@ def _load() -> ctypes.CDLL:
         "ep_combine_gated": (st, [P, U32, P, I32, P, U32, U32, P]),
         "ep_fp8_cast_back": (st, [P, P, U32, I64, I64, I32, P, P]),
         "ep_scale_ld": (I64, [P]),
+        "ep_layout_noalloc": (st, [P, I32, I32, I32, I32, I64, P, P, P, P, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

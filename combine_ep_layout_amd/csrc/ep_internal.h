@@ -19,6 +19,9 @@ namespace epk {
 // Up to this many slots the whole layout runs in a single workgroup and launch.
 constexpr int kLayoutSlotsPerBlock = 1024 * EP_LAYOUT_SLOTS_PER_LANE;
 
+// Layout arguments.  topk_w / weights, arrival / tile_ready, y_done, error
+// and density may be null (a layout into caller-owned arrays has none of
+// them); the other arrays are required.
 struct LayoutArgs {
     const int32_t* topk_idx;    // [S]
     const float* topk_w;        // [S]

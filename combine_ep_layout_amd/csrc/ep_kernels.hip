@@ -218,7 +218,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_count(LayoutArgs a) {
         if (key[i] < E && lane == __ffsll((unsigned long long)m) - 1)
             atomicAdd(&hist[key[i]], __popcll(m));
     }
-    if (__ballot(bad) && lane == 0) atomicOr(a.error, 1u);
+    if (a.error && __ballot(bad) && lane == 0) atomicOr(a.error, 1u);
     __syncthreads();
     for (int e = tid; e < E; e += kLayoutThreads)
         a.ws[(int64_t)blockIdx.x * E + e] = hist[e];
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
 #pragma unroll
     for (int j = 0; j < kSlotsPerLane; ++j) {
         const int s = base + j * kWave + lane;
-        wv[j] = (s < a.S) ? a.topk_w[s] : 0.0f;
+        wv[j] = (s < a.S && a.topk_w) ? a.topk_w[s] : 0.0f;
     }
     for (int i = tid; i < kLayoutWaves * E; i += kLayoutThreads) wc[i] = 0;
 
@@ -330,7 +330,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
 #pragma unroll
     for (int j = 0; j < kSlotsPerLane; ++j) {
         const int s = base + j * kWave + lane;
-        if (s < a.S) a.weights[s] = wv[j];
+        if (s < a.S && a.weights) a.weights[s] = wv[j];
     }
     __syncthreads();
     if (FUSED && tid == 0) report_density(a, s_rows);
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
         }
     }
     if constexpr (FUSED) {
-        if (__ballot(bad) && lane == 0) atomicOr(a.error, 1u);
+        if (a.error && __ballot(bad) && lane == 0) atomicOr(a.error, 1u);
         const int tiles = (tid < E) ? (run + BM - 1) / BM : 0;
         // with E <= 64 wave 0 holds every expert and scans without a barrier
         const int off = E <= kWave ? wave_exclusive_scan(tiles, total)
@@ -411,10 +411,12 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
             const int left = cnt - i * BM;
             a.tile_expert[j0 + i] = e;
             a.tile_target[j0 + i] = left < BM ? left : BM;
-            a.arrival[j0 + i] = 0u;
-            // not ready for any dispatch after this layout (whose sequence
-            // numbers come after seq_base), also when a graph replays both
-            a.tile_ready[j0 + i] = a.seq_base;
+            if (a.arrival) {
+                a.arrival[j0 + i] = 0u;
+                // not ready for any dispatch after this layout (whose sequence
+                // numbers come after seq_base), also when a graph replays both
+                a.tile_ready[j0 + i] = a.seq_base;
+            }
         }
         for (int r = j0 * BM + cnt + lane; r < (j0 + nt) * BM; r += kWave) a.recv_token[r] = -1;
     }
@@ -431,7 +433,8 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
     const int T = a.S / a.K;
     const int tb0 = (b * kLayoutSlotsPerBlock + a.K - 1) / a.K;
     const int tb1 = min(T, (s1 + a.K - 1) / a.K);
-    for (int t = tb0 + tid; t < tb1; t += kLayoutThreads) a.y_done[t] = 0u;
+    if (a.y_done)
+        for (int t = tb0 + tid; t < tb1; t += kLayoutThreads) a.y_done[t] = 0u;
     // counts, first tiles and the tile total (workgroup 0)
     if (b == 0) {
         for (int e = tid; e <= E; e += kLayoutThreads) {

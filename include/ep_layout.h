@@ -361,6 +361,38 @@ ep_status ep_tile_consume(const ep_handle* h, uint32_t seq, const void* pool,
                           void* out, int32_t workgroups, uint32_t spin_limit_us,
                           hipStream_t stream);
 
+/* ep_layout without a handle and without any allocation, for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops
+ * that forbid hipMalloc).  The routing metadata of ep_layout goes into arrays
+ * the caller owns; the workspace of the multi-workgroup layout (one int32 per
+ * workgroup of 2048 slots and expert) is a fixed 1 MiB device array of the
+ * library, one per GPU, held until the process ends.
+ *   topk_idx          device int32 [num_tokens, top_k]; -1 marks a masked slot.
+ *   num_tokens 0..2^19, top_k 1..32, num_experts 1..1024, block_m 1..4096.
+ *   capacity_rows     >= num_tokens*top_k + num_experts*(block_m-1), and
+ *                     below 2^30; max_tiles = capacity_rows / block_m.
+ *   outputs (device, caller-owned, 4-byte aligned), as ep_layout's arrays:
+ *     expert_counts [E], expert_pool_block_offset [E+1], num_tiles [1],
+ *     tile_expert [max_tiles], pool_arrival_target [max_tiles],
+ *     slot_to_pool_row [num_tokens*top_k], pool_recv_token [capacity_rows].
+ *   error_word        device uint32 or NULL: bit 0 is set (never cleared) when
+ *                     an id outside [-1, num_experts) was seen; such slots are
+ *                     treated as masked.
+ * Returns EP_ERR_UNSUPPORTED when the workspace would exceed the fixed array
+ * (ceil(num_tokens*top_k/2048) * num_experts > 262144 int32, e.g. more than
+ * 524288 slots at 1024 experts), EP_ERR_INVALID_ARGUMENT for bad sizes or
+ * pointers; nothing is enqueued then.  Calls that overlap on one GPU (on
+ * different streams, or from different threads) share the array and race;
+ * calls in stream order do not.  Nothing here touches a handle: no weights
+ * copy, arrival counts, tile_ready stamps or done counts. */
+ep_status ep_layout_noalloc(const int32_t* topk_idx, int32_t num_tokens, int32_t top_k,
+                            int32_t num_experts, int32_t block_m, int64_t capacity_rows,
+                            int32_t* expert_counts, int32_t* expert_pool_block_offset,
+                            int32_t* num_tiles, int32_t* tile_expert,
+                            int32_t* pool_arrival_target, int32_t* slot_to_pool_row,
+                            int32_t* pool_recv_token, uint32_t* error_word,
+                            hipStream_t stream);
+
 /* Static description of a status code. */
 const char* ep_status_string(ep_status s);
 

@@ -95,6 +95,16 @@ def test_new_entry_points_reject_before_any_hip_call():
                                 None) == INV                                              # float scales misaligned
     assert lib.ep_fp8_cast_back(0x1008, 0x2000, 0, 4, 0, 256, 0x3000, None) == INV       # codes not 16-byte aligned
     assert lib.ep_fp8_cast_back(None, None, 0, 0, 0, 1 << 17, None, None) == ep.EP_ERR_UNSUPPORTED
+    # the allocation-free layout checks sizes, capacity and output pointers first
+    nul = [None] * 7
+    assert lib.ep_layout_noalloc(None, -1, 2, 4, 8, 100, *nul, None, None) == INV
+    assert lib.ep_layout_noalloc(None, (1 << 19) + 1, 1, 4, 8, 1 << 22, *nul, None, None) == INV
+    assert lib.ep_layout_noalloc(None, 10, 33, 4, 8, 1000, *nul, None, None) == INV
+    assert lib.ep_layout_noalloc(None, 10, 2, 1025, 8, 10000, *nul, None, None) == INV
+    assert lib.ep_layout_noalloc(None, 10, 2, 4, 8, 47, *nul, None, None) == INV     # < 20 + 28
+    assert lib.ep_layout_noalloc(None, 10, 2, 4, 8, 48, *nul, None, None) == INV     # no outputs
+    big = (1 << 19) * 32 + 1024 * 127                                                # workspace too big
+    assert lib.ep_layout_noalloc(None, 1 << 19, 32, 1024, 128, big, *nul, None, None) == ep.EP_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("kind,mn,shape,dtype", [
