@@ -689,12 +689,22 @@ def main() -> int:
     cold_us = {k: pct(np.array([e[j].elapsed_time(e[j + 1]) for e in cold]) * 1e3)
                for j, k in enumerate(("layout", "dispatch", "combine"))}
 
-    # With the streaming release on, the same dispatch without it, for comparison.
+    # With the streaming release on, the same dispatch without it, for
+    # comparison, timed the same way: inside the layout -> dispatch -> combine
+    # step, with HIP events around each dispatch.
     no_ready = None
     if ready:
-        h.layout(idx, w)
-        no_ready = _time_us(lambda: h.dispatch(x, pool, scales, fp8=fp8, tile_ready=False),
-                            args.steps, args.warmup, stream)
+        st = {}
+
+        def before():
+            st["epoch"] = h.layout(idx, w)
+
+        def after():
+            h.combine(st["epoch"], eo, y)
+
+        no_ready = _time_in_step_us(before, lambda: h.dispatch(x, pool, scales, fp8=fp8,
+                                                               tile_ready=False),
+                                    after, args.steps, args.warmup, stream)
 
     counts, _ = h.counts_to_host()
     ab = algorithmic_bytes(cfg, d["topk_idx"], counts, fp8)

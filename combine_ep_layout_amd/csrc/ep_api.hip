@@ -316,9 +316,9 @@ ep_status ep_dispatch(ep_handle* h, const void* x, int32_t hidden, void* pool,
     a.scale_kind = scale_kind(flags);
     a.scale_mn = (flags & EP_SCALE_MN_MAJOR) ? 1 : 0;
     a.scale_ld = scale_ld_of(h->cap);
+    a.max_tiles = h->max_tiles;
     a.arrival = h->arrival;
     a.tile_ready = h->tile_ready;
-    a.stream_grid = h->num_cu * EP_STREAM_WG_PER_CU;
     a.seq = h->seq + 1;
     a.round = h->round + (ready ? 1u : 0u);
     ep_status st = hip_status(epk::launch_dispatch(a, fp8, ready, stream));

@@ -11,10 +11,6 @@ namespace epk {
 #define EP_LAYOUT_SLOTS_PER_LANE 2
 #endif
 
-#ifndef EP_STREAM_WG_PER_CU
-#define EP_STREAM_WG_PER_CU 1  // streaming dispatch: 1024-thread workgroups per compute unit
-#endif
-
 // Slots ranked by one layout workgroup (1024 threads x EP_LAYOUT_SLOTS_PER_LANE).
 // Up to this many slots the whole layout runs in a single workgroup and launch.
 constexpr int kLayoutSlotsPerBlock = 1024 * EP_LAYOUT_SLOTS_PER_LANE;
@@ -79,11 +75,11 @@ struct DispatchArgs {
     int32_t scale_mn;           // 1: MN-major [G, scale_ld] (UE8M0 packed 4 per word)
     int64_t scale_ld;
     // streaming release
+    int32_t max_tiles;
     uint32_t* arrival;
     uint32_t* tile_ready;
     uint32_t seq;
     uint32_t round;             // TILE_READY dispatches since the layout (1, 2, ...)
-    int32_t stream_grid;        // workgroups of a streaming dispatch (resident)
 };
 
 struct CombineArgs {

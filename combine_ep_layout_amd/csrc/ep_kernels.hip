@@ -18,11 +18,11 @@
 // writes the codes (FP8; instagit DeepEP low-latency page, "FP8 and
 // Quantization Support").  UE8M0 codes come from gfx950's scaled conversion
 // instruction wherever it equals the exact integer encoder, which is kept for
-// the rest.  With the streaming release, resident workgroups take chunks of
-// whole tokens in global order, make each chunk's rows visible at device
-// scope and then raise the arrival count of every tile it wrote; the
-// workgroup that completes a tile release-stores the sequence number into
-// tile_ready[tile].
+// the rest.  With the streaming release, each workgroup takes a chunk of two
+// tokens in token order, stores its rows with device-scope stores, and the
+// last of its waves to see its own stores complete raises the arrival count
+// of every tile the chunk wrote; the add that completes a tile stores the
+// sequence number into tile_ready[tile].
 //
 // Combine is token-major too: a wave gathers one segment of the token's k
 // expert rows, accumulates w * o in fp32 with one fused multiply-add per slot
@@ -61,10 +61,10 @@
 #define EP_ITEMS_PER_WAVE 1    // work items per wave outside streaming mode
 #endif
 #ifndef EP_STREAM_TOKENS
-#define EP_STREAM_TOKENS 64    // tokens per released chunk in streaming mode
+#define EP_STREAM_TOKENS 2     // tokens per released chunk (one workgroup) in streaming mode
 #endif
 #ifndef EP_STREAM_THREADS
-#define EP_STREAM_THREADS 1024 // threads per streaming workgroup
+#define EP_STREAM_THREADS 256  // threads per streaming workgroup
 #endif
 #ifndef EP_DISPATCH_STORE
 #define EP_DISPATCH_STORE 4    // pool stores outside streaming: see store_row
@@ -447,53 +447,43 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
 
 // ------------------------------------------------------------- dispatch ---
 
-// Streaming release of the rows a workgroup has just stored for the tokens
-// [t0, t1) of one chunk.  Every wave waits until its own stores have reached
-// the cache and the workgroup meets at a barrier (which also means wave 0 has
-// finished the previous chunk's adds); the per-expert row ranges of the chunk
-// are gathered in LDS; then wave 0 alone publishes them at device scope with a
-// single release fence and makes the arrival adds while the other waves go on
-// with the next chunk.  Rows of one expert written for a contiguous token range
-// are contiguous, so it adds once per (expert, tile) touched.  The add that
-// brings a tile to its target acquires the other workgroups' releases and
-// release-stores the sequence number into tile_ready[tile]; a consumer that
-// acquire-loads tile_ready then sees every row of the tile.
-__device__ void release_chunk(const DispatchArgs& a, int t0, int t1, int* s_lo, int* s_hi) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    const int tid = threadIdx.x;
-    for (int e = tid; e < a.E; e += blockDim.x) {
-        s_lo[e] = INT_MAX;
-        s_hi[e] = -1;
-    }
-    __syncthreads();
+// Streaming release of one chunk (a few consecutive tokens, one workgroup),
+// without a workgroup barrier or a cache write-back.  All of a streaming
+// dispatch's stores (pool rows and scales) are device-scope stores, which the
+// XCD's L2 writes through, so a store counts as complete (vmcnt) only once it
+// is visible to every XCD.  Each wave waits for its own stores, then counts
+// itself done in LDS; the wave that completes the count has seen every other
+// wave's stores complete and makes the chunk's arrival adds.  It groups the
+// chunk's rows by tile with wave match masks (64 slots at a time), so a tile
+// gets one add per chunk.  The add that brings a tile to round * target
+// stores the sequence number into tile_ready[tile]; a consumer that
+// acquire-loads it (which invalidates its own caches) then reads every row of
+// the tile from the coherent level.
+__device__ void release_chunk(const DispatchArgs& a, int t0, int t1, uint32_t* s_done) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t nw = blockDim.x / kWave;
+    __builtin_amdgcn_s_waitcnt(0);                 // this wave's stores are complete
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);       // and no memory access moves across
+    uint32_t old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(s_done, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_WORKGROUP);
+    old = (uint32_t)__shfl((int)old, 0, kWave);
+    if (old != nw - 1u) return;                    // not the last wave of the chunk
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const int nbits = 32 - __clz(a.max_tiles);     // tile ids and the no-row key max_tiles
     const int s0 = t0 * a.K, s1 = t1 * a.K;
-    for (int s = s0 + tid; s < s1; s += blockDim.x) {
-        const int r = a.slot_to_row[s];
-        if (r >= 0) {
-            const int e = a.tile_expert[r / a.BM];
-            atomicMin(&s_lo[e], r);
-            atomicMax(&s_hi[e], r);
-        }
-    }
-    __syncthreads();
-    if (tid >= kWave) return;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    for (int e = tid; e < a.E; e += kWave) {
-        const int hi = s_hi[e];
-        if (hi < 0) continue;
-        const int lo = s_lo[e];
-        for (int j = lo / a.BM; j <= hi / a.BM; ++j) {
-            const int first = max(lo, j * a.BM);
-            const int last = min(hi, j * a.BM + a.BM - 1);
-            const uint32_t n = (uint32_t)(last - first + 1);
-            const uint32_t old = __hip_atomic_fetch_add(&a.arrival[j], n, __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_AGENT);
-            if (old + n == a.round * (uint32_t)a.tile_target[j]) {
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-                __hip_atomic_store(&a.tile_ready[j], a.seq, __ATOMIC_RELEASE,
+    for (int b = s0; b < s1; b += kWave) {
+        const int s = b + lane;
+        const int r = s < s1 ? a.slot_to_row[s] : -1;
+        const int tile = r >= 0 ? r / a.BM : a.max_tiles;
+        const uint64_t m = match_any(tile, nbits);
+        if (r >= 0 && lane == __ffsll((unsigned long long)m) - 1) {
+            const uint32_t cnt = (uint32_t)__popcll(m);
+            const uint32_t prev = __hip_atomic_fetch_add(&a.arrival[tile], cnt, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
+            if (prev + cnt == a.round * (uint32_t)a.tile_target[tile])
+                __hip_atomic_store(&a.tile_ready[tile], a.seq, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
-            }
         }
     }
 }
@@ -555,7 +545,6 @@ __device__ __forceinline__ bool load_rows(const int32_t* s2r, int t, int K, int 
 // read as they are stored (an item is never skipped).
 template <int KT, bool STREAM, bool MANY>
 __global__ __launch_bounds__(1024) void k_dispatch_bf16(DispatchArgs a, int nseg, int ipb) {
-    extern __shared__ int smem[];
     constexpr int U = EP_DISPATCH_UNROLL;
     const int lane = threadIdx.x & (kWave - 1);
     const int w = uniform_i(threadIdx.x / kWave);
@@ -563,12 +552,15 @@ __global__ __launch_bounds__(1024) void k_dispatch_bf16(DispatchArgs a, int nseg
     const u32x4* x = (const u32x4*)a.x;
     u32x4* pool = (u32x4*)a.pool;
     const int nw = (int)blockDim.x / kWave;
-    // streaming: chunks of EP_STREAM_TOKENS tokens in global order, strided
-    // over a resident grid, each released as soon as it is stored
-    const int nchunk = STREAM ? (a.T + EP_STREAM_TOKENS - 1) / EP_STREAM_TOKENS : 1;
-    for (int ch = STREAM ? (int)blockIdx.x : 0; ch < nchunk; ch += STREAM ? (int)gridDim.x : 1) {
-    const int i0 = STREAM ? ch * EP_STREAM_TOKENS * nseg : (int)blockIdx.x * ipb;
-    const int i1 = min(a.T * nseg, STREAM ? i0 + EP_STREAM_TOKENS * nseg : i0 + ipb);
+    // streaming: the workgroup's items are the tokens of one chunk, released
+    // as soon as they are stored; chunks follow token order
+    __shared__ uint32_t s_done;
+    if constexpr (STREAM) {
+        if (threadIdx.x == 0) s_done = 0u;
+        __syncthreads();
+    }
+    const int i0 = (int)blockIdx.x * ipb;
+    const int i1 = min(a.T * nseg, i0 + ipb);
     // software-pipelined as in the FP8 dispatch: the next item's rows and x
     // segment are loaded before the current one is stored
     auto fetch = [&](int it_, int (&r)[KT], u32x4 (&v_)[U]) -> bool {
@@ -615,8 +607,7 @@ __global__ __launch_bounds__(1024) void k_dispatch_bf16(DispatchArgs a, int nseg
             }
         }
     }
-    if constexpr (STREAM) release_chunk(a, i0 / nseg, i1 / nseg, smem, smem + a.E);
-    }
+    if constexpr (STREAM) release_chunk(a, i0 / nseg, i1 / nseg, &s_done);
 }
 
 // --- FP8 e4m3fn with UE8M0 scales, from bf16 bit patterns, integer only ---
@@ -776,7 +767,8 @@ __device__ __forceinline__ void store_scales(const DispatchArgs& a, const int (&
 #pragma unroll
             for (int k = 0; k < KT; ++k) {
                 if (rows[k] < 0) continue;
-                ((uint8_t*)a.scales)[(int64_t)rows[k] * ngrp + g] = (uint8_t)sbyte;
+                put_scale<STREAM>((uint8_t*)a.scales + (int64_t)rows[k] * ngrp + g,
+                                                       (uint8_t)sbyte);
             }
         }
     } else if (c < nunit && (lane & 7) == 0) {
@@ -796,18 +788,20 @@ __device__ __forceinline__ void store_scales(const DispatchArgs& a, const int (&
 // units per lane per work item.
 template <int KT, bool STREAM, bool F32Q, int U, bool MANY>
 __global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg, int ipb) {
-    extern __shared__ int smem[];
     const int lane = threadIdx.x & (kWave - 1);
     const int w = uniform_i(threadIdx.x / kWave);
     const int nunit = a.H / 16;          // 16 channels (32 bytes in, 16 bytes out) per unit
     const int ngrp = a.H / 128;
     // (the streaming release is faster with plain byte stores written back by its fence)
-    const bool pack8 = EP_FP8_PACK8 && !STREAM && (ngrp & 7) == 0 && ((uintptr_t)a.scales & 7) == 0;
+    const bool pack8 = EP_FP8_PACK8 && (ngrp & 7) == 0 && ((uintptr_t)a.scales & 7) == 0;
     const u32x4* x = (const u32x4*)a.x;
     u32x4* pool = (u32x4*)a.pool;
     const int nw = (int)blockDim.x / kWave;
-    const int nchunk = STREAM ? (a.T + EP_STREAM_TOKENS - 1) / EP_STREAM_TOKENS : 1;
-    for (int ch = STREAM ? (int)blockIdx.x : 0; ch < nchunk; ch += STREAM ? (int)gridDim.x : 1) {
+    __shared__ uint32_t s_done;                     // streaming: waves done with the chunk
+    if constexpr (STREAM) {
+        if (threadIdx.x == 0) s_done = 0u;
+        __syncthreads();
+    }
     // Float32 scales are 4-byte entries whose cache lines are shared by
     // consecutive pool rows of an expert, i.e. by consecutive tokens.  With
     // each XCD on a contiguous token range those lines are completed in one
@@ -816,8 +810,8 @@ __global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg,
     // and UE8M0 keep the round-robin, which measured slightly faster there).
     const int blk = a.scale_kind != kScaleUe8m0 ? xcd_contiguous_block((int)blockIdx.x, (int)gridDim.x)
                                                 : (int)blockIdx.x;
-    const int i0 = STREAM ? ch * EP_STREAM_TOKENS * nseg : blk * ipb;
-    const int i1 = min(a.T * nseg, STREAM ? i0 + EP_STREAM_TOKENS * nseg : i0 + ipb);
+    const int i0 = blk * ipb;
+    const int i1 = min(a.T * nseg, i0 + ipb);
     // a wave's items are software-pipelined: the next item's rows and x
     // segment are loaded before the current one is quantised and stored
     auto fetch = [&](int it_, int (&r)[KT], u32x4 (&l)[U], u32x4 (&h)[U]) -> bool {
@@ -943,8 +937,7 @@ __global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg,
             }
         }
     }
-    if constexpr (STREAM) release_chunk(a, i0 / nseg, i1 / nseg, smem, smem + a.E);
-    }
+    if constexpr (STREAM) release_chunk(a, i0 / nseg, i1 / nseg, &s_done);
 }
 
 // -------------------------------------------------------------- combine ---
@@ -1578,8 +1571,7 @@ hipError_t dispatch_kt(const DispatchArgs& a, bool fp8, bool stream, hipStream_t
     const int ipb = items_per_block(nseg, stream);
     const int64_t items = (int64_t)a.T * nseg;
     int grid = (int)((items + ipb - 1) / ipb);
-    if (stream && grid > a.stream_grid) grid = a.stream_grid;      // resident grid, chunks strided
-    const size_t lds = stream ? 2 * sizeof(int) * (size_t)a.E : 0;
+    const size_t lds = 0;
     const dim3 block(stream ? EP_STREAM_THREADS : 256);
     if (fp8) {
         const bool f32q = a.scale_kind == kScaleF32;
