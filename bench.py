@@ -9,7 +9,8 @@ resident in HBM when the timed region starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
                     [--no-cpu-baseline] [--copy-calibration]
-                    [--borrow-compare | --backward | --gate | --fp8-variants | --graph | --ceiling]
+                    [--borrow-compare | --backward | --gate | --fp8-variants | --graph | --ceiling
+                     | --overlap]
 
 Prints one JSON line.  "value" is algorithmic bytes moved per step / step
 time, over exactly K steps with nothing else on the stream.  Per-kernel times
@@ -511,6 +512,108 @@ def fp8_variants_bench(cfg, steps: int, warmup: int) -> dict:
             "results": rows}
 
 
+def overlap_bench(cfg, steps: int, warmup: int, workgroups: int = 256) -> dict:
+    """Streaming dispatch on one stream and the tile consumer stand-in on a
+    second stream, enqueued right after it (StreamEP README: a consumer spins
+    on tile_ready and starts while later tokens are still landing).  HIP
+    events give each kernel's interval; the consumer's acquire stamps (device
+    wall clock, and whether its first look found the tile not ready) show how
+    many tiles it took while the dispatch was still running, and the rank
+    correlation of their acquire times with the last token each tile holds
+    shows that tiles were released in token order.  The same two kernels run
+    back to back on one stream for comparison."""
+    import torch
+    import combine_ep_layout_amd as ep
+    from synth import generate
+    dev = torch.device("cuda", 0)
+    sa = torch.cuda.current_stream()
+    sb = torch.cuda.Stream()                                   # default priority
+    d = generate(cfg, 0)
+    T, K, H = cfg.tokens, cfg.top_k, cfg.hidden
+    fp8 = cfg.fp8
+    idx = torch.from_numpy(d["topk_idx"]).to(dev)
+    w = torch.from_numpy(d["topk_weights"]).to(dev)
+    x = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    h = ep.EpHandle(T, K, cfg.num_experts, cfg.block_m)
+    pool, scales = h.new_pool(H, fp8=fp8)
+    out = torch.empty(h.capacity_rows, H, dtype=torch.bfloat16, device=dev)
+    spin = 2_000_000
+    recv = None
+    rows = []
+    for it in range(warmup + steps):
+        h.layout(idx, w)
+        e = torch.cuda.Event()
+        e.record(sa)
+        sb.wait_event(e)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record(sa)
+        seq = h.dispatch(x, pool, scales, fp8=fp8, tile_ready=True, stream=sa)
+        ev[1].record(sa)
+        ev[2].record(sb)
+        h.tile_consume(seq, pool, scales, H, out, fp8=fp8, workgroups=workgroups,
+                       spin_limit_us=spin, stream=sb, stamps=True)
+        ev[3].record(sb)
+        sa.wait_stream(sb)
+        torch.cuda.synchronize()
+        if it < warmup:
+            continue
+        if h.sync_status() != ep.EP_OK:
+            raise RuntimeError("a consumer wait timed out")
+        nt = int(h.array("num_tiles").cpu()[0])
+        if recv is None:
+            recv = h.array("pool_recv_token").cpu().numpy()
+            last_tok = np.array([recv[j * cfg.block_m:(j + 1) * cfg.block_m].max() for j in range(nt)])
+        st = h.array("tile_stamp").cpu().numpy().view(np.uint64)[:nt]
+        waited = (st >> np.uint64(63)).astype(bool)
+        clock = (st & np.uint64((1 << 63) - 1)).astype(np.int64)
+        t = [0.0] + [ev[0].elapsed_time(e_) * 1e3 for e_ in ev[1:]]
+        rho = None
+        if waited.sum() >= 2:
+            ra = np.argsort(np.argsort(clock[waited])).astype(np.float64)
+            rb = np.argsort(np.argsort(last_tok[waited])).astype(np.float64)
+            ra -= ra.mean()
+            rb -= rb.mean()
+            rho = float((ra * rb).sum() / np.sqrt((ra * ra).sum() * (rb * rb).sum()))
+        rows.append({"dispatch_us": t[1], "consumer_start_us": t[2], "consumer_end_us": t[3],
+                     "overlap_us": max(0.0, min(t[1], t[3]) - max(0.0, t[2])),
+                     "tiles": nt, "tiles_taken_while_landing": int(waited.sum()),
+                     "rank_corr_acquire_vs_last_token": rho})
+
+    def in_order():
+        h.layout(idx, w)
+        s_ = h.dispatch(x, pool, scales, fp8=fp8, tile_ready=True)
+        h.tile_consume(s_, pool, scales, H, out, fp8=fp8, workgroups=workgroups, spin_limit_us=spin)
+
+    def overlapped():
+        h.layout(idx, w)
+        e = torch.cuda.Event()
+        e.record(sa)
+        sb.wait_event(e)
+        s_ = h.dispatch(x, pool, scales, fp8=fp8, tile_ready=True, stream=sa)
+        h.tile_consume(s_, pool, scales, H, out, fp8=fp8, workgroups=workgroups,
+                       spin_limit_us=spin, stream=sb)
+        sa.wait_stream(sb)
+
+    t_order = _time_us(in_order, steps, warmup, sa)
+    t_over = _time_us(overlapped, steps, warmup, sa)
+    if h.sync_status() != ep.EP_OK:
+        raise RuntimeError("a consumer wait timed out")
+    h.close()
+    med = {k: float(np.median([r[k] for r in rows])) for k in
+           ("dispatch_us", "consumer_start_us", "consumer_end_us", "overlap_us")}
+    return {"metric": "streaming dispatch with the tile consumer on a second stream: overlap",
+            "unit": "us", "higher_is_better": False, "data": "synthetic",
+            "dtype": "fp8" if fp8 else "bf16",
+            "config": {"workload": f"{cfg.name}: {T} tokens, hidden {H}, {cfg.num_experts} experts "
+                                   f"{cfg.routing} top-{K}, BLOCK_M {cfg.block_m}, "
+                                   f"{'fp8' if fp8 else 'bf16'}, tile_ready",
+                       "consumer_workgroups": workgroups},
+            "median_us_from_dispatch_start": {k: round(v, 2) for k, v in med.items()},
+            "per_rep": rows,
+            "layout_dispatch_consumer_in_order_us": round(t_order, 2),
+            "layout_dispatch_consumer_two_streams_us": round(t_over, 2)}
+
+
 def ceiling_bench(steps: int, warmup: int) -> dict:
     """Context for the roofline: what plain torch kernels stream on this GPU
     (a 2 GiB fill, a 2 GiB read-reduce, a 2 GiB -> 2 GiB copy).  These are
@@ -557,6 +660,9 @@ def main() -> int:
                     help="print the eager vs HIP-graph step time instead")
     ap.add_argument("--ceiling", action="store_true",
                     help="print the bandwidth of plain torch fill / read / copy kernels instead")
+    ap.add_argument("--overlap", action="store_true",
+                    help="print the streaming dispatch / tile consumer overlap measurement instead "
+                         "(default workload: stream)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -587,6 +693,11 @@ def main() -> int:
     if args.ceiling:
         torch.cuda.set_device(0)
         print(json.dumps(ceiling_bench(args.steps, args.warmup)), flush=True)
+        return 0
+    if args.overlap:
+        torch.cuda.set_device(0)
+        name = "stream" if args.config == "prefill" else args.config
+        print(json.dumps(overlap_bench(CONFIGS[name], args.steps, args.warmup)), flush=True)
         return 0
     if args.fp8_variants:
         torch.cuda.set_device(0)

@@ -39,6 +39,7 @@ EP_SCALE_F32 = 1 << 4
 EP_SCALE_ROUND = 1 << 5
 EP_SCALE_MN_MAJOR = 1 << 6
 EP_CONSUME_SIGNAL_DONE = 1 << 7
+EP_CONSUME_STAMPS = 1 << 8
 
 # scale flavours by name: flags, element dtype
 SCALE_KINDS = {
@@ -59,6 +60,7 @@ ARRAYS = {
     "pool_recv_token": (8, torch.int32),
     "topk_weights": (9, torch.float32),
     "y_done_per_token": (10, torch.int32),
+    "tile_stamp": (11, torch.int64),
 }
 
 EXPORTS = [
@@ -416,7 +418,7 @@ class EpHandle:
                      hidden: int, out: torch.Tensor, fp8: bool = False, workgroups: int = 32,
                      spin_limit_us: int = 2_000_000, stream=None, gather: bool = False,
                      signal_done: bool = False, scale_kind: str = "ue8m0",
-                     mn_major: bool = False) -> None:
+                     mn_major: bool = False, stamps: bool = False) -> None:
         _require(out, torch.bfloat16, "out", self.device)
         if out.shape[0] < self.capacity_rows or out.shape[1] != hidden:
             raise ValueError("out must be at least [capacity_rows, hidden]")
@@ -430,7 +432,8 @@ class EpHandle:
         if not fp8 and (scale_kind != "ue8m0" or mn_major):
             raise ValueError("scale flavours apply to FP8 pools only")
         flags = (EP_DISPATCH_FP8 | scale_flags(scale_kind, mn_major) if fp8 else 0) | \
-                (EP_CONSUME_GATHER if gather else 0) | (EP_CONSUME_SIGNAL_DONE if signal_done else 0)
+                (EP_CONSUME_GATHER if gather else 0) | (EP_CONSUME_SIGNAL_DONE if signal_done else 0) | \
+                (EP_CONSUME_STAMPS if stamps else 0)
         ep_tile_consume(self._h, seq, pool, pool_scales if fp8 else None, hidden, flags, out,
                         workgroups, spin_limit_us, stream)
 
@@ -438,7 +441,7 @@ class EpHandle:
         """Device copy of one metadata array (see ARRAYS)."""
         which, dtype = ARRAYS[name]
         nbytes = int(_lib.ep_array_bytes(self._h, which))
-        out = torch.empty(nbytes // 4, dtype=dtype, device=self.device)
+        out = torch.empty(nbytes // dtype.itemsize, dtype=dtype, device=self.device)
         _check(_lib.ep_copy_array(self._h, which, _ptr(out), nbytes, _stream(stream)), "ep_copy_array")
         return out
 

@@ -33,6 +33,7 @@ struct ep_handle {
     uint32_t* error;
     int32_t* ws;
     uint32_t* y_done;         // per-token done counts of the combine gate
+    uint64_t* tile_stamp;     // consumer acquire stamps (EP_CONSUME_STAMPS)
     // routing density of the last completed layout (epk::Density), written by
     // the layout kernel into pinned host memory and read by ep_combine for
     // its launch shape; density_dev is the device's address of the word
@@ -164,6 +165,7 @@ ep_status ep_handle_create(const ep_config* cfg, ep_handle** out) {
         {(void**)&h->error, sizeof(uint32_t)},
         {(void**)&h->ws, sizeof(int32_t) * (size_t)h->ws_blocks * E},
         {(void**)&h->y_done, sizeof(uint32_t) * (size_t)cfg->max_tokens},
+        {(void**)&h->tile_stamp, sizeof(uint64_t) * mt},
     };
     size_t total = 0;
     for (const Part& p : parts) total += round_up(p.bytes ? p.bytes : 1, 256);
@@ -485,6 +487,7 @@ int64_t ep_array_bytes(const ep_handle* h, ep_array which) {
         case EP_ARRAY_TOPK_WEIGHTS: return 4 * slots;
         case EP_ARRAY_POOL_RECV_TOKEN: return 4 * h->cap;
         case EP_ARRAY_Y_DONE: return 4 * (int64_t)(h->T < 0 ? 0 : h->T);
+        case EP_ARRAY_TILE_STAMP: return 8 * mt;
     }
     return -1;
 }
@@ -508,6 +511,7 @@ ep_status ep_copy_array(const ep_handle* h, ep_array which, void* dst, int64_t d
         case EP_ARRAY_POOL_RECV_TOKEN: src = h->recv_token; break;
         case EP_ARRAY_TOPK_WEIGHTS: src = h->weights; break;
         case EP_ARRAY_Y_DONE: src = h->y_done; break;
+        case EP_ARRAY_TILE_STAMP: src = h->tile_stamp; break;
     }
     return hip_status(hipMemcpyAsync(dst, src, (size_t)n, hipMemcpyDeviceToDevice, stream));
 }
@@ -546,7 +550,7 @@ ep_status ep_tile_consume(const ep_handle* h, uint32_t seq, const void* pool,
                           int32_t workgroups, uint32_t spin_limit_us, hipStream_t stream) {
     if (!h) return EP_ERR_INVALID_ARGUMENT;
     if (flags & ~(EP_DISPATCH_FP8 | EP_DISPATCH_TILE_READY | EP_CONSUME_GATHER |
-                  EP_CONSUME_SIGNAL_DONE | kScaleFlags))
+                  EP_CONSUME_SIGNAL_DONE | EP_CONSUME_STAMPS | kScaleFlags))
         return EP_ERR_INVALID_ARGUMENT;
     const bool fp8 = (flags & EP_DISPATCH_FP8) != 0;
     const bool gather = (flags & EP_CONSUME_GATHER) != 0;
@@ -574,6 +578,7 @@ ep_status ep_tile_consume(const ep_handle* h, uint32_t seq, const void* pool,
     a.out = out;
     a.error = h->error;
     a.y_done = (flags & EP_CONSUME_SIGNAL_DONE) ? h->y_done : nullptr;
+    a.stamps = (flags & EP_CONSUME_STAMPS) ? h->tile_stamp : nullptr;
     a.scale_kind = scale_kind(flags);
     a.scale_mn = (flags & EP_SCALE_MN_MAJOR) ? 1 : 0;
     a.scale_ld = scale_ld_of(h->cap);

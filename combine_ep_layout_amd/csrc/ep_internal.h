@@ -126,6 +126,7 @@ struct ConsumeArgs {
     void* out;
     uint32_t* error;
     uint32_t* y_done;           // non-null: count each written row for its token
+    uint64_t* stamps;           // non-null: per tile, acquire clock | waited << 63
     int32_t scale_kind;         // FP8 scales: ScaleKind, layout and leading dimension
     int32_t scale_mn;
     int64_t scale_ld;

@@ -1409,9 +1409,11 @@ __global__ __launch_bounds__(256) void k_tile_consume(ConsumeArgs a) {
     for (int j = (int)blockIdx.x; j < nt; j += (int)gridDim.x) {
         if (tid == 0) {
             int go = 1;
+            uint64_t waited = 0;
             const uint64_t start = wall_clock64();
             while ((int32_t)(__hip_atomic_load(&a.tile_ready[j], __ATOMIC_ACQUIRE,
                                                __HIP_MEMORY_SCOPE_AGENT) - a.seq) < 0) {
+                waited = 1ull << 63;
                 if (wall_clock64() - start > a.limit_ticks) {
                     go = 0;
                     atomicOr(a.error, 2u);
@@ -1419,6 +1421,7 @@ __global__ __launch_bounds__(256) void k_tile_consume(ConsumeArgs a) {
                 }
                 __builtin_amdgcn_s_sleep(8);
             }
+            if (a.stamps && go) a.stamps[j] = wall_clock64() | waited;
             s_go = go;
         }
         __syncthreads();

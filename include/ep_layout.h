@@ -135,6 +135,14 @@ typedef struct ep_config {
  * for each real row r of the tile. */
 #define EP_CONSUME_GATHER      (1u << 3)
 #define EP_CONSUME_SIGNAL_DONE (1u << 7)
+/* EP_CONSUME_STAMPS: the consumer records, for each tile it takes, the
+ * device's constant-rate wall clock (hipDeviceAttributeWallClockRate) at the
+ * moment it saw tile_ready reach seq, with bit 63 set when its first look
+ * found the tile not yet ready (the dispatch was still landing rows), in the
+ * handle's array EP_ARRAY_TILE_STAMP (uint64 [max_tiles]; a tile that timed
+ * out keeps its old stamp).  Evidence that, and in which order, tiles were
+ * released while the dispatch ran. */
+#define EP_CONSUME_STAMPS      (1u << 8)
 
 /* Allocate a handle and all its device metadata on the current device.
  * Returns EP_ERR_INVALID_ARGUMENT for out-of-range fields or when the pool
@@ -322,7 +330,8 @@ typedef enum ep_array {
     EP_ARRAY_SLOT_TO_POOL_ROW = 7,
     EP_ARRAY_POOL_RECV_TOKEN = 8,
     EP_ARRAY_TOPK_WEIGHTS = 9,
-    EP_ARRAY_Y_DONE = 10
+    EP_ARRAY_Y_DONE = 10,
+    EP_ARRAY_TILE_STAMP = 11        /* uint64 [max_tiles], see EP_CONSUME_STAMPS */
 } ep_array;
 
 /* Byte size of a metadata array for the current layout. */
@@ -355,7 +364,7 @@ ep_status ep_handle_sync_status(ep_handle* h, hipStream_t stream);
  * on that tile and sets EP_ERR_TIMEOUT in the error word, so it always ends.
  * The caller orders it after ep_layout (e.g. with an event).  flags:
  * EP_DISPATCH_FP8 with any EP_SCALE_* flags, EP_CONSUME_GATHER (bf16 only),
- * EP_CONSUME_SIGNAL_DONE. */
+ * EP_CONSUME_SIGNAL_DONE, EP_CONSUME_STAMPS. */
 ep_status ep_tile_consume(const ep_handle* h, uint32_t seq, const void* pool,
                           const void* pool_scales, int32_t hidden, uint32_t flags,
                           void* out, int32_t workgroups, uint32_t spin_limit_us,

@@ -162,3 +162,73 @@ def test_layout_stamps_its_tiles_with_the_last_sequence_number():
     assert s3 == s2 + 1 and (ready(L2["num_tiles"]) == s3).all()
     assert h.sync_status() == ep.EP_OK
     h.close()
+
+
+def _spearman(a, b):
+    ra = np.argsort(np.argsort(a)).astype(np.float64)
+    rb = np.argsort(np.argsort(b)).astype(np.float64)
+    ra -= ra.mean()
+    rb -= rb.mean()
+    return float((ra * rb).sum() / np.sqrt((ra * ra).sum() * (rb * rb).sum()))
+
+
+def test_consumer_overlaps_dispatch_in_token_order():
+    """Full stream workload, consumer (256 workgroups, acquire stamps on) on a
+    second stream enqueued right after the streaming dispatch.  Every row is
+    checked.  When the consumer's stream started before the dispatch ended
+    (they did not share a hardware queue), some tiles must have been seen not
+    ready and then ready -- the consumer ran while rows were landing -- and
+    those tiles must have become ready in the order the dispatch writes
+    tokens: their acquire clocks rank-correlate with the last token each tile
+    holds."""
+    import combine_ep_layout_amd as ep
+    import oracle_par
+    say("[stream] consumer overlapping the dispatch, acquire stamps")
+    cfg, d = inputs("stream")
+    L = oracle_layout("stream")
+    q_tok, s_tok = oracle_par.quantize_tokens(d["x"])
+    per_token = (q_tok, s_tok, oracle_par.dequant_tokens(q_tok, s_tok))
+    h = new_handle(cfg)
+    H = cfg.hidden
+    sa, sb = torch.cuda.current_stream(), torch.cuda.Stream()      # default priority
+    h.layout(*device_routing(d))
+    x = to_dev_bf16(d["x"])
+    pool, scales = h.new_pool(H, fp8=True)
+    out = torch.zeros(h.capacity_rows, H, dtype=torch.bfloat16, device=dev())
+    ev = torch.cuda.Event()
+    ev.record(sa)
+    sb.wait_event(ev)
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record(sa)
+    seq = h.dispatch(x, pool, scales, fp8=True, tile_ready=True, stream=sa)
+    d1.record(sa)
+    c0.record(sb)
+    h.tile_consume(seq, pool, scales, H, out, fp8=True, workgroups=256, spin_limit_us=SPIN_US,
+                   stream=sb, stamps=True)
+    c1.record(sb)
+    sa.synchronize()
+    sb.synchronize()
+    assert h.sync_status() == ep.EP_OK, "a consumer wait timed out"
+    _check_end_state(h, L, seq, 1)
+    _check_rows(d, L, True, out, pool, scales, per_token)
+    nt = L["num_tiles"]
+    st = h.array("tile_stamp").cpu().numpy().view(np.uint64)[:nt]
+    waited = (st >> np.uint64(63)).astype(bool)
+    clock = (st & np.uint64((1 << 63) - 1)).astype(np.int64)
+    started_before_end = c0.elapsed_time(d1) > 0          # consumer stream began before the dispatch ended
+    say(f"  dispatch {d0.elapsed_time(d1) * 1e3:.1f} us; consumer began "
+        f"{d0.elapsed_time(c0) * 1e3:.1f} us after the dispatch, ended "
+        f"{d0.elapsed_time(c1) * 1e3:.1f} us after it; tiles seen not ready first: "
+        f"{int(waited.sum())} of {nt}")
+    if not started_before_end:
+        say("  the two streams ran one after the other (shared hardware queue): no overlap to check")
+        h.close()
+        return
+    assert waited.sum() >= 16
+    recv = L["pool_recv_token"]
+    last_tok = np.array([recv[j * cfg.block_m:(j + 1) * cfg.block_m].max() for j in range(nt)])
+    rho = _spearman(clock[waited], last_tok[waited])
+    say(f"  rank correlation of acquire clock and last token, waited tiles: {rho:.3f}")
+    assert rho > 0.8
+    h.close()
