@@ -104,42 +104,56 @@ def read_traffic(kernel: str, workload: str, per_launch_alg: float):
 
 
 def cpu_baseline(cfg, d, eo_host: np.ndarray, reps: int, tokens: int):
-    """Time the oracle (single-threaded C) on the first `tokens` tokens of the
-    same workload (all of them when tokens >= T); GB/s uses the same
-    algorithmic byte counts as the GPU figure, for that sample."""
+    """Time the oracle on the first `tokens` tokens of the same workload (all
+    of them when tokens >= T), twice: as it stands, on one host thread, and
+    with its dispatch and combine split over token or row ranges on every
+    host core this process may use (at most 16), calling the same oracle
+    functions; the layout is a global stable sort and runs on one thread in
+    both.  GB/s uses the same algorithmic byte counts as the GPU figure, for
+    that sample."""
     import oracle
+    from oracle import par
     n = min(tokens, cfg.tokens)
     sub = {k: v[:n] for k, v in d.items()}
     scfg = cfg.replace(tokens=n)
     L0 = oracle.layout(sub["topk_idx"], cfg.num_experts, cfg.block_m)
     ab = algorithmic_bytes(scfg, sub["topk_idx"], L0["expert_counts"], cfg.fp8)
     alg = ab["layout"] + ab["dispatch"] + ab["combine"]
-    times, stages = [], []
-    for _ in range(reps):
-        t0 = time.perf_counter()
-        L = oracle.layout(sub["topk_idx"], cfg.num_experts, cfg.block_m)
-        t1 = time.perf_counter()
-        if cfg.fp8:
-            oracle.dispatch_fp8(sub["x"], L["pool_recv_token"])
-        else:
-            oracle.dispatch_bf16(sub["x"], L["pool_recv_token"])
-        t2 = time.perf_counter()
-        oracle.combine(eo_host, L["slot_to_pool_row"], sub["topk_weights"])
-        t3 = time.perf_counter()
-        times.append(t3 - t0)
-        stages.append((t1 - t0, t2 - t1, t3 - t2))
-    t = float(np.median(times))
-    st = np.median(np.array(stages), axis=0)
+
+    def leg(threaded: bool):
+        times, stages = [], []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            L = oracle.layout(sub["topk_idx"], cfg.num_experts, cfg.block_m)
+            t1 = time.perf_counter()
+            if cfg.fp8:
+                (par.dispatch_fp8_rows if threaded else oracle.dispatch_fp8)(sub["x"], L["pool_recv_token"])
+            else:
+                (par.dispatch_bf16_rows if threaded else oracle.dispatch_bf16)(sub["x"], L["pool_recv_token"])
+            t2 = time.perf_counter()
+            (par.combine if threaded else oracle.combine)(eo_host, L["slot_to_pool_row"], sub["topk_weights"])
+            t3 = time.perf_counter()
+            times.append(t3 - t0)
+            stages.append((t1 - t0, t2 - t1, t3 - t2))
+        t = float(np.median(times))
+        st = np.median(np.array(stages), axis=0)
+        return {"value": round(alg / t / 1e9, 3), "unit": "GB/s",
+                "cores": par.threads() if threaded else 1,
+                "seconds_per_pass": round(t, 3),
+                "stage_seconds": {"layout": round(float(st[0]), 4),
+                                  "dispatch": round(float(st[1]), 4),
+                                  "combine": round(float(st[2]), 4)}}
+
+    one = leg(False)
+    many = leg(True)
     what = (f"the full {cfg.name} workload ({n} tokens)" if n == cfg.tokens else
             f"the first {n} of {cfg.tokens} tokens of the {cfg.name} workload")
-    return {"value": round(alg / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "seconds_per_pass": round(t, 3),
-            "stage_seconds": {"layout": round(float(st[0]), 4), "dispatch": round(float(st[1]), 4),
-                              "combine": round(float(st[2]), 4)},
-            "tokens": n,
-            "tokens_per_s": round(n / t, 1),
-            "sample": f"{what}, layout + dispatch + combine, median of {reps} passes, "
-                      f"one host thread"}
+    out = dict(many)
+    out.update({"kind": "oracle", "tokens": n, "tokens_per_s": round(n / many["seconds_per_pass"], 1),
+                "sample": f"{what}, layout + dispatch + combine, median of {reps} passes; dispatch and "
+                          f"combine split over {many['cores']} host threads (layout on one)",
+                "single_thread": one})
+    return out
 
 
 def borrow_compare(steps: int, warmup: int) -> dict:
@@ -278,9 +292,10 @@ def _time_us(fn, steps: int, warmup: int, stream) -> float:
     return a.elapsed_time(b) / steps * 1e3
 
 
-def _time_in_step_us(before, fn, after, steps: int, warmup: int, stream) -> float:
+def _time_in_step_us(before, fn, after, steps: int, warmup: int, stream, flush=None) -> float:
     """Mean duration of fn's launches when each one runs between `before` and
-    `after` (the kernels around it in a step), from HIP events on `stream`."""
+    `after` (the kernels around it in a step), from HIP events on `stream`;
+    with `flush`, it runs before every timed step."""
     import torch
     for _ in range(warmup):
         before()
@@ -290,6 +305,8 @@ def _time_in_step_us(before, fn, after, steps: int, warmup: int, stream) -> floa
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     for a, b in ev:
+        if flush is not None:
+            flush()
         before()
         a.record(stream)
         fn()
@@ -645,7 +662,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--cpu-tokens", type=int, default=-1,
-                    help="tokens of the CPU-oracle sample (default: all for bf16, 2048 for FP8)")
+                    help="tokens of the CPU-oracle sample (default: all for bf16, 1024 for FP8)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--borrow-compare", action="store_true",
@@ -747,63 +764,76 @@ def main() -> int:
     torch.cuda.synchronize()
     assert h.sync_status() == ep.EP_OK
 
-    # Timed region: exactly K steps between two events, nothing else on the
-    # stream (a per-kernel event costs a few microseconds of marker packets).
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    log(f"[bench] timing {args.steps} steps")
+    def pct(v):
+        return {"p10": round(float(np.percentile(v, 10)), 2), "p50": round(float(np.median(v)), 2),
+                "p90": round(float(np.percentile(v, 90)), 2)}
+
+    # Caches are flushed before every timed step: reading 1 GiB replaces L2
+    # and the 256 MB MALL with clean lines (a read, not a write, so no dirty
+    # line is left to be written back inside the timed kernels; the smaller
+    # workloads would otherwise stay in the MALL from one step to the next).
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    sink = torch.empty((), dtype=torch.int64, device=dev)
+
+    def do_flush():
+        torch.sum(flush, dim=0, dtype=torch.int64, out=sink)
+
+    do_flush()                                            # the fill's dirty lines go out here
+    torch.cuda.synchronize()
+
+    # Timed region (the headline): exactly K steps, each after a flush, with
+    # a HIP event pair around the step only (the flush is outside it).
+    log(f"[bench] timing {args.steps} steps, caches flushed before each")
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
+    for a_, b_ in step_ev:
+        do_flush()
+        a_.record(stream)
+        step()
+        b_.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_us = np.array([a_.elapsed_time(b_) for a_, b_ in step_ev]) * 1e3
+    ms_per_step = float(step_us.mean()) / 1e3
+
+    # Per-kernel durations in flushed steps: a second pass of K steps with HIP
+    # events around every launch, on the stream the library launches on.
+    log(f"[bench] timing {args.steps} flushed steps per kernel")
+    cold = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        do_flush()
+        step(cold[i])
+    torch.cuda.synchronize()
+    cold_s = {k: np.array([e[j].elapsed_time(e[j + 1]) for e in cold]) * 1e3
+              for j, k in enumerate(("layout", "dispatch", "combine"))}
+    lay, dis, com = (float(cold_s[k].mean()) / 1e3 for k in ("layout", "dispatch", "combine"))
+
+    # Warm steps, labelled as such: K steps back to back between two events
+    # (each step finds what the previous one left in L2 and MALL), then a pass
+    # with events around every launch.
+    log(f"[bench] timing {args.steps} warm steps")
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
         step()
     t_end.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_per_step = t_start.elapsed_time(t_end) / args.steps
-    # Per-kernel durations: a second timed pass of K steps with HIP events
-    # around every launch, on the stream the library launches on.
+    warm_ms_per_step = t_start.elapsed_time(t_end) / args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    i_start = torch.cuda.Event(enable_timing=True)
-    i_end = torch.cuda.Event(enable_timing=True)
-    log(f"[bench] timing {args.steps} instrumented steps")
-    i_start.record(stream)
     for i in range(args.steps):
         step(evs[i])
-    i_end.record(stream)
     torch.cuda.synchronize()
-    ms_instrumented = i_start.elapsed_time(i_end) / args.steps
-    lay_s = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
-    dis_s = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
-    com_s = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e3
-    lay, dis, com = (float(v.mean()) / 1e3 for v in (lay_s, dis_s, com_s))
-
-    def pct(v):
-        return {"p10": round(float(np.percentile(v, 10)), 2), "p50": round(float(np.median(v)), 2),
-                "p90": round(float(np.percentile(v, 90)), 2)}
-
-    # Cold per-kernel times: reading 1 GiB between steps replaces L2 and MALL
-    # with clean lines (the smaller workloads fit in the 256 MB MALL when run
-    # back to back).  A read, not a write, so no dirty lines are left to be
-    # written back during the timed kernels.
-    log(f"[bench] timing {args.steps} cold steps")
-    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
-    sink = torch.empty((), dtype=torch.int64, device=dev)
-    torch.sum(flush, dim=0, dtype=torch.int64, out=sink)        # the fill's dirty lines go out here
-    torch.cuda.synchronize()
-    cold = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        torch.sum(flush, dim=0, dtype=torch.int64, out=sink)
-        step(cold[i])
-    torch.cuda.synchronize()
-    del flush, sink
-    cold_us = {k: pct(np.array([e[j].elapsed_time(e[j + 1]) for e in cold]) * 1e3)
-               for j, k in enumerate(("layout", "dispatch", "combine"))}
+    warm_s = {k: np.array([e[j].elapsed_time(e[j + 1]) for e in evs]) * 1e3
+              for j, k in enumerate(("layout", "dispatch", "combine"))}
 
     # With the streaming release on, the same dispatch without it, for
     # comparison, timed the same way: inside the layout -> dispatch -> combine
     # step, with HIP events around each dispatch.
-    no_ready = None
+    no_ready = no_ready_warm = None
     if ready:
         st = {}
 
@@ -813,14 +843,19 @@ def main() -> int:
         def after():
             h.combine(st["epoch"], eo, y)
 
-        no_ready = _time_in_step_us(before, lambda: h.dispatch(x, pool, scales, fp8=fp8,
-                                                               tile_ready=False),
-                                    after, args.steps, args.warmup, stream)
+        def plain():
+            h.dispatch(x, pool, scales, fp8=fp8, tile_ready=False)
+
+        no_ready = _time_in_step_us(before, plain, after, args.steps, args.warmup, stream,
+                                    flush=do_flush)
+        no_ready_warm = _time_in_step_us(before, plain, after, args.steps, args.warmup, stream)
+    del flush, sink
 
     counts, _ = h.counts_to_host()
     ab = algorithmic_bytes(cfg, d["topk_idx"], counts, fp8)
     total = ab["layout"] + ab["dispatch"] + ab["combine"]
     value = total / (ms_per_step * 1e-3) / 1e9
+    warm_value = total / (warm_ms_per_step * 1e-3) / 1e9
     kern = {"dispatch": (dis, ab["dispatch"]), "combine": (com, ab["combine"])}
     dom = max(kern, key=lambda k: kern[k][0])
     dom_ms, dom_bytes = kern[dom]
@@ -839,7 +874,7 @@ def main() -> int:
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         eo_host = eo.view(torch.int16).cpu().numpy().view(np.uint16)
-        ntok = args.cpu_tokens if args.cpu_tokens > 0 else (2048 if fp8 else T)
+        ntok = args.cpu_tokens if args.cpu_tokens > 0 else (1024 if fp8 else T)
         cpu = cpu_baseline(cfg, d, eo_host, args.cpu_reps, ntok)
         del eo_host
 
@@ -850,6 +885,8 @@ def main() -> int:
         gpu_s = {"layout": lay * 1e-3, "dispatch": dis * 1e-3, "combine": com * 1e-3}
         cpu["speedup_per_stage"] = {k: round(cpu["stage_seconds"][k] * scale / gpu_s[k], 1)
                                     for k in gpu_s}
+        cpu["single_thread"]["speedup_per_stage"] = {
+            k: round(cpu["single_thread"]["stage_seconds"][k] * scale / gpu_s[k], 1) for k in gpu_s}
     mode = "fp8" if fp8 else "bf16"
     out = {
         "metric": METRIC,
@@ -871,11 +908,23 @@ def main() -> int:
                    "block_m": cfg.block_m, "routing": cfg.routing},
         "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
         "pct_of_peak": round(100.0 * value / PEAK_GBS, 2),
+        "timing": "caches flushed (1 GiB read) before every step; mean of the K steps' HIP-event "
+                  "intervals, the flush outside them",
+        "step_us_percentiles": pct(step_us),
         "kernels_us": {"layout": round(lay * 1e3, 2), "dispatch": round(dis * 1e3, 2),
                        "combine": round(com * 1e3, 2)},
-        "kernels_us_percentiles": {"layout": pct(lay_s), "dispatch": pct(dis_s),
-                                   "combine": pct(com_s)},
-        "kernels_us_cold": cold_us,
+        "kernels_us_percentiles": {k: pct(v) for k, v in cold_s.items()},
+        "warm": {"what": "K steps back to back (each step finds the previous step's data in L2 "
+                         "and MALL), one event pair around all of them; per-kernel times from a "
+                         "pass with events around every launch",
+                 "ms_per_step": round(warm_ms_per_step, 4),
+                 "value": round(warm_value, 2),
+                 "pct_of_peak": round(100.0 * warm_value / PEAK_GBS, 2),
+                 "tokens_per_s": round(T / (warm_ms_per_step * 1e-3), 1),
+                 "kernels_us": {k: round(float(v.mean()), 2) for k, v in warm_s.items()},
+                 "kernels_us_percentiles": {k: pct(v) for k, v in warm_s.items()},
+                 "dispatch_us_without_tile_ready": None if no_ready_warm is None
+                 else round(no_ready_warm, 2)},
         "dispatch_us_without_tile_ready": None if no_ready is None else round(no_ready, 2),
         "alg_bytes": {k: ab[k] for k in ("layout", "dispatch", "combine")},
         "routing_stats": {"n_assign": ab["n_a"], "active_tokens": ab["t_act"],
@@ -883,9 +932,8 @@ def main() -> int:
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": PEAK_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
                      "traffic": traffic,
-                     "timing": f"mean of the kernel's HIP-event intervals over a second timed "
-                               f"pass of {args.steps} steps"},
-        "ms_per_step_instrumented": round(ms_instrumented, 4),
+                     "timing": f"mean of the kernel's HIP-event intervals over {args.steps} "
+                               f"flushed steps (a second pass, events around every launch)"},
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }

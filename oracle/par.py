@@ -1,4 +1,5 @@
-"""The oracle's results at full workload sizes, for the GPU parity tests.
+"""The oracle's results at full workload sizes: test infrastructure, used by
+the GPU parity tests and by the benchmark's CPU-baseline leg only.
 
 The oracle's per-token functions are called from a pool of host threads
 (ctypes releases the interpreter lock during a foreign call, so the plain C
@@ -117,3 +118,30 @@ def dispatch_backward(grad_pool: np.ndarray, slot_to_row: np.ndarray, tokens: in
 
     _run(tokens, work)
     return gx
+
+
+def dispatch_bf16_rows(x: np.ndarray, recv_token: np.ndarray) -> np.ndarray:
+    """oracle.dispatch_bf16 over ranges of pool rows (every range writes its own rows)."""
+    recv = np.ascontiguousarray(recv_token, dtype=np.int32)
+    pool = np.zeros((recv.size, x.shape[1]), np.uint16)
+
+    def work(a, b):
+        pool[a:b] = oracle.dispatch_bf16(x, recv[a:b])
+
+    _run(recv.size, work, min_chunk=1024)
+    return pool
+
+
+def dispatch_fp8_rows(x: np.ndarray, recv_token: np.ndarray):
+    """oracle.dispatch_fp8 over ranges of pool rows: the oracle quantises each
+    row from its token, as it does in one call."""
+    recv = np.ascontiguousarray(recv_token, dtype=np.int32)
+    H = x.shape[1]
+    pool = np.zeros((recv.size, H), np.uint8)
+    scales = np.zeros((recv.size, H // 128), np.uint8)
+
+    def work(a, b):
+        pool[a:b], scales[a:b] = oracle.dispatch_fp8(x, recv[a:b])
+
+    _run(recv.size, work, min_chunk=64)
+    return pool, scales

@@ -73,7 +73,7 @@ def test_max_tokens_top32():
     say("  dispatch matches")
     # combine on seeded expert rows, NaN in every row no slot owns: every
     # token against the oracle (top-32 walks the slots in four groups of 8)
-    import oracle_par
+    from oracle import par as oracle_par
     eo = torch.randn(cap, H, generator=g, device=dev()).to(torch.bfloat16)
     eo[~real] = float("nan")
     y = h.combine(epoch, eo)

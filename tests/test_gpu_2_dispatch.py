@@ -33,7 +33,7 @@ def _full_size_dispatch(name, fp8):
     oracle: a real row holds its token's bytes, a padding row keeps its
     poison.  The oracle quantises each token once; its codes and scales are
     the expected contents of each of the token's rows."""
-    import oracle_par
+    from oracle import par as oracle_par
     cfg, d = inputs(name)
     L = oracle_layout(name)
     h = new_handle(cfg)

@@ -61,7 +61,7 @@ def test_combine_full_compare(name):
 def test_combine_full_size(name):
     """The metric's workload and the streaming one at full size: every
     element of y against the oracle's combine of the same expert rows."""
-    import oracle_par
+    from oracle import par as oracle_par
     say(f"[combine] {name} full size, every token")
     cfg, d = inputs(name)
     L = oracle_layout(name)

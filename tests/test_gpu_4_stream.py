@@ -56,7 +56,7 @@ def _check_rows(d, L, fp8, out, pool, scales, per_token):
 
 def _run(name, tokens, fp8, replays=1, top_k=None):
     import combine_ep_layout_amd as ep
-    import oracle_par
+    from oracle import par as oracle_par
     cfg, d = inputs(name, tokens)
     if top_k is not None:                       # the same tokens, routed to top_k experts
         cfg = cfg.replace(top_k=top_k)
@@ -182,7 +182,7 @@ def test_consumer_overlaps_dispatch_in_token_order():
     tokens: their acquire clocks rank-correlate with the last token each tile
     holds."""
     import combine_ep_layout_amd as ep
-    import oracle_par
+    from oracle import par as oracle_par
     say("[stream] consumer overlapping the dispatch, acquire stamps")
     cfg, d = inputs("stream")
     L = oracle_layout("stream")

@@ -84,7 +84,7 @@ def test_dispatch_backward_parity(name, tokens):
 def test_backward_full_size():
     """The metric's workload at full size: every gradient row, every weight
     gradient and every row of grad_x against the oracle."""
-    import oracle_par
+    from oracle import par as oracle_par
     say("[backward] prefill full size, every token")
     cfg, d = inputs("prefill")
     L = oracle.layout(d["topk_idx"], cfg.num_experts, cfg.block_m)

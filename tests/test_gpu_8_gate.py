@@ -28,7 +28,7 @@ def _slots_per_token(L, T, K):
 def _expected_y(d, L, fp8):
     """Oracle combine of the producer's rows: copies of x (bf16) or the
     dequantised FP8 rows; padding rows are NaN and never read."""
-    import oracle_par
+    from oracle import par as oracle_par
     recv = L["pool_recv_token"]
     H = d["x"].shape[1]
     eo = np.full((recv.size, H), 0x7FC0, np.uint16)

@@ -64,7 +64,7 @@ def _dispatch_check(cfg, d, kind, mn, tile_ready=False, per_token=None):
     else:
         # full size: every real row against the oracle's quantisation of its
         # token (computed once per token), every padding row untouched
-        import oracle_par
+        from oracle import par as oracle_par
         real = np.flatnonzero(recv >= 0)
         q_tok, s_tok = per_token
         G = H // 128
@@ -169,7 +169,7 @@ def test_streaming_consumer_every_flavour(kind, mn):
 def test_scaled_dispatch_full_size(kind):
     """The prefill workload at full size in each flavour and both scale
     layouts: every pool row and scale against the oracle."""
-    import oracle_par
+    from oracle import par as oracle_par
     cfg, d = inputs("prefill")
     per_token = oracle_par.quantize_tokens(d["x"], kind=kind)
     for mn in (False, True):

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 import oracle
-import oracle_par
+from oracle import par as oracle_par
 from synth import CONFIGS, generate, expert_rows
 
 
