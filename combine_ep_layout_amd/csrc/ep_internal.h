@@ -7,13 +7,9 @@
 
 namespace epk {
 
-#ifndef EP_LAYOUT_SLOTS_PER_LANE
-#define EP_LAYOUT_SLOTS_PER_LANE 2
-#endif
-
-// Slots ranked by one layout workgroup (1024 threads x EP_LAYOUT_SLOTS_PER_LANE).
+// Slots ranked by one layout workgroup (1024 threads x 2 slots per lane).
 // Up to this many slots the whole layout runs in a single workgroup and launch.
-constexpr int kLayoutSlotsPerBlock = 1024 * EP_LAYOUT_SLOTS_PER_LANE;
+constexpr int kLayoutSlotsPerBlock = 1024 * 2;
 
 // Layout arguments.  topk_w / weights, arrival / tile_ready, y_done, error
 // and density may be null (a layout into caller-owned arrays has none of

@@ -39,61 +39,39 @@
 
 #include "ep_internal.h"
 
-#ifndef EP_DISPATCH_UNROLL
-#define EP_DISPATCH_UNROLL 7   // 16-byte chunks per lane per bf16 dispatch work item
-#endif
-#ifndef EP_FP8_UNROLL
-#define EP_FP8_UNROLL 1        // 16-channel units per lane per FP8 dispatch work item
-#endif
-#ifndef EP_FP8_STREAM_UNROLL
-#define EP_FP8_STREAM_UNROLL 2 // the same for the streaming (tile_ready) FP8 dispatch
-#endif
-#ifndef EP_FP8_HW_ENCODE
-#define EP_FP8_HW_ENCODE 1     // UE8M0 codes through gfx950's scaled conversion
-#endif
-#ifndef EP_FP8_PACK8
-#define EP_FP8_PACK8 1         // UE8M0 scale bytes of a full step as one 64-bit store per row
-#endif
-#ifndef EP_COMBINE_UNROLL
-#define EP_COMBINE_UNROLL 2    // 16-byte chunks per lane per combine work item
-#endif
-#ifndef EP_ITEMS_PER_WAVE
-#define EP_ITEMS_PER_WAVE 1    // work items per wave outside streaming mode
-#endif
-#ifndef EP_STREAM_TOKENS
-#define EP_STREAM_TOKENS 2     // tokens per released chunk (one workgroup) in streaming mode
-#endif
-#ifndef EP_STREAM_THREADS
-#define EP_STREAM_THREADS 256  // threads per streaming workgroup
-#endif
-#ifndef EP_DISPATCH_STORE
-#define EP_DISPATCH_STORE 4    // pool stores outside streaming: see store_row
-#endif
-#ifndef EP_COMBINE_STORE
-#define EP_COMBINE_STORE 1     // y stores: see store_row
-#endif
-#ifndef EP_COMBINE_RESIDENT_WAVES
-#define EP_COMBINE_RESIDENT_WAVES 8  // combine grids up to this many waves per CU run at full occupancy
-#endif
-#ifndef EP_COMBINE_DENSE_LDS
-#define EP_COMBINE_DENSE_LDS 55296  // unused LDS per combine workgroup for dense routing: 2 per CU
-#endif
-#ifndef EP_COMBINE_NT_LOADS
-#define EP_COMBINE_NT_LOADS 1  // non-temporal loads of expert rows
-#endif
-#ifndef EP_STREAM_STORE
-#define EP_STREAM_STORE 2      // pool stores in streaming mode: see store_row
-#endif
-
 namespace epk {
 namespace {
+
+// Work shapes, chosen by measurement on MI355X (see the design notes): 16-byte
+// chunks or 16-channel units each lane handles per work item, and the
+// streaming dispatch's chunk.
+constexpr int kDispatchChunks = 7;      // bf16 dispatch: 16-byte chunks per lane per item
+constexpr int kFp8Units = 1;            // FP8 dispatch: 16-channel units per lane per item
+constexpr int kFp8StreamUnits = 2;      // the same with the streaming release
+constexpr int kCombineChunks = 2;       // combine: 16-byte chunks per lane per item
+constexpr int kStreamTokens = 2;        // streaming dispatch: tokens per chunk (one workgroup)
+constexpr int kStreamThreads = 256;     // streaming dispatch: threads per workgroup
+constexpr int kCombineResidentWaves = 8;   // combine grids up to this many waves per CU: full occupancy
+constexpr int kCombineDenseLds = 55296;    // unused LDS per combine workgroup for dense routing: 2 per CU
+constexpr int kBwdChunks = 2;           // combine backward: 16-byte chunks per lane in flight
+constexpr int kCastLds = 32768;         // cast back: unused LDS per workgroup for power-of-two scales
+constexpr int kCastLdsMinGrid = 16384;  // ... on grids of at least this many workgroups
+constexpr int kCastUnits = 2;           // cast back: 16-channel units per lane per item
+constexpr int kGateTokens = 16;         // gated combine: most tokens per workgroup (<= 64)
+constexpr int kGateWaves = 16;          // gated combine: most waves per workgroup
+constexpr int kGateDefer = 4;           // gated combine: dense items computed before their stores
+
+// Cache policy bits of buffer loads and stores on gfx950.
+constexpr int kAuxNonTemporal = 2;      // nt: streaming, not kept in the caches
+constexpr int kAuxDevice = 16;          // sc1: device scope (write-through / coherent read)
+
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kLayoutThreads = 1024;                          // 16 waves
 constexpr int kLayoutWaves = kLayoutThreads / kWave;
-constexpr int kSlotsPerLane = kLayoutSlotsPerBlock / kLayoutThreads;   // EP_LAYOUT_SLOTS_PER_LANE
+constexpr int kSlotsPerLane = kLayoutSlotsPerBlock / kLayoutThreads;   // slots per lane
 constexpr int kWaveSlots = kLayoutSlotsPerBlock / kLayoutWaves;       // slots per wave
 
 __device__ __forceinline__ int uniform_i(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -488,30 +466,30 @@ __device__ void release_chunk(const DispatchArgs& a, int t0, int t1, uint32_t* s
     }
 }
 
-// Store of 16-byte chunk c of a row.  MODE 0: plain; 1: non-temporal;
-// 2: device-coherent (sc1) buffer store; 3: device-coherent 64-bit atomic
-// stores; 4: device-coherent and non-temporal buffer store.  Device-coherent
-// stores leave no dirty lines in the XCD's L2, which makes a later
-// device-scope release (and the end-of-kernel write-back) cheap.
-template <int MODE>
+// Stores of 16-byte chunk c of a row.  The pool, the gradient rows and y are
+// written once and read by another kernel, so nothing is kept in the caches
+// (non-temporal).  Device-scope stores are written through the XCD's L2: they
+// leave no dirty line behind, which keeps a later device-scope release (and
+// the end-of-kernel write-back) cheap, and they count as complete only once
+// every XCD can see them, which the streaming release relies on.
+enum StoreMode { kStoreNonTemporal, kStoreDevice, kStoreDeviceNonTemporal };
+
+template <StoreMode MODE>
 __device__ __forceinline__ void store_row(u32x4* row, int row_bytes, int c, const u32x4& v) {
-    if constexpr (MODE == 3) {
-        uint64_t* q = (uint64_t*)(row + c);
-        __hip_atomic_store(q, (uint64_t)v[0] | ((uint64_t)v[1] << 32), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(q + 1, (uint64_t)v[2] | ((uint64_t)v[3] << 32), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    } else if constexpr (MODE == 2 || MODE == 4) {
-        __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(row, (short)0, row_bytes, 0x00020000);
-        __builtin_amdgcn_raw_buffer_store_b128(v, r, c * 16, 0, MODE == 2 ? 16 : 18);
+    if constexpr (MODE == kStoreNonTemporal) {
+        __builtin_nontemporal_store(v, row + c);
     } else {
-        store_v<MODE == 1>(row + c, v);
+        __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(row, (short)0, row_bytes, 0x00020000);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            v, r, c * 16, 0, MODE == kStoreDevice ? kAuxDevice : kAuxDevice | kAuxNonTemporal);
     }
 }
 
+// Pool rows: device-scope non-temporal stores, plain device-scope ones with
+// the streaming release (measured faster there).
 template <bool STREAM>
 __device__ __forceinline__ void store_pool(u32x4* row, int row_bytes, int c, const u32x4& v) {
-    store_row<STREAM ? EP_STREAM_STORE : EP_DISPATCH_STORE>(row, row_bytes, c, v);
+    store_row<STREAM ? kStoreDevice : kStoreDeviceNonTemporal>(row, row_bytes, c, v);
 }
 
 // Slot groups.  A kernel holds the pool rows (and weights) of at most KT <= 8
@@ -545,7 +523,7 @@ __device__ __forceinline__ bool load_rows(const int32_t* s2r, int t, int K, int 
 // read as they are stored (an item is never skipped).
 template <int KT, bool STREAM, bool MANY>
 __global__ __launch_bounds__(1024) void k_dispatch_bf16(DispatchArgs a, int nseg, int ipb) {
-    constexpr int U = EP_DISPATCH_UNROLL;
+    constexpr int U = kDispatchChunks;
     const int lane = threadIdx.x & (kWave - 1);
     const int w = uniform_i(threadIdx.x / kWave);
     const int n16 = a.H / 8;
@@ -793,7 +771,7 @@ __global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg,
     const int nunit = a.H / 16;          // 16 channels (32 bytes in, 16 bytes out) per unit
     const int ngrp = a.H / 128;
     // (the streaming release is faster with plain byte stores written back by its fence)
-    const bool pack8 = EP_FP8_PACK8 && (ngrp & 7) == 0 && ((uintptr_t)a.scales & 7) == 0;
+    const bool pack8 = (ngrp & 7) == 0 && ((uintptr_t)a.scales & 7) == 0;
     const u32x4* x = (const u32x4*)a.x;
     u32x4* pool = (u32x4*)a.pool;
     const int nw = (int)blockDim.x / kWave;
@@ -901,7 +879,7 @@ __global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg,
                     special |= ((lo[u][i] & 0x7F80u) == 0x7F80u) | ((lo[u][i] & 0x7F800000u) == 0x7F800000u);
                     special |= ((hi[u][i] & 0x7F80u) == 0x7F80u) | ((hi[u][i] & 0x7F800000u) == 0x7F800000u);
                 }
-                if (EP_FP8_HW_ENCODE && !special) {
+                if (!special) {
                     const float hs = __uint_as_float(sbyte << 23);
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
@@ -942,6 +920,7 @@ __global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg,
 
 // -------------------------------------------------------------- combine ---
 
+
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     const uint32_t u = __float_as_uint(f);
     if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) & 0x8000u) | 0x7FC0u;
@@ -971,10 +950,10 @@ __device__ __forceinline__ void load_slots(const V* p, int t, int K, int k0, V f
 // waves run at a time).  Otherwise they are read as vector loads, one slot
 // after another (the gated combine).  With MANY the slots are taken in groups
 // of KT, each group's rows loaded together, the accumulators carried over.
-template <int KT, bool UNIT, bool SCALAR, bool MANY>
+template <int KT, bool UNIT, bool SCALAR, bool MANY, bool COHERENT = false>
 __device__ __forceinline__ int combine_compute(const CombineArgs& a, int t, int seg, int lane,
-                                               u32x4 (&out)[EP_COMBINE_UNROLL]) {
-    constexpr int U = EP_COMBINE_UNROLL;
+                                               u32x4 (&out)[kCombineChunks]) {
+    constexpr int U = kCombineChunks;
     const int n16 = a.H / 8;
     const u32x4* eo = (const u32x4*)a.expert_out;
     const int c0 = seg * (kWave * U) + lane;
@@ -1013,7 +992,16 @@ __device__ __forceinline__ int combine_compute(const CombineArgs& a, int t, int 
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int c = c0 + u * kWave;
-                if (c < n16) v[k][u] = load_v<EP_COMBINE_NT_LOADS>(src + c);
+                if (c >= n16) continue;
+                if constexpr (COHERENT) {
+                    // device-scope load: reads what another XCD's producer made
+                    // visible, without an invalidation of this XCD's caches
+                    __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                        (void*)src, (short)0, a.H * 2, 0x00020000);
+                    v[k][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, c * 16, 0, kAuxDevice);
+                } else {
+                    v[k][u] = load_v<true>(src + c);
+                }
             }
         }
 #pragma unroll
@@ -1043,15 +1031,15 @@ __device__ __forceinline__ int combine_compute(const CombineArgs& a, int t, int 
 
 // Stores of one combine work item's outputs (row t of y, segment seg).
 __device__ __forceinline__ void combine_store(const CombineArgs& a, int t, int seg, int lane,
-                                              const u32x4 (&o)[EP_COMBINE_UNROLL]) {
-    constexpr int U = EP_COMBINE_UNROLL;
+                                              const u32x4 (&o)[kCombineChunks]) {
+    constexpr int U = kCombineChunks;
     const int n16 = a.H / 8;
     const int c0 = seg * (kWave * U) + lane;
     u32x4* dst = (u32x4*)a.y + (int64_t)t * n16;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int c = c0 + u * kWave;
-        if (c < n16) store_row<EP_COMBINE_STORE>(dst, a.H * 2, c, o[u]);
+        if (c < n16) store_row<kStoreNonTemporal>(dst, a.H * 2, c, o[u]);
     }
 }
 
@@ -1064,25 +1052,12 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a, int nseg, int ip
     for (int it = i0 + w; it < i1; it += 4) {
         const int t = it / nseg;
         const int seg = it - t * nseg;
-        u32x4 o[EP_COMBINE_UNROLL];
+        u32x4 o[kCombineChunks];
         combine_compute<KT, UNIT, true, MANY>(a, t, seg, lane, o);
         combine_store(a, t, seg, lane, o);
     }
 }
 
-#ifndef EP_GATE_TOKENS
-#define EP_GATE_TOKENS 16      // most tokens per workgroup of the gated combine (<= 64)
-#endif
-static_assert(EP_GATE_TOKENS >= 1 && EP_GATE_TOKENS <= 64, "one wave lane per gated token");
-#ifndef EP_GATE_WAVES
-#define EP_GATE_WAVES 16       // most waves per workgroup of the gated combine
-#endif
-#ifndef EP_GATE_DEFER
-#define EP_GATE_DEFER 4        // gated combine items computed before their stores are issued
-#endif
-#ifndef EP_GATE_STRIDED
-#define EP_GATE_STRIDED 1      // 1: a workgroup's tokens are strided by the grid size
-#endif
 
 // The items of a gated batch (token slot j < gtok, segment): wave w takes
 // items w, w + nw, ...  On gfx9 a wait for a load also waits for every store
@@ -1092,16 +1067,16 @@ static_assert(EP_GATE_TOKENS >= 1 && EP_GATE_TOKENS <= 64, "one wave lane per ga
 // measured slower, so those batches use D = 1, and read a token's slots in
 // one batch through the scalar unit, which measured faster there (and slower
 // for dense batches, as in the plain combine at full occupancy).
-template <int KT, int D, bool MANY>
+template <int KT, int D, bool MANY, bool COHERENT>
 __device__ __forceinline__ void gated_items(const CombineArgs& a, int nseg, int gtok, uint64_t mask,
                                             int w, int nw, int lane) {
     const int b = (int)blockIdx.x, nb = (int)gridDim.x;
     auto token_of = [&](int j) {
-        return EP_GATE_STRIDED ? b + j * nb : b * gtok + j;
+        return b + j * nb;
     };
     const int nit = gtok * nseg;
     for (int i0 = w; i0 < nit; i0 += D * nw) {
-        u32x4 o[D][EP_COMBINE_UNROLL];
+        u32x4 o[D][kCombineChunks];
         int tt[D], sg[D];
 #pragma unroll
         for (int d = 0; d < D; ++d) {
@@ -1111,7 +1086,7 @@ __device__ __forceinline__ void gated_items(const CombineArgs& a, int nseg, int 
             if (i < nit && token_of(j) < a.T && ((mask >> j) & 1ull)) {
                 tt[d] = token_of(j);
                 sg[d] = i - j * nseg;
-                combine_compute<KT, false, D == 1, MANY>(a, tt[d], sg[d], lane, o[d]);
+                combine_compute<KT, false, D == 1, MANY, COHERENT>(a, tt[d], sg[d], lane, o[d]);
             }
         }
 #pragma unroll
@@ -1121,7 +1096,7 @@ __device__ __forceinline__ void gated_items(const CombineArgs& a, int nseg, int 
 }
 
 // Per-token gate (StreamEP README, y_done_per_token).  A workgroup takes
-// EP_GATE_TOKENS tokens, strided by the grid size so that the workgroups in
+// kGateTokens tokens, strided by the grid size so that the workgroups in
 // flight cover a compact window of tokens (their expert rows are then close
 // together in each expert's block, as in the plain combine); one acquire per
 // workgroup keeps the cache invalidations few.  Wave 0 waits, one lane per token, until
@@ -1132,7 +1107,7 @@ __device__ __forceinline__ void gated_items(const CombineArgs& a, int nseg, int 
 // (error bit 2), it gives up, sets bit 2, and the batch's tokens that were
 // not done are skipped (their y rows keep their contents).
 template <int KT, bool MANY>
-__global__ __launch_bounds__(64 * EP_GATE_WAVES) void k_combine_gated(CombineArgs a, int nseg, int gtok) {
+__global__ __launch_bounds__(64 * kGateWaves) void k_combine_gated(CombineArgs a, int nseg, int gtok) {
     __shared__ uint64_t s_done;
     __shared__ int s_dense;
     const int lane = threadIdx.x & (kWave - 1);
@@ -1142,7 +1117,7 @@ __global__ __launch_bounds__(64 * EP_GATE_WAVES) void k_combine_gated(CombineArg
     // batch slot j < gtok holds token b + j * nb (strided: the workgroups in
     // flight cover a compact window of tokens) or b * gtok + j
     auto token_of = [&](int j) {
-        return EP_GATE_STRIDED ? b + j * nb : b * gtok + j;
+        return b + j * nb;
     };
     if (w == 0) {
         const int t = token_of(lane);
@@ -1184,23 +1159,25 @@ __global__ __launch_bounds__(64 * EP_GATE_WAVES) void k_combine_gated(CombineArg
                 }
             }
         }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        // A dense batch acquires the producers' releases for the whole
+        // workgroup (one cache invalidation per batch); a sparse batch reads
+        // its few rows with device-scope loads instead, so workgroups do not
+        // invalidate the caches the others are reading from.
+        const bool dense = rows >= 4 * toks;
+        if (dense) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         if (lane == 0) {
             s_done = mask;
-            s_dense = rows >= 4 * toks;
+            s_dense = dense;
         }
     }
     __syncthreads();
     const uint64_t mask = s_done;
-    if (s_dense) gated_items<KT, MANY ? 1 : EP_GATE_DEFER, MANY>(a, nseg, gtok, mask, w, nw, lane);
-    else gated_items<KT, 1, MANY>(a, nseg, gtok, mask, w, nw, lane);
+    if (s_dense) gated_items<KT, MANY ? 1 : kGateDefer, MANY, false>(a, nseg, gtok, mask, w, nw, lane);
+    else gated_items<KT, 1, MANY, true>(a, nseg, gtok, mask, w, nw, lane);
 }
 
 // ----------------------------------------------------- combine backward ---
 
-#ifndef EP_BWD_UNROLL
-#define EP_BWD_UNROLL 2        // 16-byte chunks per lane in flight in combine backward
-#endif
 
 // Backward of the combine, one wave per token: grad_y[t] is read once (once
 // per slot group with MANY); for each unmasked slot the gradient row
@@ -1210,7 +1187,7 @@ __global__ __launch_bounds__(64 * EP_GATE_WAVES) void k_combine_gated(CombineArg
 // float.
 template <int KT, bool MANY>
 __global__ __launch_bounds__(256) void k_combine_bwd(CombineBwdArgs a) {
-    constexpr int U = EP_BWD_UNROLL;
+    constexpr int U = kBwdChunks;
     const int lane = threadIdx.x & (kWave - 1);
     const int w = uniform_i(threadIdx.x / kWave);
     const int t = (int)blockIdx.x * 4 + w;
@@ -1246,7 +1223,7 @@ __global__ __launch_bounds__(256) void k_combine_bwd(CombineBwdArgs a) {
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int c = c0 + u * kWave;
-                    if (c < n16) o[u] = load_v<EP_COMBINE_NT_LOADS>(eo + (int64_t)rows[k] * n16 + c);
+                    if (c < n16) o[u] = load_v<true>(eo + (int64_t)rows[k] * n16 + c);
                 }
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
@@ -1263,7 +1240,7 @@ __global__ __launch_bounds__(256) void k_combine_bwd(CombineBwdArgs a) {
                         acc[k] = __builtin_fma((double)g0, (double)o0, acc[k]);
                         acc[k] = __builtin_fma((double)g1, (double)o1, acc[k]);
                     }
-                    store_row<EP_DISPATCH_STORE>(geo + (int64_t)rows[k] * n16, a.H * 2, c, q);
+                    store_row<kStoreDeviceNonTemporal>(geo + (int64_t)rows[k] * n16, a.H * 2, c, q);
                 }
             }
         }
@@ -1305,15 +1282,6 @@ __device__ __forceinline__ uint32_t e4m3_to_bf16_fast(uint32_t code, int e) {
 
 // ---------------------------------------------------- FP8 decode helpers ---
 
-#ifndef EP_CAST_LDS
-#define EP_CAST_LDS 32768      // unused LDS per cast-back workgroup for power-of-two scales
-#endif
-#ifndef EP_CAST_LDS_MIN_GRID
-#define EP_CAST_LDS_MIN_GRID 16384  // ... on grids of at least this many workgroups
-#endif
-#ifndef EP_CAST_UNROLL
-#define EP_CAST_UNROLL 2       // 16-channel units per lane per cast-back work item
-#endif
 
 // Exact float32 value of an e4m3fn code magnitude (0..0x7E).
 __device__ __forceinline__ float e4m3_value_f32(uint32_t mag) {
@@ -1473,10 +1441,10 @@ __global__ __launch_bounds__(256) void k_tile_consume(ConsumeArgs a) {
 // per_token_cast_back (instagit DeepEP low-latency page, example usage):
 // bf16 rows from e4m3fn codes and their per-128-channel scales in any of the
 // dispatch's flavours and layouts.  One work item is one wave over up to
-// 64 * EP_CAST_UNROLL units of 16 channels of one row: 16 bytes of codes in,
+// 64 * kCastUnits units of 16 channels of one row: 16 bytes of codes in,
 // 32 bytes of bf16 out per unit, the group's scale read once per unit.
 __global__ __launch_bounds__(256) void k_cast_back(CastBackArgs a, int nseg) {
-    constexpr int U = EP_CAST_UNROLL;
+    constexpr int U = kCastUnits;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t items = a.rows * nseg;
     for (int64_t it = (int64_t)blockIdx.x * 4 + (threadIdx.x / kWave); it < items;
@@ -1552,30 +1520,30 @@ __global__ __launch_bounds__(256) void k_cast_back(CastBackArgs a, int nseg) {
                     else { o1[2 * (i - 2)] = lo; o1[2 * (i - 2) + 1] = hi; }
                 }
             }
-            store_row<EP_COMBINE_STORE>(dst, a.H * 2, 2 * c, o0);
-            store_row<EP_COMBINE_STORE>(dst, a.H * 2, 2 * c + 1, o1);
+            store_row<kStoreNonTemporal>(dst, a.H * 2, 2 * c, o0);
+            store_row<kStoreNonTemporal>(dst, a.H * 2, 2 * c + 1, o1);
         }
     }
 }
 
 // ------------------------------------------------------------- launchers ---
 
-// Items per workgroup: 4 waves x EP_ITEMS_PER_WAVE, or whole tokens when streaming.
+// Items per workgroup: one per wave of 4, or the streaming chunk's whole tokens.
 inline int items_per_block(int nseg, bool stream) {
-    return stream ? EP_STREAM_TOKENS * nseg : 4 * EP_ITEMS_PER_WAVE;
+    return stream ? kStreamTokens * nseg : 4;
 }
 
 template <int KT, bool MANY>
 hipError_t dispatch_kt(const DispatchArgs& a, bool fp8, bool stream, hipStream_t st) {
-    constexpr int FU = EP_FP8_UNROLL, FS = EP_FP8_STREAM_UNROLL;
+    constexpr int FU = kFp8Units, FS = kFp8StreamUnits;
     const int fu = stream ? FS : FU;
-    const int per_seg = fp8 ? kWave * fu * 16 : kWave * EP_DISPATCH_UNROLL * 8;  // channels
+    const int per_seg = fp8 ? kWave * fu * 16 : kWave * kDispatchChunks * 8;  // channels
     const int nseg = (a.H + per_seg - 1) / per_seg;
     const int ipb = items_per_block(nseg, stream);
     const int64_t items = (int64_t)a.T * nseg;
     int grid = (int)((items + ipb - 1) / ipb);
     const size_t lds = 0;
-    const dim3 block(stream ? EP_STREAM_THREADS : 256);
+    const dim3 block(stream ? kStreamThreads : 256);
     if (fp8) {
         const bool f32q = a.scale_kind == kScaleF32;
         if (stream && f32q)
@@ -1597,22 +1565,22 @@ hipError_t dispatch_kt(const DispatchArgs& a, bool fp8, bool stream, hipStream_t
 
 template <int KT, bool UNIT, bool GATE, bool MANY>
 hipError_t combine_kt(const CombineArgs& a, hipStream_t st) {
-    const int per_seg = kWave * EP_COMBINE_UNROLL * 8;
+    const int per_seg = kWave * kCombineChunks * 8;
     const int nseg = (a.H + per_seg - 1) / per_seg;
     if constexpr (GATE) {
         // Tokens per workgroup.  Dense routing (or density not reported yet):
-        // halved until every wave has at most EP_GATE_DEFER items, so that
+        // halved until every wave has at most kGateDefer items, so that
         // each wave issues its stores in one batch (prefill's 7 segments per
         // token: 16 -> 8 tokens, 371 -> 355 us; at 4 segments 16 tokens
         // already fit, and halving only adds polls and acquires).  Sparse
         // batches keep 16 (fewer measured slower).  Then fewer when the batch
         // would not give every compute unit two workgroups; no more waves
         // than the batch has items.
-        int gtok = EP_GATE_TOKENS;
+        int gtok = a.density == kDensitySparse ? kGateTokens : kGateTokens;
         if (a.density != kDensitySparse)
-            while (gtok > 1 && gtok * nseg > EP_GATE_WAVES * EP_GATE_DEFER) gtok >>= 1;
+            while (gtok > 1 && gtok * nseg > kGateWaves * kGateDefer) gtok >>= 1;
         while (gtok > 1 && (a.T + gtok - 1) / gtok < 2 * a.num_cu) gtok >>= 1;
-        const int gw = gtok * nseg < EP_GATE_WAVES ? gtok * nseg : EP_GATE_WAVES;
+        const int gw = gtok * nseg < kGateWaves ? gtok * nseg : kGateWaves;
         const int grid = (a.T + gtok - 1) / gtok;
         hipLaunchKernelGGL((k_combine_gated<KT, MANY>), dim3(grid), dim3(64 * gw), 0, st, a, nseg, gtok);
         return hipGetLastError();
@@ -1630,8 +1598,8 @@ hipError_t combine_kt(const CombineArgs& a, hipStream_t st) {
     // The density is the one the last completed layout on the handle
     // reported; before any has, the dense shape is taken, where a wrong guess
     // costs least.
-    const bool resident = items <= (int64_t)a.num_cu * EP_COMBINE_RESIDENT_WAVES;
-    const size_t lds = (resident || a.density == kDensitySparse) ? 0 : EP_COMBINE_DENSE_LDS;
+    const bool resident = items <= (int64_t)a.num_cu * kCombineResidentWaves;
+    const size_t lds = (resident || a.density == kDensitySparse) ? 0 : kCombineDenseLds;
     hipLaunchKernelGGL((k_combine<KT, UNIT, MANY>), dim3(grid), dim3(256), lds, st, a, nseg, ipb);
     return hipGetLastError();
 }
@@ -1712,7 +1680,7 @@ hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t stream) {
 hipError_t launch_cast_back(const CastBackArgs& a, hipStream_t stream) {
     if (a.rows == 0) return hipSuccess;
     const int nunit = a.H / 16;
-    const int nseg = (nunit + kWave * EP_CAST_UNROLL - 1) / (kWave * EP_CAST_UNROLL);
+    const int nseg = (nunit + kWave * kCastUnits - 1) / (kWave * kCastUnits);
     const int64_t items = a.rows * nseg;
     int64_t grid = (items + 3) / 4;
     if (grid > (1 << 20)) grid = 1 << 20;          // grid-stride beyond a million workgroups
@@ -1723,7 +1691,7 @@ hipError_t launch_cast_back(const CastBackArgs& a, hipStream_t stream) {
     // rows at hidden 7168).  Small grids are
     // latency-bound and arbitrary float32 scales take the ALU-heavy software
     // decode; both keep every wave they can get.
-    const size_t lds = a.scale_kind != kScaleF32 && grid >= EP_CAST_LDS_MIN_GRID ? EP_CAST_LDS : 0;
+    const size_t lds = a.scale_kind != kScaleF32 && grid >= kCastLdsMinGrid ? kCastLds : 0;
     hipLaunchKernelGGL(k_cast_back, dim3((uint32_t)grid), dim3(256), lds, stream, a, nseg);
     return hipGetLastError();
 }
