@@ -349,6 +349,10 @@ def graph_bench(cfg, steps: int, warmup: int, per_replay: int = 4) -> dict:
     with torch.cuda.stream(s):
         eager = _time_us(step, steps, warmup, s)
         want = y.clone()
+        # a captured combine cannot wait for its layout's density report:
+        # fix its launch shape to the density the eager layouts reported
+        density = h.layout_density(s)
+        h.set_density_hint(density)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=s):
             for _ in range(per_replay):
@@ -371,6 +375,7 @@ def graph_bench(cfg, steps: int, warmup: int, per_replay: int = 4) -> dict:
                                    f"{cfg.routing} top-{K}, BLOCK_M {cfg.block_m}, "
                                    f"{'fp8' if fp8 else 'bf16'}" + (", tile_ready" if ready else ""),
                        "steps_per_replay": per_replay},
+            "combine_density_hint": {1: "sparse", 2: "dense"}.get(density, "auto"),
             "eager_us_per_step": round(eager, 2), "graph_us_per_step": round(replay, 2),
             "change_pct": round(100.0 * (replay - eager) / eager, 1),
             "graph_output_equals_eager": same}

@@ -69,8 +69,12 @@ EXPORTS = [
     "ep_array_bytes", "ep_copy_array", "ep_counts_to_host", "ep_handle_sync_status",
     "ep_tile_consume", "ep_status_string", "ep_borrow_release", "ep_combine_backward",
     "ep_dispatch_backward", "ep_combine_gated", "ep_fp8_cast_back", "ep_scale_ld",
-    "ep_layout_noalloc",
+    "ep_layout_noalloc", "ep_set_density_hint", "ep_layout_density",
 ]
+
+EP_DENSITY_AUTO = 0
+EP_DENSITY_SPARSE = 1
+EP_DENSITY_DENSE = 2
 
 
 class EpError(RuntimeError):
@@ -114,6 +118,8 @@ def _load() -> ctypes.CDLL:
         "ep_fp8_cast_back": (st, [P, P, U32, I64, I64, I32, P, P]),
         "ep_scale_ld": (I64, [P]),
         "ep_layout_noalloc": (st, [P, I32, I32, I32, I32, I64, P, P, P, P, P, P, P, P, P]),
+        "ep_set_density_hint": (st, [P, I32]),
+        "ep_layout_density": (I32, [P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -452,6 +458,14 @@ class EpHandle:
                                       nt.ctypes.data_as(ctypes.c_void_p), _stream(stream)),
                "ep_counts_to_host")
         return counts, int(nt[0])
+
+    def set_density_hint(self, hint: int) -> None:
+        """EP_DENSITY_AUTO / _SPARSE / _DENSE: launch shape of the combine calls."""
+        _check(_lib.ep_set_density_hint(self._h, int(hint)), "ep_set_density_hint")
+
+    def layout_density(self, stream=None) -> int:
+        """The density the current layout reported (EP_DENSITY_SPARSE / _DENSE)."""
+        return int(_lib.ep_layout_density(self._h, _stream(stream)))
 
     def sync_status(self, stream=None) -> int:
         return ep_handle_sync_status(self._h, stream)

@@ -5,7 +5,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#include <chrono>
 #include <new>
+#include <thread>
 
 #include "ep_layout.h"
 #include "ep_internal.h"
@@ -34,11 +36,13 @@ struct ep_handle {
     int32_t* ws;
     uint32_t* y_done;         // per-token done counts of the combine gate
     uint64_t* tile_stamp;     // consumer acquire stamps (EP_CONSUME_STAMPS)
-    // routing density of the last completed layout (epk::Density), written by
-    // the layout kernel into pinned host memory and read by ep_combine for
-    // its launch shape; density_dev is the device's address of the word
-    int32_t* density_host;
-    int32_t* density_dev;
+    // routing density (epk::Density) of a layout, tagged with its epoch
+    // (epoch << 32 | density), written by the layout kernel into pinned host
+    // memory and read by the combine calls for their launch shape;
+    // density_dev is the device's address of the word
+    uint64_t* density_host;
+    uint64_t* density_dev;
+    int32_t density_hint;     // EP_DENSITY_* set by ep_set_density_hint
     // host state of the current layout
     int32_t T;                // tokens of the current layout, -1 before the first
     uint32_t epoch;
@@ -93,6 +97,44 @@ ep_status check_config(const ep_config* c) {
 }
 
 ep_status hip_status(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP; }
+
+// Longest a combine call waits on the host for its layout's density word.
+constexpr auto kDensityWait = std::chrono::milliseconds(200);
+
+// Routing density of the handle's current layout, for the launch shape of
+// the plain combine and the dispatch backward.  The layout kernel stores it,
+// tagged with its epoch, as soon as its total is known; when that store has
+// not arrived yet the call waits for it on the host (for the layout kernel
+// only, not for the rest of the stream), so the shape follows the routing
+// and never the timing.  Under HIP graph capture nothing has run yet, and a
+// captured call takes the dense shape.  A layout that has not run after
+// kDensityWait (a stream held back by work the host has not enqueued yet)
+// also gets the dense shape.  Sizes whose shape does not depend on the
+// density do not wait.
+// The density report of the current layout, waiting up to kDensityWait;
+// kDensityUnknown when it does not arrive.
+int32_t reported_density(const ep_handle* h) {
+    const auto start = std::chrono::steady_clock::now();
+    for (;;) {
+        const uint64_t w = __atomic_load_n(h->density_host, __ATOMIC_ACQUIRE);
+        if ((uint32_t)(w >> 32) == h->epoch) return (int32_t)(uint32_t)w;
+        if (std::chrono::steady_clock::now() - start > kDensityWait) return epk::kDensityUnknown;
+        std::this_thread::yield();
+    }
+}
+
+int32_t current_density(const ep_handle* h, int32_t hidden, hipStream_t stream) {
+    if (h->density_hint == EP_DENSITY_SPARSE) return epk::kDensitySparse;
+    if (h->density_hint == EP_DENSITY_DENSE) return epk::kDensityDense;
+    if (!epk::combine_shape_uses_density(h->T, hidden, h->num_cu)) return epk::kDensityDense;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+        (void)hipGetLastError();
+        return epk::kDensityDense;
+    }
+    const int32_t d = reported_density(h);
+    return d == epk::kDensityUnknown ? epk::kDensityDense : d;
+}
 
 // Calls that rewrite the row map wait for the consumers of a released view.
 ep_status wait_lease(ep_handle* h, hipStream_t stream) {
@@ -192,7 +234,7 @@ ep_status ep_handle_create(const ep_config* cfg, ep_handle** out) {
         delete h;
         return EP_ERR_OUT_OF_MEMORY;
     }
-    __atomic_store_n(h->density_host, (int32_t)epk::kDensityUnknown, __ATOMIC_RELAXED);
+    __atomic_store_n(h->density_host, (uint64_t)epk::kDensityUnknown, __ATOMIC_RELAXED);
     if (hipHostGetDevicePointer((void**)&h->density_dev, h->density_host, 0) != hipSuccess ||
         !h->density_dev) {
         (void)hipHostFree(h->density_host);
@@ -203,6 +245,7 @@ ep_status ep_handle_create(const ep_config* cfg, ep_handle** out) {
     }
     h->lease = false;
     h->lease_wait = false;
+    h->density_hint = EP_DENSITY_AUTO;
     *out = h;
     return EP_OK;
 }
@@ -264,6 +307,7 @@ ep_status ep_layout(ep_handle* h, const int32_t* topk_idx, const float* topk_wei
     a.ws = h->ws;
     a.y_done = h->y_done;
     a.density = h->density_dev;
+    a.epoch = h->epoch + 1;
     ep_status st = hip_status(epk::launch_layout(a, stream));
     if (st != EP_OK) return st;
     h->T = num_tokens;
@@ -348,9 +392,7 @@ ep_status ep_combine(const ep_handle* h, uint32_t epoch, const void* expert_out,
     a.weights = h->weights;
     a.y = y;
     a.num_cu = h->num_cu;
-    // the density of the latest layout whose kernel has finished (the one
-    // just enqueued may not have run yet): it chooses the launch shape only
-    a.density = __atomic_load_n(h->density_host, __ATOMIC_RELAXED);
+    a.density = current_density(h, hidden, stream);     // launch shape only
     return hip_status(epk::launch_combine(a, stream));
 }
 
@@ -376,7 +418,6 @@ ep_status ep_combine_gated(const ep_handle* h, uint32_t epoch, const void* exper
     a.limit_ticks = (uint64_t)spin_limit_us * (uint64_t)h->wall_khz / 1000u;
     a.error = h->error;
     a.num_cu = h->num_cu;
-    a.density = __atomic_load_n(h->density_host, __ATOMIC_RELAXED);   // launch shape, as ep_combine
     return hip_status(epk::launch_combine_gated(a, stream));
 }
 
@@ -442,8 +483,22 @@ ep_status ep_dispatch_backward(const ep_handle* h, uint32_t epoch, const void* g
     a.weights = nullptr;
     a.y = grad_x;
     a.num_cu = h->num_cu;
-    a.density = __atomic_load_n(h->density_host, __ATOMIC_RELAXED);   // launch shape, as ep_combine
+    a.density = current_density(h, hidden, stream);     // launch shape, as ep_combine
     return hip_status(epk::launch_combine_unit(a, stream));
+}
+
+ep_status ep_set_density_hint(ep_handle* h, int32_t hint) {
+    if (!h || hint < EP_DENSITY_AUTO || hint > EP_DENSITY_DENSE) return EP_ERR_INVALID_ARGUMENT;
+    h->density_hint = hint;
+    return EP_OK;
+}
+
+int32_t ep_layout_density(ep_handle* h, hipStream_t stream) {
+    (void)stream;
+    if (!h || h->T < 0) return EP_DENSITY_AUTO;
+    const int32_t d = reported_density(h);
+    return d == epk::kDensitySparse ? EP_DENSITY_SPARSE
+         : d == epk::kDensityDense ? EP_DENSITY_DENSE : EP_DENSITY_AUTO;
 }
 
 ep_status ep_borrow_release(ep_handle* h, hipStream_t consumer_stream) {

@@ -37,7 +37,8 @@ struct LayoutArgs {
     uint32_t* error;            // [1]
     int32_t* ws;                // [blocks * E] per-workgroup expert counts
     uint32_t* y_done;           // [T] per-token done counts, zeroed here
-    int32_t* density;           // host-mapped word: kDensitySparse / kDensityDense
+    uint64_t* density;          // host-mapped word: epoch << 32 | Density (may be null)
+    uint32_t epoch;             // the epoch this layout starts
 };
 
 // Routing density of a layout, as the layout reports it for the next combine's
@@ -92,7 +93,7 @@ struct CombineArgs {
     uint64_t limit_ticks;
     uint32_t* error;
     int32_t num_cu;             // compute units of the device (launch shapes)
-    int32_t density;            // Density of the last layout that reported one (launch shape)
+    int32_t density;            // Density of the current layout (launch shape of the plain combine)
 };
 
 struct CombineBwdArgs {
@@ -148,6 +149,10 @@ hipError_t launch_cast_back(const CastBackArgs& a, hipStream_t stream);
 hipError_t launch_combine_unit(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_combine_bwd(const CombineBwdArgs& a, hipStream_t stream);
 hipError_t launch_consume(const ConsumeArgs& a, int workgroups, hipStream_t stream);
+// Whether the plain combine's (and the dispatch backward's) launch shape for
+// these sizes depends on the routing density (it does not for grids that are
+// resident at once, nor when there are no tokens).
+bool combine_shape_uses_density(int T, int H, int num_cu);
 
 // Workgroups the multi-workgroup layout path needs for S slots.
 inline int layout_blocks(int64_t S) {

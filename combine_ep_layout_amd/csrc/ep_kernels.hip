@@ -202,15 +202,17 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_count(LayoutArgs a) {
         a.ws[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
-// The layout's routing density for the next combine's launch shape: 4 or more
+// The layout's routing density, for its combine's launch shape: 4 or more
 // real rows per token on average is dense.  The word lives in pinned host
-// memory; the store is issued as early as the total is known, so that its
-// trip to the host overlaps the rest of the kernel.
+// memory and carries the layout's epoch, so the host can tell which layout
+// it belongs to; the store is issued as early as the total is known, so that
+// its trip to the host overlaps the rest of the kernel.
 __device__ __forceinline__ void report_density(const LayoutArgs& a, int rows) {
     if (!a.density) return;
     const int64_t T = a.S / a.K;
-    __hip_atomic_store(a.density, (int64_t)rows >= 4 * T ? (int32_t)kDensityDense : (int32_t)kDensitySparse,
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const uint32_t d = (int64_t)rows >= 4 * T ? (uint32_t)kDensityDense : (uint32_t)kDensitySparse;
+    __hip_atomic_store(a.density, ((uint64_t)a.epoch << 32) | d, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 // Layout ranks.  FUSED: the whole layout in this one workgroup (nb == 1, no
@@ -1568,17 +1570,15 @@ hipError_t combine_kt(const CombineArgs& a, hipStream_t st) {
     const int per_seg = kWave * kCombineChunks * 8;
     const int nseg = (a.H + per_seg - 1) / per_seg;
     if constexpr (GATE) {
-        // Tokens per workgroup.  Dense routing (or density not reported yet):
-        // halved until every wave has at most kGateDefer items, so that
-        // each wave issues its stores in one batch (prefill's 7 segments per
-        // token: 16 -> 8 tokens, 371 -> 355 us; at 4 segments 16 tokens
-        // already fit, and halving only adds polls and acquires).  Sparse
-        // batches keep 16 (fewer measured slower).  Then fewer when the batch
-        // would not give every compute unit two workgroups; no more waves
-        // than the batch has items.
-        int gtok = a.density == kDensitySparse ? kGateTokens : kGateTokens;
-        if (a.density != kDensitySparse)
-            while (gtok > 1 && gtok * nseg > kGateWaves * kGateDefer) gtok >>= 1;
+        // Tokens per workgroup: halved from kGateTokens until every wave has
+        // at most kGateDefer items, so that a dense batch issues its stores
+        // in one batch (prefill's 7 segments per token: 16 -> 8 tokens, 371 ->
+        // 355 us; at 3 or 4 segments 16 tokens already fit); then fewer when
+        // the batch would not give every compute unit two workgroups.  No
+        // more waves than the batch has items.  (Sizes only: a batch's
+        // density is decided inside the kernel.)
+        int gtok = kGateTokens;
+        while (gtok > 1 && gtok * nseg > kGateWaves * kGateDefer) gtok >>= 1;
         while (gtok > 1 && (a.T + gtok - 1) / gtok < 2 * a.num_cu) gtok >>= 1;
         const int gw = gtok * nseg < kGateWaves ? gtok * nseg : kGateWaves;
         const int grid = (a.T + gtok - 1) / gtok;
@@ -1595,9 +1595,7 @@ hipError_t combine_kt(const CombineArgs& a, hipStream_t st) {
     // issuing all its row loads at once, that was the fastest shape for it
     // (345 against 375 us at full occupancy, 16384 tokens x top-8), while
     // sparse routing is latency-bound and wants every wave (23 against 38 us).
-    // The density is the one the last completed layout on the handle
-    // reported; before any has, the dense shape is taken, where a wrong guess
-    // costs least.
+    // The density is the current layout's (the caller waits for it).
     const bool resident = items <= (int64_t)a.num_cu * kCombineResidentWaves;
     const size_t lds = (resident || a.density == kDensitySparse) ? 0 : kCombineDenseLds;
     hipLaunchKernelGGL((k_combine<KT, UNIT, MANY>), dim3(grid), dim3(256), lds, st, a, nseg, ipb);
@@ -1694,6 +1692,12 @@ hipError_t launch_cast_back(const CastBackArgs& a, hipStream_t stream) {
     const size_t lds = a.scale_kind != kScaleF32 && grid >= kCastLdsMinGrid ? kCastLds : 0;
     hipLaunchKernelGGL(k_cast_back, dim3((uint32_t)grid), dim3(256), lds, stream, a, nseg);
     return hipGetLastError();
+}
+
+bool combine_shape_uses_density(int T, int H, int num_cu) {
+    const int per_seg = kWave * kCombineChunks * 8;
+    const int64_t items = (int64_t)T * ((H + per_seg - 1) / per_seg);
+    return T > 0 && items > (int64_t)num_cu * kCombineResidentWaves;
 }
 
 hipError_t launch_consume(const ConsumeArgs& a, int workgroups, hipStream_t stream) {

@@ -226,12 +226,15 @@ ep_status ep_dispatch(ep_handle* h, const void* x, int32_t hidden, void* pool,
  *   y           device bf16 [num_tokens, hidden], fully written.
  * y[t,c] = bf16_rne( fp32 fma chain over k ascending of w[t,k] * o[row(t,k),c] )
  * starting from +0 and skipping masked slots; a token with no slot gets +0.
- * Launch shape: ep_layout reports whether its routing averages 4 or more real
- * rows per token into a word of pinned host memory that the handle owns; this
- * call (and ep_dispatch_backward) reads the word when it launches and runs
- * fewer waves per compute unit for dense routing.  The word holds the latest
- * layout whose kernel has finished, normally the current one; y is the same in
- * every shape, only the timing depends on it. */
+ * Launch shape: the layout kernel reports whether its routing averages 4 or
+ * more real rows per token, tagged with its epoch, into a word of pinned host
+ * memory that the handle owns; for batches too large to be resident at once
+ * this call (and ep_dispatch_backward) runs fewer waves per compute unit for
+ * dense routing.  It uses the current layout's word, and when the layout
+ * kernel has not stored it yet the call waits for that store on the host (for
+ * the layout kernel only, at most 200 ms; past that, or while the stream is
+ * being captured into a HIP graph, it takes the dense shape).  So the shape
+ * follows the routing, not the timing; y is the same in every shape. */
 ep_status ep_combine(const ep_handle* h, uint32_t epoch, const void* expert_out,
                      int32_t hidden, void* y, hipStream_t stream);
 
@@ -251,6 +254,23 @@ ep_status ep_combine(const ep_handle* h, uint32_t epoch, const void* expert_out,
 ep_status ep_combine_gated(const ep_handle* h, uint32_t epoch, const void* expert_out,
                            int32_t hidden, void* y, uint32_t round, uint32_t spin_limit_us,
                            hipStream_t stream);
+
+/* Launch-shape hint of ep_combine and ep_dispatch_backward.  EP_DENSITY_AUTO
+ * (the default) takes the current layout's reported density as described at
+ * ep_combine (waiting for it if needed; the dense shape under graph capture).
+ * EP_DENSITY_SPARSE or EP_DENSITY_DENSE fix the shape for the handle's later
+ * calls, which then never wait: for callers that capture the combine in a HIP
+ * graph, or know their routing.  Results never depend on the shape. */
+#define EP_DENSITY_AUTO   0
+#define EP_DENSITY_SPARSE 1     /* fewer than 4 real rows per token on average */
+#define EP_DENSITY_DENSE  2     /* 4 or more */
+ep_status ep_set_density_hint(ep_handle* h, int32_t hint);
+
+/* BLOCKING (on the layout kernel only, as ep_combine waits): the density the
+ * current layout reported, EP_DENSITY_SPARSE or EP_DENSITY_DENSE;
+ * EP_DENSITY_AUTO when the handle has no layout or the report did not arrive
+ * within 200 ms. */
+int32_t ep_layout_density(ep_handle* h, hipStream_t stream);
 
 /* per_token_cast_back ([FP8], example usage): bf16 rows from e4m3fn codes and
  * their scales, in any flavour and layout of the FP8 dispatch.

@@ -83,6 +83,10 @@ def test_new_entry_points_reject_before_any_hip_call():
     assert lib.ep_dispatch_backward(None, 1, None, 128, None, None) == INV
     assert lib.ep_tile_consume(None, 1, None, None, 128, 0, None, 1, 1000, None) == INV
     assert lib.ep_borrow_release(None, None) == INV
+    assert lib.ep_set_density_hint(None, 0) == INV
+    assert lib.ep_layout_density(None, None) == ep.EP_DENSITY_AUTO
+    assert lib.ep_set_density_hint(None, 0) == INV
+    assert lib.ep_layout_density(None, None) == ep.EP_DENSITY_AUTO
     assert lib.ep_scale_ld(None) == -1
     # the cast back needs no handle: every check happens on the host first
     assert lib.ep_fp8_cast_back(None, None, 0, 0, 0, 256, None, None) == ep.EP_OK      # no rows

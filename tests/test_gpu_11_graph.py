@@ -31,9 +31,14 @@ def _eager(cfg, d, eo_bits, fp8):
 
 
 @pytest.mark.parametrize("name,tokens,hidden,fp8", [("tiny", -1, -1, False), ("decode", -1, -1, True),
-                                                     ("stream", 3000, 512, False)])
+                                                     ("stream", 3000, 512, False),
+                                                     ("share", 4000, 1024, False)])
 def test_step_in_graph(name, tokens, hidden, fp8):
-    """(3000 stream tokens take the two-launch layout.)"""
+    """(3000 stream tokens take the two-launch layout; the share routing is
+    sparse, and its combine grid is not resident: before the capture the
+    handle's launch-shape hint is set to the density the warm-up layout
+    reported, which the test checks against the routing.)"""
+    import combine_ep_layout_amd as ep
     say(f"[graph] {name} tokens={tokens} hidden={hidden} fp8={fp8}")
     cfg = CONFIGS[name]
     if tokens >= 0:
@@ -68,6 +73,10 @@ def test_step_in_graph(name, tokens, hidden, fp8):
         y = h.combine(epoch, eo)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
+    d0 = generate(cfg, 0)
+    dense = (d0["topk_idx"] >= 0).sum() >= 4 * T
+    assert h.layout_density() == (ep.EP_DENSITY_DENSE if dense else ep.EP_DENSITY_SPARSE)
+    h.set_density_hint(h.layout_density())
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
         epoch = h.layout(idx, w)
