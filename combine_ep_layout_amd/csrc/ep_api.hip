@@ -48,6 +48,9 @@ struct ep_handle {
     uint32_t epoch;
     uint32_t seq;
     uint32_t round;           // TILE_READY dispatches since the layout
+    // graph capture of the current layout: 0 when it was enqueued eagerly,
+    // else the id of the capture it was recorded in
+    unsigned long long layout_capture;
     // borrowed-view lease
     bool lease;               // a borrowing dispatch's view is out
     bool lease_wait;          // the next call waits for lease_event first
@@ -136,6 +139,26 @@ int32_t current_density(const ep_handle* h, int32_t hidden, hipStream_t stream) 
     return d == epk::kDensityUnknown ? epk::kDensityDense : d;
 }
 
+// Id of the graph capture `stream` is in, 0 when it is not capturing.
+unsigned long long capture_id(hipStream_t stream) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    unsigned long long id = 0;
+    if (hipStreamGetCaptureInfo(stream, &cs, &id) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return cs == hipStreamCaptureStatusActive ? (id ? id : ~0ull) : 0;
+}
+
+// A streaming dispatch and a gated combine rely on counts that only the
+// layout resets (tile arrivals, per-token done counts).  Captured into a
+// graph without that layout, a replay would find the previous replay's
+// counts and stamps and its consumers could pass early: refuse it.
+bool capture_without_layout(const ep_handle* h, hipStream_t stream) {
+    const unsigned long long id = capture_id(stream);
+    return id != 0 && id != h->layout_capture;
+}
+
 // Calls that rewrite the row map wait for the consumers of a released view.
 ep_status wait_lease(ep_handle* h, hipStream_t stream) {
     if (!h->lease_wait) return EP_OK;
@@ -177,6 +200,7 @@ ep_status ep_handle_create(const ep_config* cfg, ep_handle** out) {
     h->max_tiles = (int32_t)(h->cap / BM);
     h->ws_blocks = epk::layout_blocks(h->max_slots);
     h->T = -1;
+    h->layout_capture = 0;
     h->epoch = 0;
     h->seq = 0;
     h->round = 0;
@@ -310,6 +334,7 @@ ep_status ep_layout(ep_handle* h, const int32_t* topk_idx, const float* topk_wei
     a.epoch = h->epoch + 1;
     ep_status st = hip_status(epk::launch_layout(a, stream));
     if (st != EP_OK) return st;
+    h->layout_capture = capture_id(stream);
     h->T = num_tokens;
     h->epoch += 1;
     h->round = 0;
@@ -345,6 +370,7 @@ ep_status ep_dispatch(ep_handle* h, const void* x, int32_t hidden, void* pool,
     if (h->T < 0 || h->lease) return EP_ERR_HANDLE_STATE;
     if (h->T > 0 && (!x || !pool || !aligned16(x) || !aligned16(pool)))
         return EP_ERR_INVALID_ARGUMENT;
+    if (ready && capture_without_layout(h, stream)) return EP_ERR_UNSUPPORTED;
     ep_status ws = wait_lease(h, stream);
     if (ws != EP_OK) return ws;
     epk::DispatchArgs a{};
@@ -405,6 +431,7 @@ ep_status ep_combine_gated(const ep_handle* h, uint32_t epoch, const void* exper
     if (h->T < 0 || epoch != h->epoch || h->lease) return EP_ERR_HANDLE_STATE;
     if (h->T > 0 && (!expert_out || !y || !aligned16(expert_out) || !aligned16(y)))
         return EP_ERR_INVALID_ARGUMENT;
+    if (capture_without_layout(h, stream)) return EP_ERR_UNSUPPORTED;
     epk::CombineArgs a{};
     a.expert_out = expert_out;
     a.T = h->T;

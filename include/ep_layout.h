@@ -59,9 +59,12 @@
  *     tile_ready with the captured base (the sequence number before the
  *     captured dispatches), so a streaming dispatch and its consumer captured
  *     after the layout wait for that replay's stamps, not the last replay's.
- *     A streaming dispatch replayed without its layout would repeat the last
- *     replay's stamp, and its consumer could pass early.  The BLOCKING calls
- *     and ep_borrow_release (which records an event) are not for capture.
+ *     A streaming dispatch or a gated combine captured without its layout
+ *     would find the last replay's stamps and counts, and its consumers could
+ *     pass early: such calls return EP_ERR_UNSUPPORTED when the stream is
+ *     capturing and the handle's current layout was not recorded in the same
+ *     capture.  The BLOCKING calls and ep_borrow_release (which records an
+ *     event) are not for capture.
  */
 #ifndef EP_LAYOUT_H
 #define EP_LAYOUT_H

@@ -164,3 +164,54 @@ def test_streaming_dispatch_and_consumer_in_graph():
         say(f"  replay {rep}: consumer rows match")
     del g
     h.close()
+
+
+def test_capture_without_layout_is_refused():
+    """A streaming dispatch or a gated combine recorded into a graph whose
+    capture does not also hold the handle's layout is refused (a replay would
+    find the previous replay's arrival and done counts); a plain dispatch is
+    accepted, and so is a streaming dispatch captured after its layout."""
+    import ctypes
+    import combine_ep_layout_amd as ep
+    say("[graph] streaming dispatch / gated combine captured without their layout")
+    lib = ep.library()
+    cfg = CONFIGS["stream"].replace(tokens=600, hidden=512)
+    d = generate(cfg, 0)
+    H = cfg.hidden
+    h = new_handle(cfg)
+    idx = torch.from_numpy(d["topk_idx"]).to(dev())
+    w = torch.from_numpy(d["topk_weights"]).to(dev())
+    x = to_dev_bf16(d["x"])
+    pool, scales = h.new_pool(H, fp8=True)
+    eo = torch.zeros(h.capacity_rows, H, dtype=torch.bfloat16, device=dev())
+    y = torch.empty(cfg.tokens, H, dtype=torch.bfloat16, device=dev())
+    s = torch.cuda.Stream()                              # default priority
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        epoch = h.layout(idx, w)                         # eager layout
+        h.dispatch(x, pool, scales, fp8=True, tile_ready=True)
+    torch.cuda.synchronize()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    sp = ctypes.c_void_p(s.cuda_stream)
+    fp8, ready = ep.EP_DISPATCH_FP8, ep.EP_DISPATCH_TILE_READY
+    codes = {}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        codes["streaming"] = lib.ep_dispatch(h.raw, P(x), H, P(pool), P(scales), fp8 | ready, sp, None)
+        codes["gated"] = lib.ep_combine_gated(h.raw, epoch, P(eo), H, P(y), 1, 1000, sp)
+        codes["plain"] = lib.ep_dispatch(h.raw, P(x), H, P(pool), P(scales), fp8, sp, None)
+    assert codes["streaming"] == ep.EP_ERR_UNSUPPORTED, codes
+    assert codes["gated"] == ep.EP_ERR_UNSUPPORTED, codes
+    assert codes["plain"] == ep.EP_OK, codes
+    g.replay()
+    torch.cuda.synchronize()
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2, stream=s):
+        h.layout(idx, w)
+        h.dispatch(x, pool, scales, fp8=True, tile_ready=True)
+    for _ in range(2):
+        g2.replay()
+        torch.cuda.synchronize()
+    assert h.sync_status() == ep.EP_OK
+    del g, g2
+    h.close()
