@@ -73,6 +73,8 @@ def kernel_source_sha() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "combine_ep_layout_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
+        if name == "ep_ceiling.hip":                    # the bandwidth probes, not the path
+            continue
         with open(os.path.join(csrc, name), encoding="utf-8") as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -381,14 +383,15 @@ def graph_bench(cfg, steps: int, warmup: int, per_replay: int = 4) -> dict:
             "graph_output_equals_eager": same}
 
 
-def gate_bench(cfg, steps: int, warmup: int) -> dict:
+def gate_bench(cfg, steps: int, warmup: int, serial: bool = False) -> dict:
     """Per-token combine gate.  (1) The gate's own cost: the gated combine
     with every token already done vs the plain combine.  (2) A forward pass
     layout -> dispatch (tile_ready) -> expert-output producer (the tile
     consumer stand-in, copying each tile to expert_out and signalling its
     tokens) -> combine, once in order on one stream with the plain combine,
     once with the producer on a second stream overlapping the dispatch and
-    the gated combine on a third overlapping the producer."""
+    the gated combine on a third overlapping the producer.  With `serial`
+    (for counter passes, which run one kernel at a time) only (1) runs."""
     import torch
     import combine_ep_layout_amd as ep
     from synth import generate
@@ -440,14 +443,20 @@ def gate_bench(cfg, steps: int, warmup: int) -> dict:
         sa.wait_event(e2)
         sa.wait_event(e3)
 
-    t_order = _time_us(in_order, steps, warmup, sa)
-    t_over = _time_us(overlapped, steps, warmup, sa)
-    t_order2 = _time_us(in_order, steps, warmup, sa)
-    t_over2 = _time_us(overlapped, steps, warmup, sa)
+    if serial:
+        t_order = t_over = t_order2 = t_over2 = float("nan")
+    else:
+        t_order = _time_us(in_order, steps, warmup, sa)
+        t_over = _time_us(overlapped, steps, warmup, sa)
+        t_order2 = _time_us(in_order, steps, warmup, sa)
+        t_over2 = _time_us(overlapped, steps, warmup, sa)
     assert h.sync_status() == ep.EP_OK
     h.close()
     n_a = int((d["topk_idx"] >= 0).sum())
     comb_bytes = 8 * T * K + 2 * H * n_a + 2 * H * T
+    if serial:
+        return {"metric": "gated combine with every token done (serial run)", "unit": "us",
+                "combine_us": round(plain, 2), "combine_gated_all_done_us": round(gated, 2)}
     return {"metric": "per-token combine gate: gate cost and forward pass with overlap",
             "unit": "us", "higher_is_better": False, "data": "synthetic", "dtype": "bf16",
             "config": {"workload": f"{cfg.name}: {T} tokens, hidden {H}, {cfg.num_experts} experts "
@@ -636,26 +645,113 @@ def overlap_bench(cfg, steps: int, warmup: int, workgroups: int = 256) -> dict:
             "layout_dispatch_consumer_two_streams_us": round(t_over, 2)}
 
 
-def ceiling_bench(steps: int, warmup: int) -> dict:
-    """Context for the roofline: what plain torch kernels stream on this GPU
-    (a 2 GiB fill, a 2 GiB read-reduce, a 2 GiB -> 2 GiB copy).  These are
-    measured ceilings of simple HBM-bound kernels, not the nameplate peak."""
+def ceiling_bench(cfg, steps: int, warmup: int) -> dict:
+    """Context for the roofline: what simple HBM-bound kernels reach on this
+    GPU, measured with the probe library (libep_ceiling.so: rows of 2*hidden
+    bytes moved in 16-byte accesses by one wave per row, "@1w", or by a
+    256-thread workgroup per row, "@4w"), on the workload's own row size and
+    row count N_a (every routed slot's row once):
+
+      flat_write*       the same bytes as one flat array, every thread striding
+                        over it (non-temporal or plain stores)
+      seq_*             rows 0..N_a-1 in order (write, plain-store write, read,
+                        copy)
+      dispatch_order_*  the pool rows of the workload's layout in slot order,
+                        as dispatch writes them and combine reads them
+      pool_order_write  the same rows sorted by pool row
+      random_write      the same rows in a seeded random order
+
+    beside the library's own dispatch (bf16) and combine on the same layout,
+    and torch's fill_ / copy_ over 2 GiB.  These are measured ceilings of
+    plain kernels, not the nameplate peak."""
+    import ctypes
     import torch
+    import combine_ep_layout_amd as ep
+    from synth import generate
+    lib = ctypes.CDLL(os.path.join(ROOT, "combine_ep_layout_amd", "libep_ceiling.so"))
+    lib.ep_ceiling_rows.restype = ctypes.c_int
+    lib.ep_ceiling_rows.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                    ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                    ctypes.c_void_p]
     dev = torch.device("cuda", 0)
     stream = torch.cuda.current_stream()
+    d = generate(cfg, 0)
+    T, K, H = cfg.tokens, cfg.top_k, cfg.hidden
+    idx = torch.from_numpy(d["topk_idx"]).to(dev)
+    w = torch.from_numpy(d["topk_weights"]).to(dev)
+    x = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    h = ep.EpHandle(T, K, cfg.num_experts, cfg.block_m)
+    cap = h.capacity_rows
+    epoch = h.layout(idx, w)
+    s2r = h.array("slot_to_pool_row").cpu().numpy().reshape(-1)
+    rows_slot = s2r[s2r >= 0].astype(np.int32)
+    n_a = len(rows_slot)
+    row_bytes = 2 * H
+    perm = np.random.default_rng(0).permutation(n_a)
+    orders = {"seq": np.arange(n_a, dtype=np.int32), "dispatch_order": rows_slot,
+              "pool_order": np.sort(rows_slot), "random": rows_slot[perm]}
+    orders = {k: torch.from_numpy(v).to(dev) for k, v in orders.items()}
+    pool = torch.empty(cap, H, dtype=torch.bfloat16, device=dev)
+    pool.fill_(1.0)
+    src = torch.ones(n_a, H, dtype=torch.bfloat16, device=dev)
+    sink = torch.zeros(n_a, dtype=torch.int32, device=dev)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    W, WD, R, C, WP, F, FP = 0, 1, 2, 3, 4, 5, 6
+
+    def probe(op, wpr, rows, n_dst, dst=None, source=None):
+        def fn():
+            rc = lib.ep_ceiling_rows(op, wpr, None if dst is None else P(dst),
+                                     None if source is None else P(source), n_dst, row_bytes,
+                                     P(rows), n_a, P(sink), sp)
+            if rc != 0:
+                raise RuntimeError(f"ep_ceiling_rows returned {rc}")
+        return fn
+
+    nb = row_bytes * n_a
+    legs = {"flat_write": (probe(F, 1, orders["seq"], n_a, dst=src), nb),
+            "flat_write_plain": (probe(FP, 1, orders["seq"], n_a, dst=src), nb)}
+    for wpr in (1, 4):
+        for name, fn, nbytes in (
+                ("seq_write", probe(W, wpr, orders["seq"], n_a, dst=src), nb),
+                ("seq_write_plain", probe(WP, wpr, orders["seq"], n_a, dst=src), nb),
+                ("seq_read", probe(R, wpr, orders["seq"], n_a, source=src), nb),
+                ("seq_copy", probe(C, wpr, orders["seq"], cap, dst=pool, source=src), 2 * nb),
+                ("dispatch_order_write", probe(W, wpr, orders["dispatch_order"], cap, dst=pool), nb),
+                ("dispatch_order_write_device_scope",
+                 probe(WD, wpr, orders["dispatch_order"], cap, dst=pool), nb),
+                ("pool_order_write", probe(W, wpr, orders["pool_order"], cap, dst=pool), nb),
+                ("random_write", probe(W, wpr, orders["random"], cap, dst=pool), nb),
+                ("dispatch_order_read", probe(R, wpr, orders["dispatch_order"], cap, source=pool), nb)):
+            legs[f"{name}@{wpr}w"] = (fn, nbytes)
+    ab = algorithmic_bytes(cfg, d["topk_idx"], h.array("expert_counts").cpu().numpy(), False)
+    lp, _ = h.new_pool(H)
+    y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    legs["library_dispatch_bf16"] = (lambda: h.dispatch(x, lp, None), ab["dispatch"])
+    legs["library_combine"] = (lambda: h.combine(epoch, pool, y), ab["combine"])
+    res = {}
+    for name, (fn, nbytes) in legs.items():
+        t = min(_time_us(fn, steps, warmup, stream) for _ in range(2))
+        res[name] = {"us": round(t, 1), "GB_s": round(nbytes / (t * 1e-6) / 1e9, 1),
+                     "frac_of_8TBs": round(nbytes / (t * 1e-6) / 1e9 / PEAK_GBS, 4)}
+    assert h.sync_status() == ep.EP_OK
+    h.close()
+    del pool, src, lp
     n = 1 << 29                                          # 2 GiB of float32
     a = torch.ones(n, dtype=torch.float32, device=dev)
     b = torch.empty_like(a)
-    res = {}
-    for name, fn, nbytes in (("write", lambda: b.fill_(3.0), 4 * n),
-                             ("read", lambda: torch.amax(a), 4 * n),
-                             ("copy", lambda: b.copy_(a), 8 * n)):
+    for name, fn, nbytes in (("torch_fill", lambda: b.fill_(3.0), 4 * n),
+                             ("torch_copy", lambda: b.copy_(a), 8 * n)):
         t = min(_time_us(fn, steps, warmup, stream) for _ in range(2))
         res[name] = {"us": round(t, 1), "GB_s": round(nbytes / (t * 1e-6) / 1e9, 1),
                      "frac_of_8TBs": round(nbytes / (t * 1e-6) / 1e9 / PEAK_GBS, 4)}
     del a, b
-    return {"metric": "HBM bandwidth of plain torch kernels (context for the roofline)",
-            "unit": "GB/s", "data": "synthetic", "results": res}
+    return {"metric": "HBM bandwidth of plain kernels (context for the roofline)",
+            "unit": "GB/s", "data": "synthetic",
+            "config": {"workload": f"{cfg.name}: {T} tokens, hidden {H}, {cfg.num_experts} experts "
+                                   f"{cfg.routing} top-{K}, BLOCK_M {cfg.block_m}",
+                       "rows": n_a, "row_bytes": row_bytes},
+            "results": res}
 
 
 def main() -> int:
@@ -682,6 +778,9 @@ def main() -> int:
                     help="print the eager vs HIP-graph step time instead")
     ap.add_argument("--ceiling", action="store_true",
                     help="print the bandwidth of plain torch fill / read / copy kernels instead")
+    ap.add_argument("--serial", action="store_true",
+                    help="with --gate: skip the legs that need kernels running at the same time "
+                         "(for counter passes, which serialise kernels)")
     ap.add_argument("--overlap", action="store_true",
                     help="print the streaming dispatch / tile consumer overlap measurement instead "
                          "(default workload: stream)")
@@ -696,6 +795,17 @@ def main() -> int:
     import combine_ep_layout_amd as ep
     from synth import CONFIGS, generate
 
+    if args.copy_calibration:
+        # a plain 1 GiB device copy, three times: the reference launch that
+        # HBM counter passes scale their FETCH_SIZE / WRITE_SIZE by
+        torch.cuda.set_device(0)
+        a = torch.empty(1 << 29, dtype=torch.int16, device=torch.device("cuda", 0))
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
     if args.borrow_compare:
         torch.cuda.set_device(0)
         print(json.dumps(borrow_compare(args.steps, args.warmup)), flush=True)
@@ -706,7 +816,8 @@ def main() -> int:
         return 0
     if args.gate:
         torch.cuda.set_device(0)
-        print(json.dumps(gate_bench(CONFIGS[args.config], args.steps, args.warmup)), flush=True)
+        print(json.dumps(gate_bench(CONFIGS[args.config], args.steps, args.warmup, args.serial)),
+              flush=True)
         return 0
     if args.graph:
         torch.cuda.set_device(0)
@@ -714,7 +825,7 @@ def main() -> int:
         return 0
     if args.ceiling:
         torch.cuda.set_device(0)
-        print(json.dumps(ceiling_bench(args.steps, args.warmup)), flush=True)
+        print(json.dumps(ceiling_bench(CONFIGS[args.config], args.steps, args.warmup)), flush=True)
         return 0
     if args.overlap:
         torch.cuda.set_device(0)
@@ -866,14 +977,6 @@ def main() -> int:
     dom_ms, dom_bytes = kern[dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = read_traffic(dom, cfg.name, dom_bytes)
-
-    if args.copy_calibration:
-        a = torch.empty(1 << 29, dtype=torch.int16, device=dev)       # 1 GiB
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -1,4 +1,5 @@
-"""Build libep_layout.so (gfx950) in-tree with hipcc.
+"""Build libep_layout.so (gfx950) in-tree with hipcc, and beside it
+libep_ceiling.so, the bandwidth probes the benchmark's ceiling leg loads.
 
     python combine_ep_layout_amd/build.py [-v] [-o OUT]
 
@@ -17,6 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libep_layout.so")
 SOURCES = [os.path.join(CSRC, "ep_kernels.hip"), os.path.join(CSRC, "ep_api.hip"),
            os.path.join(CSRC, "ep_noalloc.hip")]
+CEILING_LIB = os.path.join(PKG, "libep_ceiling.so")
+CEILING_SOURCES = [os.path.join(CSRC, "ep_ceiling.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -41,15 +44,21 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, out: Optional[str] = None) -> str:
-    out = out or LIB
+def _hipcc(out: str, sources: list, verbose: bool) -> str:
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp, *SOURCES]
+    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp, *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
+
+
+def build(verbose: bool = False, out: Optional[str] = None) -> str:
+    """Builds the library (to `out` if given) and the probe library; returns
+    the library's path."""
+    _hipcc(CEILING_LIB, CEILING_SOURCES, verbose)
+    return _hipcc(out or LIB, SOURCES, verbose)
 
 
 if __name__ == "__main__":

@@ -37,6 +37,27 @@ def test_library_exports_every_declared_symbol():
     assert sorted(ep.EXPORTS) == names
 
 
+def test_probe_library_rejects_bad_arguments_without_gpu():
+    """libep_ceiling.so (the benchmark's bandwidth probes) loads and rejects
+    invalid arguments before it launches anything."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "combine_ep_layout_amd", "libep_ceiling.so"))
+    f = lib.ep_ceiling_rows
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                  ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    rows = ctypes.c_void_p(16)
+    buf = ctypes.c_void_p(1 << 20)
+    assert f(7, 1, buf, buf, 4, 64, rows, 1, buf, None) == -1        # unknown probe
+    assert f(5, 1, buf, None, 4, 64, rows, 5, None, None) == -1      # flat beyond dst
+    assert f(0, 3, buf, None, 4, 64, rows, 1, None, None) == -1      # 3 waves per row
+    assert f(0, 1, buf, None, 4, 24, rows, 1, None, None) == -1      # row not a multiple of 16
+    assert f(0, 1, ctypes.c_void_p((1 << 20) + 8), None, 4, 64, rows, 1, None, None) == -1
+    assert f(2, 1, None, buf, 4, 64, rows, 1, None, None) == -1      # read without a sink
+    assert f(3, 1, buf, None, 4, 64, rows, 1, None, None) == -1      # copy without a source
+    assert f(0, 1, buf, None, 4, 64, None, 1, None, None) == -1      # no row list
+    assert f(0, 4, buf, None, 4, 64, rows, 0, None, None) == 0       # nothing to do
+
+
 def test_status_strings():
     import combine_ep_layout_amd as ep
     lib = ep.library()
