@@ -648,8 +648,9 @@ def overlap_bench(cfg, steps: int, warmup: int, workgroups: int = 256) -> dict:
 def ceiling_bench(cfg, steps: int, warmup: int) -> dict:
     """Context for the roofline: what simple HBM-bound kernels reach on this
     GPU, measured with the probe library (libep_ceiling.so: rows of 2*hidden
-    bytes moved in 16-byte accesses by one wave per row, "@1w", or by a
-    256-thread workgroup per row, "@4w"), on the workload's own row size and
+    bytes moved in 16-byte accesses by one wave per row, "@1w", by a
+    256-thread workgroup per row, "@4w", or by one wave per 1 KB piece of a
+    row, one access per lane, "@piece"), on the workload's own row size and
     row count N_a (every routed slot's row once):
 
       flat_write*       the same bytes as one flat array, every thread striding
@@ -711,7 +712,7 @@ def ceiling_bench(cfg, steps: int, warmup: int) -> dict:
     nb = row_bytes * n_a
     legs = {"flat_write": (probe(F, 1, orders["seq"], n_a, dst=src), nb),
             "flat_write_plain": (probe(FP, 1, orders["seq"], n_a, dst=src), nb)}
-    for wpr in (1, 4):
+    for wpr, tag in ((0, "piece"), (1, "1w"), (4, "4w")):
         for name, fn, nbytes in (
                 ("seq_write", probe(W, wpr, orders["seq"], n_a, dst=src), nb),
                 ("seq_write_plain", probe(WP, wpr, orders["seq"], n_a, dst=src), nb),
@@ -723,7 +724,7 @@ def ceiling_bench(cfg, steps: int, warmup: int) -> dict:
                 ("pool_order_write", probe(W, wpr, orders["pool_order"], cap, dst=pool), nb),
                 ("random_write", probe(W, wpr, orders["random"], cap, dst=pool), nb),
                 ("dispatch_order_read", probe(R, wpr, orders["dispatch_order"], cap, source=pool), nb)):
-            legs[f"{name}@{wpr}w"] = (fn, nbytes)
+            legs[f"{name}@{tag}"] = (fn, nbytes)
     ab = algorithmic_bytes(cfg, d["topk_idx"], h.array("expert_counts").cpu().numpy(), False)
     lp, _ = h.new_pool(H)
     y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)

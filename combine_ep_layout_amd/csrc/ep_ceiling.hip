@@ -1,10 +1,10 @@
 // Bandwidth probes for the roofline's context (libep_ceiling.so, loaded only
 // by the benchmark's ceiling leg; nothing on the dispatch/combine path uses
 // it).  Each row of `row_bytes` bytes is moved in 16-byte chunks by 1, 2 or
-// 4 waves of a 256-thread workgroup, rows taken from a list, so the same
-// kernel measures sequential streams (rows 0, 1, 2, ...) and the pool's
-// scattered-row pattern (rows in the order dispatch writes them, or combine
-// reads them).
+// 4 waves of a 256-thread workgroup, or in 1 KB pieces by one wave each (one
+// access per lane), rows taken from a list, so the same kernel measures
+// sequential streams (rows 0, 1, 2, ...) and the pool's scattered-row pattern
+// (rows in the order dispatch writes them, or combine reads them).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -40,8 +40,19 @@ __global__ void __launch_bounds__(kThreads) k_rows(int op, int waves_per_row, u3
         return;
     }
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-    const int64_t i = (int64_t)blockIdx.x * (kThreads / 64 / waves_per_row) + wave / waves_per_row;
-    const int first = (wave % waves_per_row) * 64 + lane, stride = waves_per_row * 64;
+    int64_t i;
+    int first, stride;
+    if (waves_per_row == 0) {               // one wave per 1 KB piece of a row
+        const int pieces = (n16 + 63) / 64;
+        const int64_t wv = (int64_t)blockIdx.x * (kThreads / 64) + wave;
+        i = wv / pieces;
+        first = (int)(wv - i * pieces) * 64 + lane;
+        stride = n16;                       // one chunk per lane
+    } else {
+        i = (int64_t)blockIdx.x * (kThreads / 64 / waves_per_row) + wave / waves_per_row;
+        first = (wave % waves_per_row) * 64 + lane;
+        stride = waves_per_row * 64;
+    }
     if (i >= n_rows) return;
     const int64_t r = rows[i];
     if (r < 0 || r >= n_dst_rows) return;
@@ -82,22 +93,26 @@ __global__ void __launch_bounds__(kThreads) k_rows(int op, int waves_per_row, u3
 // n_dst_rows rows and dst is unused); for kCopy src holds n_rows rows, read
 // in order.  row_bytes is a multiple of 16 and at most 2^30, pointers are
 // 16-byte aligned, sink holds n_rows words for kRead, waves_per_row is 1, 2
-// or 4 (the flat writes ignore it and the list's contents, and need
-// n_rows <= n_dst_rows).  Listed rows outside [0, n_dst_rows) are skipped.
+// or 4, or 0 for one wave per 1 KB piece (the flat writes ignore it and the
+// list's contents, and need n_rows <= n_dst_rows).  Listed rows outside [0, n_dst_rows) are skipped.
 // Returns 0, -1 for an invalid argument, or the HIP error code.
 extern "C" int ep_ceiling_rows(int op, int waves_per_row, void* dst, const void* src, int64_t n_dst_rows, int64_t row_bytes,
                                const int32_t* rows, int64_t n_rows, uint32_t* sink, hipStream_t stream) {
     if (op < kWriteNonTemporal || op > kWriteFlatPlain || row_bytes <= 0 || row_bytes % 16 || row_bytes > (1 << 30) ||
         n_rows < 0 || n_rows > INT32_MAX || n_dst_rows < 0 || !rows ||
-        (waves_per_row != 1 && waves_per_row != 2 && waves_per_row != 4))
+        (waves_per_row != 0 && waves_per_row != 1 && waves_per_row != 2 && waves_per_row != 4))
         return -1;
     if (((uintptr_t)dst | (uintptr_t)src) & 15u) return -1;
     if ((op != kRead && !dst) || ((op == kRead || op == kCopy) && !src) || (op == kRead && !sink))
         return -1;
     if ((op == kWriteFlat || op == kWriteFlatPlain) && n_rows > n_dst_rows) return -1;
     if (n_rows == 0) return 0;
-    const int64_t rows_per_block = kThreads / 64 / waves_per_row;
-    const unsigned blocks = (unsigned)((n_rows + rows_per_block - 1) / rows_per_block);
+    const int64_t n16 = row_bytes / 16;
+    const int64_t waves = waves_per_row == 0 ? n_rows * ((n16 + 63) / 64) : 0;
+    if (waves_per_row == 0 && (waves + 3) / 4 > INT32_MAX) return -1;
+    const int64_t rows_per_block = waves_per_row == 0 ? 1 : kThreads / 64 / waves_per_row;
+    const unsigned blocks = waves_per_row == 0 ? (unsigned)((waves + 3) / 4)
+                                               : (unsigned)((n_rows + rows_per_block - 1) / rows_per_block);
     hipLaunchKernelGGL(k_rows, dim3(blocks), dim3(kThreads), 0, stream, op, waves_per_row, (u32x4*)dst,
                        (const u32x4*)src, n_dst_rows, (int)(row_bytes / 16), rows, n_rows, sink);
     return (int)hipGetLastError();

@@ -42,10 +42,10 @@
 namespace epk {
 namespace {
 
-// Work shapes, chosen by measurement on MI355X (see the design notes): 16-byte
+// Work shapes, each chosen by timing the alternatives on MI355X: 16-byte
 // chunks or 16-channel units each lane handles per work item, and the
 // streaming dispatch's chunk.
-constexpr int kDispatchChunks = 7;      // bf16 dispatch: 16-byte chunks per lane per item
+constexpr int kDispatchChunks = 2;      // bf16 dispatch: 16-byte chunks per lane per item
 constexpr int kFp8Units = 1;            // FP8 dispatch: 16-channel units per lane per item
 constexpr int kFp8StreamUnits = 2;      // the same with the streaming release
 constexpr int kCombineChunks = 2;       // combine: 16-byte chunks per lane per item
@@ -701,10 +701,10 @@ __device__ __forceinline__ uint32_t mag_for_max(uint32_t b) {
 }
 
 // Scale stores of one 64-lane step (8 groups): every lane of a group holds
-// its group's byte (UE8M0) and float (the other flavours).  Packed MN-major
-// words and float scales are device-coherent atomic stores when streaming, so
-// the release stays cheap; row-major UE8M0 bytes are plain stores in every
-// mode (when streaming, the release fence writes them back).
+// its group's byte (UE8M0) and float (the other flavours).  When streaming,
+// every scale store is a relaxed device-scope atomic store, written through
+// the XCD's L2 like the pool rows, so the release needs no write-back; plain
+// stores otherwise.
 template <bool STREAM, typename V>
 __device__ __forceinline__ void put_scale(V* p, V v) {
     if constexpr (STREAM)
@@ -772,7 +772,7 @@ __global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg,
     const int w = uniform_i(threadIdx.x / kWave);
     const int nunit = a.H / 16;          // 16 channels (32 bytes in, 16 bytes out) per unit
     const int ngrp = a.H / 128;
-    // (the streaming release is faster with plain byte stores written back by its fence)
+    // a row's 8 UE8M0 scale bytes of a 64-lane step go out as one 64-bit store
     const bool pack8 = (ngrp & 7) == 0 && ((uintptr_t)a.scales & 7) == 0;
     const u32x4* x = (const u32x4*)a.x;
     u32x4* pool = (u32x4*)a.pool;

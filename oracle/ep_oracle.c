@@ -25,7 +25,7 @@
  * that fmaf is a single correctly rounded fused multiply-add and no other
  * expression is contracted.
  *
- * Readings where the pages are silent (each is listed in the design notes):
+ * Readings where the pages are silent:
  *   - rows of one expert are filled in ascending flat slot order s = t*K + k;
  *   - topk id -1 is a masked slot; ids outside [-1, E) set error bit 1 and are
  *     treated as masked;

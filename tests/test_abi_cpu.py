@@ -55,7 +55,9 @@ def test_probe_library_rejects_bad_arguments_without_gpu():
     assert f(2, 1, None, buf, 4, 64, rows, 1, None, None) == -1      # read without a sink
     assert f(3, 1, buf, None, 4, 64, rows, 1, None, None) == -1      # copy without a source
     assert f(0, 1, buf, None, 4, 64, None, 1, None, None) == -1      # no row list
+    assert f(0, 5, buf, None, 4, 64, rows, 1, None, None) == -1     # 5 waves per row
     assert f(0, 4, buf, None, 4, 64, rows, 0, None, None) == 0       # nothing to do
+    assert f(0, 0, buf, None, 4, 64, rows, 0, None, None) == 0       # (one wave per piece)
 
 
 def test_status_strings():
