@@ -105,7 +105,7 @@ ep_status hip_status(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP
 constexpr auto kDensityWait = std::chrono::milliseconds(200);
 
 // Routing density of the handle's current layout, for the launch shape of
-// the plain combine and the dispatch backward.  The layout kernel stores it,
+// the bf16 dispatch, the plain combine and the dispatch backward.  The layout kernel stores it,
 // tagged with its epoch, as soon as its total is known; when that store has
 // not arrived yet the call waits for it on the host (for the layout kernel
 // only, not for the rest of the stream), so the shape follows the routing
@@ -126,10 +126,10 @@ int32_t reported_density(const ep_handle* h) {
     }
 }
 
-int32_t current_density(const ep_handle* h, int32_t hidden, hipStream_t stream) {
+int32_t current_density(const ep_handle* h, bool shape_depends, hipStream_t stream) {
     if (h->density_hint == EP_DENSITY_SPARSE) return epk::kDensitySparse;
     if (h->density_hint == EP_DENSITY_DENSE) return epk::kDensityDense;
-    if (!epk::combine_shape_uses_density(h->T, hidden, h->num_cu)) return epk::kDensityDense;
+    if (!shape_depends) return epk::kDensityDense;
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
         (void)hipGetLastError();
@@ -393,6 +393,10 @@ ep_status ep_dispatch(ep_handle* h, const void* x, int32_t hidden, void* pool,
     a.tile_ready = h->tile_ready;
     a.seq = h->seq + 1;
     a.round = h->round + (ready ? 1u : 0u);
+    // launch shape of the bf16 dispatch (dense routing: one workgroup per
+    // token segment), from the current layout's report as for ep_combine
+    const bool shape_depends = !fp8 && !ready && epk::dispatch_shape_uses_density(a.T, a.H, a.K);
+    a.density = shape_depends ? current_density(h, true, stream) : epk::kDensitySparse;
     ep_status st = hip_status(epk::launch_dispatch(a, fp8, ready, stream));
     if (st != EP_OK) return st;
     h->seq = a.seq;
@@ -418,7 +422,8 @@ ep_status ep_combine(const ep_handle* h, uint32_t epoch, const void* expert_out,
     a.weights = h->weights;
     a.y = y;
     a.num_cu = h->num_cu;
-    a.density = current_density(h, hidden, stream);     // launch shape only
+    // launch shape only
+    a.density = current_density(h, epk::combine_shape_uses_density(h->T, hidden, h->num_cu), stream);
     return hip_status(epk::launch_combine(a, stream));
 }
 
@@ -510,7 +515,8 @@ ep_status ep_dispatch_backward(const ep_handle* h, uint32_t epoch, const void* g
     a.weights = nullptr;
     a.y = grad_x;
     a.num_cu = h->num_cu;
-    a.density = current_density(h, hidden, stream);     // launch shape, as ep_combine
+    // launch shape, as ep_combine
+    a.density = current_density(h, epk::combine_shape_uses_density(h->T, hidden, h->num_cu), stream);
     return hip_status(epk::launch_combine_unit(a, stream));
 }
 

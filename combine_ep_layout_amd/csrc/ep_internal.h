@@ -41,8 +41,9 @@ struct LayoutArgs {
     uint32_t epoch;             // the epoch this layout starts
 };
 
-// Routing density of a layout, as the layout reports it for the next combine's
-// launch shape (results never depend on it).
+// Routing density of a layout, as the layout reports it for the launch shapes
+// of the bf16 dispatch and the combine that follow it (results never depend
+// on it).
 enum Density : int32_t {
     kDensityUnknown = 0,        // no layout reported yet
     kDensitySparse = 1,         // fewer than 4 real rows per token on average
@@ -77,6 +78,7 @@ struct DispatchArgs {
     uint32_t* tile_ready;
     uint32_t seq;
     uint32_t round;             // TILE_READY dispatches since the layout (1, 2, ...)
+    int32_t density;            // Density of the current layout (launch shape of the bf16 dispatch)
 };
 
 struct CombineArgs {
@@ -153,6 +155,10 @@ hipError_t launch_consume(const ConsumeArgs& a, int workgroups, hipStream_t stre
 // these sizes depends on the routing density (it does not for grids that are
 // resident at once, nor when there are no tokens).
 bool combine_shape_uses_density(int T, int H, int num_cu);
+// Whether the launch shape of the bf16 dispatch without the streaming release
+// depends on the routing density for these sizes (top_k up to 8 and at least
+// 64 MiB of x).
+bool dispatch_shape_uses_density(int T, int H, int K);
 
 // Workgroups the multi-workgroup layout path needs for S slots.
 inline int layout_blocks(int64_t S) {

@@ -210,7 +210,12 @@ ep_status ep_layout(ep_handle* h, const int32_t* topk_idx, const float* topk_wei
  * e4m3fn.  With EP_DISPATCH_TILE_READY each tile's arrival count is raised as
  * its rows land and the dispatch that completes the tile release-stores the
  * sequence number into tile_ready[tile] (device scope), so a consumer on
- * another stream may acquire-load it and read the tile's rows. */
+ * another stream may acquire-load it and read the tile's rows.
+ * Launch shape: a bf16 dispatch without EP_DISPATCH_TILE_READY, with top_k up
+ * to 8 and at least 64 MiB of x, takes its shape from the current layout's
+ * routing density as ep_combine does (and may wait for the layout kernel's
+ * report on the host in the same way); the pool is the same in every
+ * shape. */
 ep_status ep_dispatch(ep_handle* h, const void* x, int32_t hidden, void* pool,
                       void* pool_scales, uint32_t flags, hipStream_t stream,
                       uint32_t* seq_out);
@@ -258,12 +263,14 @@ ep_status ep_combine_gated(const ep_handle* h, uint32_t epoch, const void* exper
                            int32_t hidden, void* y, uint32_t round, uint32_t spin_limit_us,
                            hipStream_t stream);
 
-/* Launch-shape hint of ep_combine and ep_dispatch_backward.  EP_DENSITY_AUTO
- * (the default) takes the current layout's reported density as described at
- * ep_combine (waiting for it if needed; the dense shape under graph capture).
- * EP_DENSITY_SPARSE or EP_DENSITY_DENSE fix the shape for the handle's later
- * calls, which then never wait: for callers that capture the combine in a HIP
- * graph, or know their routing.  Results never depend on the shape. */
+/* Launch-shape hint of ep_combine, ep_dispatch_backward and the bf16
+ * ep_dispatch.  EP_DENSITY_AUTO (the default) takes the current layout's
+ * reported density as described at ep_combine (waiting for it if needed; the
+ * dense shape under graph capture).  EP_DENSITY_SPARSE or EP_DENSITY_DENSE fix
+ * the shape for the handle's later calls, which then never wait: for callers
+ * that capture these calls in a HIP graph, that enqueue far ahead of the GPU
+ * (whose calls would otherwise wait for the layout kernel to run), or that
+ * know their routing.  Results never depend on the shape. */
 #define EP_DENSITY_AUTO   0
 #define EP_DENSITY_SPARSE 1     /* fewer than 4 real rows per token on average */
 #define EP_DENSITY_DENSE  2     /* 4 or more */

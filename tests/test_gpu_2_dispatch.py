@@ -71,6 +71,39 @@ def _full_size_dispatch(name, fp8):
     h.close()
 
 
+@pytest.mark.parametrize("top_k", [1, 2, 4, 8])
+def test_bf16_dispatch_shapes_write_the_same_pool(top_k):
+    """The bf16 dispatch's two launch shapes (one workgroup per token segment
+    for dense routing, waves over tokens otherwise), each forced with the
+    density hint on the same layout, against the oracle's layout: every real
+    row is its token's row of x, every padding row keeps its poison.  8192
+    tokens x hidden 4096 (64 MiB of x, where the shape depends on the
+    density); then the shape the handle takes by itself, for this routing."""
+    import combine_ep_layout_amd as ep
+    say(f"[dispatch bf16] both launch shapes, top_k={top_k}")
+    cfg = CONFIGS["prefill"].replace(tokens=8192, hidden=4096, top_k=top_k)
+    d = generate(cfg, 5)
+    L = oracle.layout(d["topk_idx"], cfg.num_experts, cfg.block_m)
+    recv = L["pool_recv_token"]
+    real = torch.from_numpy(np.flatnonzero(recv >= 0)).to(dev())
+    pad = torch.from_numpy(np.flatnonzero(recv < 0)).to(dev())
+    src = torch.from_numpy(recv[recv >= 0].astype(np.int64)).to(dev())
+    h = new_handle(cfg)
+    h.layout(*device_routing(d))
+    x = to_dev_bf16(d["x"])
+    for hint in (ep.EP_DENSITY_DENSE, ep.EP_DENSITY_SPARSE, ep.EP_DENSITY_AUTO):
+        h.set_density_hint(hint)
+        pool = torch.full((h.capacity_rows, cfg.hidden), POISON_BF16 - 0x10000, dtype=torch.int16,
+                          device=dev()).view(torch.bfloat16)
+        h.dispatch(x, pool)
+        torch.cuda.synchronize()
+        assert torch.equal(pool.view(torch.int16)[real], x.view(torch.int16)[src]), hint
+        assert bool((pool.view(torch.int16)[pad] == POISON_BF16 - 0x10000).all()), hint
+        say(f"  hint {hint}: {real.numel()} rows match, {pad.numel()} padding rows untouched")
+    assert h.sync_status() == ep.EP_OK
+    h.close()
+
+
 def test_bf16_prefill_full_size():
     say("[dispatch bf16] prefill full size")
     _full_size_dispatch("prefill", fp8=False)
