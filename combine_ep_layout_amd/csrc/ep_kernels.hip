@@ -1232,12 +1232,12 @@ __global__ __launch_bounds__(64 * kGateWaves) void k_combine_gated(CombineArgs a
 // ----------------------------------------------------- combine backward ---
 
 
-// Backward of the combine, one wave per token: grad_y[t] is read once (once
-// per slot group with MANY); for each unmasked slot the gradient row
-// bf16(fp32(w * g)) is stored and the exact bf16 x bf16 products are
-// accumulated in double, per lane in ascending chunk order and then across
-// lanes by a fixed butterfly (lane 0's sum is kept), then rounded once to
-// float.
+// Backward of the combine for top_k above 8 (k_combine_bwd_slots serves the
+// rest), one wave per token: grad_y[t] is read once per slot group; for each
+// unmasked slot the gradient row bf16(fp32(w * g)) is stored and the exact
+// bf16 x bf16 products are accumulated in double, per lane in ascending chunk
+// order and then across lanes by a fixed butterfly (lane 0's sum is kept),
+// then rounded once to float.
 template <int KT, bool MANY>
 __global__ __launch_bounds__(256) void k_combine_bwd(CombineBwdArgs a) {
     constexpr int U = kBwdChunks;
@@ -1306,6 +1306,86 @@ __global__ __launch_bounds__(256) void k_combine_bwd(CombineBwdArgs a) {
             if (lane == 0 && k0 + k < a.K) a.grad_w[t * a.K + k0 + k] = rows[k] >= 0 ? (float)v : 0.0f;
         }
     }
+}
+
+// Backward of the combine for top_k up to 8: one workgroup per token, wave k
+// taking slot k.  The wave walks the slot's row segment by segment, loading
+// the next segment of grad_y and of the expert row before it stores the
+// current gradient segment (on gfx9 a wait for a load also waits for every
+// store issued before it), and keeps the same per-lane fp64 chain in
+// ascending chunk order and the same butterfly as k_combine_bwd, so its
+// results are identical.  grad_y's segment is read by every wave of the
+// workgroup (once from memory, then from the caches).  With one row per wave
+// the workgroups in flight write a narrower window of rows than one wave per
+// token writing all its rows: prefill 736 against 760 us, the stream shape
+// 810 against 854 us, share 32 against 40 us.
+template <int KT>
+__global__ __launch_bounds__(kWave * kSlotGroup) void k_combine_bwd_slots(CombineBwdArgs a, int nseg) {
+    constexpr int U = kBwdChunks;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int k = uniform_i(threadIdx.x / kWave);
+    const int t = (int)blockIdx.x;
+    if (k >= a.K) return;
+    const int row = a.slot_to_row[t * a.K + k];
+    if (row < 0) {
+        if (lane == 0) a.grad_w[t * a.K + k] = 0.0f;
+        return;
+    }
+    const int n16 = a.H / 8;
+    const float wt = a.weights[t * a.K + k];
+    const u32x4* gy = (const u32x4*)a.grad_y + (int64_t)t * n16;
+    const u32x4* orow = (const u32x4*)a.expert_out + (int64_t)row * n16;
+    u32x4* grow = (u32x4*)a.grad_eo + (int64_t)row * n16;
+    double acc = 0.0;
+    u32x4 g_n[U], o_n[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c = lane + u * kWave;
+        if (c < n16) {
+            g_n[u] = gy[c];
+            o_n[u] = load_v<true>(orow + c);
+        }
+    }
+    for (int seg = 0; seg < nseg; ++seg) {
+        const int c0 = seg * (kWave * U) + lane;
+        u32x4 g[U], o[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            g[u] = g_n[u];
+            o[u] = o_n[u];
+        }
+        if (seg + 1 < nseg) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + kWave * U + u * kWave;
+                if (c < n16) {
+                    g_n[u] = gy[c];
+                    o_n[u] = load_v<true>(orow + c);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + u * kWave;
+            if (c >= n16) continue;
+            u32x4 q;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float g0 = __uint_as_float(g[u][i] << 16);
+                const float g1 = __uint_as_float(g[u][i] & 0xFFFF0000u);
+                const float o0 = __uint_as_float(o[u][i] << 16);
+                const float o1 = __uint_as_float(o[u][i] & 0xFFFF0000u);
+                q[i] = f32_to_bf16_rne(wt * g0) | (f32_to_bf16_rne(wt * g1) << 16);
+                acc = __builtin_fma((double)g0, (double)o0, acc);
+                acc = __builtin_fma((double)g1, (double)o1, acc);
+            }
+            store_row<kStoreNonTemporal>(grow, a.H * 2, c, q);
+        }
+    }
+    double v = acc;
+#pragma unroll
+    for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
+    if (lane == 0) a.grad_w[t * a.K + k] = (float)v;
 }
 
 // ------------------------------------------- consumer stand-in (tests) ---
@@ -1671,8 +1751,13 @@ hipError_t combine_any(const CombineArgs& a, hipStream_t stream) {
 
 template <int KT, bool MANY>
 hipError_t combine_bwd_kt(const CombineBwdArgs& a, hipStream_t st) {
-    const int grid = (a.T + 3) / 4;
-    hipLaunchKernelGGL((k_combine_bwd<KT, MANY>), dim3(grid), dim3(256), 0, st, a);
+    if constexpr (!MANY) {
+        const int nseg = (a.H / 8 + kWave * kBwdChunks - 1) / (kWave * kBwdChunks);
+        hipLaunchKernelGGL((k_combine_bwd_slots<KT>), dim3(a.T), dim3(kWave * KT), 0, st, a, nseg);
+    } else {
+        const int grid = (a.T + 3) / 4;
+        hipLaunchKernelGGL((k_combine_bwd<KT, MANY>), dim3(grid), dim3(256), 0, st, a);
+    }
     return hipGetLastError();
 }
 
