@@ -318,12 +318,13 @@ def _time_in_step_us(before, fn, after, steps: int, warmup: int, stream, flush=N
     return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
 
 
-def graph_bench(cfg, steps: int, warmup: int, per_replay: int = 4) -> dict:
+def graph_bench(cfg, steps: int, warmup: int, per_replay: int = 4, separate: bool = False) -> dict:
     """The layout -> dispatch -> combine step launched eagerly vs captured in
     a HIP graph of `per_replay` steps (torch's graph capture on the library's
     stream).  Small batches are launch-bound, and a graph replay removes the
-    gaps between launches.  The graph's output is checked against the eager
-    step's."""
+    gaps between launches.  Batches of at most 2048 slots take the one-launch
+    ep_layout_dispatch unless `separate`.  The graph's output is checked
+    against the eager step's."""
     import torch
     import combine_ep_layout_amd as ep
     from synth import generate
@@ -341,9 +342,14 @@ def graph_bench(cfg, steps: int, warmup: int, per_replay: int = 4) -> dict:
     eo = torch.randn(h.capacity_rows, H, generator=g, device=dev).to(torch.bfloat16)
     y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
 
+    one_launch = not ready and T * K <= 2048 and not separate
+
     def step():
-        e = h.layout(idx, w)
-        h.dispatch(x, pool, scales, fp8=fp8, tile_ready=ready)
+        if one_launch:
+            e, _ = h.layout_dispatch(idx, w, x, pool, scales, fp8=fp8)
+        else:
+            e = h.layout(idx, w)
+            h.dispatch(x, pool, scales, fp8=fp8, tile_ready=ready)
         h.combine(e, eo, y)
 
     s = torch.cuda.Stream()                              # default priority
@@ -377,6 +383,7 @@ def graph_bench(cfg, steps: int, warmup: int, per_replay: int = 4) -> dict:
                                    f"{cfg.routing} top-{K}, BLOCK_M {cfg.block_m}, "
                                    f"{'fp8' if fp8 else 'bf16'}" + (", tile_ready" if ready else ""),
                        "steps_per_replay": per_replay},
+            "step_calls": "ep_layout_dispatch, ep_combine" if one_launch else "ep_layout, ep_dispatch, ep_combine",
             "combine_density_hint": {1: "sparse", 2: "dense"}.get(density, "auto"),
             "eager_us_per_step": round(eager, 2), "graph_us_per_step": round(replay, 2),
             "change_pct": round(100.0 * (replay - eager) / eager, 1),
@@ -782,6 +789,9 @@ def main() -> int:
     ap.add_argument("--serial", action="store_true",
                     help="with --gate: skip the legs that need kernels running at the same time "
                          "(for counter passes, which serialise kernels)")
+    ap.add_argument("--separate", action="store_true",
+                    help="run layout and dispatch as two calls also where the one-launch "
+                         "ep_layout_dispatch applies (batches of at most 2048 slots)")
     ap.add_argument("--overlap", action="store_true",
                     help="print the streaming dispatch / tile consumer overlap measurement instead "
                          "(default workload: stream)")
@@ -822,7 +832,8 @@ def main() -> int:
         return 0
     if args.graph:
         torch.cuda.set_device(0)
-        print(json.dumps(graph_bench(CONFIGS[args.config], args.steps, args.warmup)), flush=True)
+        print(json.dumps(graph_bench(CONFIGS[args.config], args.steps, args.warmup,
+                                     separate=args.separate)), flush=True)
         return 0
     if args.ceiling:
         torch.cuda.set_device(0)
@@ -862,18 +873,26 @@ def main() -> int:
     y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
+    # Batches of at most 2048 slots take the library's one-launch layout and
+    # dispatch (ep_layout_dispatch) unless --separate asks for the two calls.
+    one_launch = not ready and T * K <= 2048 and not args.separate
+    phases = ("layout_dispatch", "combine") if one_launch else ("layout", "dispatch", "combine")
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        epoch = h.layout(idx, w)
+        if one_launch:
+            epoch, _ = h.layout_dispatch(idx, w, x, pool, scales, fp8=fp8)
+        else:
+            epoch = h.layout(idx, w)
+            if ev is not None:
+                ev[1].record(stream)
+            h.dispatch(x, pool, scales, fp8=fp8, tile_ready=ready)
         if ev is not None:
-            ev[1].record(stream)
-        h.dispatch(x, pool, scales, fp8=fp8, tile_ready=ready)
-        if ev is not None:
-            ev[2].record(stream)
+            ev[len(phases) - 1].record(stream)
         h.combine(epoch, eo, y)
         if ev is not None:
-            ev[3].record(stream)
+            ev[len(phases)].record(stream)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -918,14 +937,15 @@ def main() -> int:
     # Per-kernel durations in flushed steps: a second pass of K steps with HIP
     # events around every launch, on the stream the library launches on.
     log(f"[bench] timing {args.steps} flushed steps per kernel")
-    cold = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    nev = len(phases) + 1
+    cold = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     for i in range(args.steps):
         do_flush()
         step(cold[i])
     torch.cuda.synchronize()
     cold_s = {k: np.array([e[j].elapsed_time(e[j + 1]) for e in cold]) * 1e3
-              for j, k in enumerate(("layout", "dispatch", "combine"))}
-    lay, dis, com = (float(cold_s[k].mean()) / 1e3 for k in ("layout", "dispatch", "combine"))
+              for j, k in enumerate(phases)}
+    cold_ms = {k: float(v.mean()) / 1e3 for k, v in cold_s.items()}
 
     # Warm steps, labelled as such: K steps back to back between two events
     # (each step finds what the previous one left in L2 and MALL), then a pass
@@ -940,12 +960,12 @@ def main() -> int:
     t_end.record(stream)
     torch.cuda.synchronize()
     warm_ms_per_step = t_start.elapsed_time(t_end) / args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     warm_s = {k: np.array([e[j].elapsed_time(e[j + 1]) for e in evs]) * 1e3
-              for j, k in enumerate(("layout", "dispatch", "combine"))}
+              for j, k in enumerate(phases)}
 
     # With the streaming release on, the same dispatch without it, for
     # comparison, timed the same way: inside the layout -> dispatch -> combine
@@ -973,7 +993,11 @@ def main() -> int:
     total = ab["layout"] + ab["dispatch"] + ab["combine"]
     value = total / (ms_per_step * 1e-3) / 1e9
     warm_value = total / (warm_ms_per_step * 1e-3) / 1e9
-    kern = {"dispatch": (dis, ab["dispatch"]), "combine": (com, ab["combine"])}
+    if one_launch:
+        kern = {"layout_dispatch": (cold_ms["layout_dispatch"], ab["layout"] + ab["dispatch"]),
+                "combine": (cold_ms["combine"], ab["combine"])}
+    else:
+        kern = {"dispatch": (cold_ms["dispatch"], ab["dispatch"]), "combine": (cold_ms["combine"], ab["combine"])}
     dom = max(kern, key=lambda k: kern[k][0])
     dom_ms, dom_bytes = kern[dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
@@ -991,11 +1015,16 @@ def main() -> int:
         # per stage: oracle seconds scaled to the whole workload (linear in
         # tokens for a sample) over the GPU kernel's seconds
         scale = T / cpu["tokens"]
-        gpu_s = {"layout": lay * 1e-3, "dispatch": dis * 1e-3, "combine": com * 1e-3}
-        cpu["speedup_per_stage"] = {k: round(cpu["stage_seconds"][k] * scale / gpu_s[k], 1)
-                                    for k in gpu_s}
-        cpu["single_thread"]["speedup_per_stage"] = {
-            k: round(cpu["single_thread"]["stage_seconds"][k] * scale / gpu_s[k], 1) for k in gpu_s}
+        gpu_s = {k: v * 1e-3 for k, v in cold_ms.items()}
+
+        def speedups(stage_s):
+            if one_launch:
+                stage_s = {"layout_dispatch": stage_s["layout"] + stage_s["dispatch"],
+                           "combine": stage_s["combine"]}
+            return {k: round(stage_s[k] * scale / gpu_s[k], 1) for k in gpu_s}
+
+        cpu["speedup_per_stage"] = speedups(cpu["stage_seconds"])
+        cpu["single_thread"]["speedup_per_stage"] = speedups(cpu["single_thread"]["stage_seconds"])
     mode = "fp8" if fp8 else "bf16"
     out = {
         "metric": METRIC,
@@ -1020,8 +1049,8 @@ def main() -> int:
         "timing": "caches flushed (1 GiB read) before every step; mean of the K steps' HIP-event "
                   "intervals, the flush outside them",
         "step_us_percentiles": pct(step_us),
-        "kernels_us": {"layout": round(lay * 1e3, 2), "dispatch": round(dis * 1e3, 2),
-                       "combine": round(com * 1e3, 2)},
+        "kernels_us": {k: round(v * 1e3, 2) for k, v in cold_ms.items()},
+        "step_calls": "ep_layout_dispatch, ep_combine" if one_launch else "ep_layout, ep_dispatch, ep_combine",
         "kernels_us_percentiles": {k: pct(v) for k, v in cold_s.items()},
         "warm": {"what": "K steps back to back (each step finds the previous step's data in L2 "
                          "and MALL), one event pair around all of them; per-kernel times from a "

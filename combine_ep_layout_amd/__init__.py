@@ -69,7 +69,7 @@ EXPORTS = [
     "ep_array_bytes", "ep_copy_array", "ep_counts_to_host", "ep_handle_sync_status",
     "ep_tile_consume", "ep_status_string", "ep_borrow_release", "ep_combine_backward",
     "ep_dispatch_backward", "ep_combine_gated", "ep_fp8_cast_back", "ep_scale_ld",
-    "ep_layout_noalloc", "ep_set_density_hint", "ep_layout_density",
+    "ep_layout_noalloc", "ep_set_density_hint", "ep_layout_density", "ep_layout_dispatch",
 ]
 
 EP_DENSITY_AUTO = 0
@@ -103,6 +103,8 @@ def _load() -> ctypes.CDLL:
         "ep_num_tokens": (I32, [P]),
         "ep_layout": (st, [P, P, P, I32, P, ctypes.POINTER(U32)]),
         "ep_dispatch": (st, [P, P, I32, P, P, U32, P, ctypes.POINTER(U32)]),
+        "ep_layout_dispatch": (st, [P, P, P, I32, P, I32, P, P, U32, P, ctypes.POINTER(U32),
+                                    ctypes.POINTER(U32)]),
         "ep_combine": (st, [P, U32, P, I32, P, P]),
         "ep_handle_get_view": (st, [P, P]),
         "ep_array_bytes": (I64, [P, ctypes.c_int]),
@@ -185,6 +187,17 @@ def ep_dispatch(h, x: torch.Tensor, pool: torch.Tensor, pool_scales: Optional[to
     _check(_lib.ep_dispatch(h, _ptr(x), x.shape[1], _ptr(pool), _ptr(pool_scales), flags,
                             _stream(stream), ctypes.byref(seq)), "ep_dispatch")
     return seq.value
+
+
+def ep_layout_dispatch(h, topk_idx: torch.Tensor, topk_weights: torch.Tensor, x: torch.Tensor,
+                       pool: torch.Tensor, pool_scales: Optional[torch.Tensor], flags: int,
+                       stream=None) -> tuple:
+    epoch = ctypes.c_uint32()
+    seq = ctypes.c_uint32()
+    _check(_lib.ep_layout_dispatch(h, _ptr(topk_idx), _ptr(topk_weights), topk_idx.shape[0], _ptr(x),
+                                   x.shape[1], _ptr(pool), _ptr(pool_scales), flags, _stream(stream),
+                                   ctypes.byref(epoch), ctypes.byref(seq)), "ep_layout_dispatch")
+    return epoch.value, seq.value
 
 
 def ep_combine(h, epoch: int, expert_out: torch.Tensor, y: torch.Tensor, stream=None) -> None:
@@ -345,6 +358,33 @@ class EpHandle:
         flags = (EP_DISPATCH_FP8 | scale_flags(scale_kind, mn_major) if fp8 else 0) | \
                 (EP_DISPATCH_TILE_READY if tile_ready else 0)
         return ep_dispatch(self._h, x, pool, pool_scales if fp8 else None, flags, stream)
+
+    def layout_dispatch(self, topk_idx: torch.Tensor, topk_weights: torch.Tensor, x: torch.Tensor,
+                        pool: torch.Tensor, pool_scales: Optional[torch.Tensor] = None, fp8: bool = False,
+                        stream=None, scale_kind: str = "ue8m0", mn_major: bool = False) -> tuple:
+        """layout() and dispatch() in one call (one kernel launch for batches
+        of at most 2048 slots); returns (epoch, dispatch sequence number)."""
+        _require(topk_idx, torch.int32, "topk_idx", self.device)
+        _require(topk_weights, torch.float32, "topk_weights", self.device)
+        if topk_idx.dim() != 2 or topk_idx.shape[1] != self.top_k or topk_weights.shape != topk_idx.shape:
+            raise ValueError("topk_idx / topk_weights must both be [num_tokens, top_k]")
+        _require(x, torch.bfloat16, "x", self.device)
+        if x.dim() != 2 or x.shape[0] != topk_idx.shape[0]:
+            raise ValueError("x must be [num_tokens, hidden]")
+        H = x.shape[1]
+        if pool.shape[0] < self.capacity_rows or pool.shape[1] != H:
+            raise ValueError(f"pool must be at least [{self.capacity_rows}, {H}]")
+        _require(pool, torch.uint8 if fp8 else torch.bfloat16, "pool", self.device)
+        if fp8:
+            shape, dtype = self.scale_shape(H, scale_kind, mn_major)
+            if pool_scales is None or tuple(pool_scales.shape) != shape:
+                raise ValueError(f"pool_scales must be {shape}")
+            _require(pool_scales, dtype, "pool_scales", self.device)
+        elif scale_kind != "ue8m0" or mn_major:
+            raise ValueError("scale flavours apply to FP8 dispatch only")
+        flags = EP_DISPATCH_FP8 | scale_flags(scale_kind, mn_major) if fp8 else 0
+        return ep_layout_dispatch(self._h, topk_idx, topk_weights, x, pool, pool_scales if fp8 else None,
+                                  flags, stream)
 
     def combine_backward(self, epoch: int, grad_y: torch.Tensor, expert_out: torch.Tensor,
                          grad_expert_out: Optional[torch.Tensor] = None, stream=None):

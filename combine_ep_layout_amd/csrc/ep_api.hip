@@ -298,15 +298,21 @@ int32_t ep_num_tokens(const ep_handle* h) { return h ? h->T : -1; }
 
 int64_t ep_scale_ld(const ep_handle* h) { return h ? scale_ld_of(h->cap) : -1; }
 
-ep_status ep_layout(ep_handle* h, const int32_t* topk_idx, const float* topk_weights,
-                    int32_t num_tokens, hipStream_t stream, uint32_t* epoch_out) {
+namespace {
+
+// Argument checks of a layout of num_tokens tokens (no state change).
+ep_status check_layout(const ep_handle* h, const int32_t* topk_idx, const float* topk_weights,
+                       int32_t num_tokens) {
     if (!h || num_tokens < 0 || num_tokens > h->cfg.max_tokens) return EP_ERR_INVALID_ARGUMENT;
     if (num_tokens > 0 && (!topk_idx || !topk_weights || !aligned4(topk_idx) ||
                            !aligned4(topk_weights)))
         return EP_ERR_INVALID_ARGUMENT;
     if (h->lease) return EP_ERR_HANDLE_STATE;
-    ep_status ws = wait_lease(h, stream);
-    if (ws != EP_OK) return ws;
+    return EP_OK;
+}
+
+epk::LayoutArgs layout_args(const ep_handle* h, const int32_t* topk_idx, const float* topk_weights,
+                            int32_t num_tokens) {
     epk::LayoutArgs a{};
     a.topk_idx = topk_idx;
     a.topk_w = topk_weights;
@@ -332,13 +338,78 @@ ep_status ep_layout(ep_handle* h, const int32_t* topk_idx, const float* topk_wei
     a.y_done = h->y_done;
     a.density = h->density_dev;
     a.epoch = h->epoch + 1;
-    ep_status st = hip_status(epk::launch_layout(a, stream));
-    if (st != EP_OK) return st;
+    return a;
+}
+
+// Handle state once a layout of num_tokens tokens is enqueued.
+void after_layout(ep_handle* h, int32_t num_tokens, hipStream_t stream, uint32_t* epoch_out) {
     h->layout_capture = capture_id(stream);
     h->T = num_tokens;
     h->epoch += 1;
     h->round = 0;
     if (epoch_out) *epoch_out = h->epoch;
+}
+
+// Argument checks of a copying dispatch (not BORROW) of T tokens.
+ep_status check_dispatch(const ep_handle* h, int32_t T, const void* x, int32_t hidden, const void* pool,
+                         const void* pool_scales, uint32_t flags) {
+    if (flags & ~(EP_DISPATCH_FP8 | EP_DISPATCH_TILE_READY | kScaleFlags)) return EP_ERR_INVALID_ARGUMENT;
+    const bool fp8 = (flags & EP_DISPATCH_FP8) != 0;
+    if (!fp8 && (flags & kScaleFlags)) return EP_ERR_INVALID_ARGUMENT;
+    if (hidden <= 0 || hidden % 8 != 0) return EP_ERR_INVALID_ARGUMENT;
+    if (hidden > kMaxHidden) return EP_ERR_UNSUPPORTED;
+    if (fp8 && (hidden % 128 != 0 || !pool_scales || !scales_aligned(pool_scales, flags)))
+        return EP_ERR_INVALID_ARGUMENT;
+    if (!fp8 && pool_scales) return EP_ERR_INVALID_ARGUMENT;
+    if (T < 0 || h->lease) return EP_ERR_HANDLE_STATE;
+    if (T > 0 && (!x || !pool || !aligned16(x) || !aligned16(pool))) return EP_ERR_INVALID_ARGUMENT;
+    return EP_OK;
+}
+
+epk::DispatchArgs dispatch_args(const ep_handle* h, int32_t T, uint32_t round, const void* x, int32_t hidden,
+                                void* pool, void* pool_scales, uint32_t flags) {
+    const bool ready = (flags & EP_DISPATCH_TILE_READY) != 0;
+    epk::DispatchArgs a{};
+    a.x = x;
+    a.T = T;
+    a.K = h->cfg.top_k;
+    a.H = hidden;
+    a.BM = h->cfg.block_m;
+    a.E = h->cfg.num_experts;
+    a.slot_to_row = h->slot_to_row;
+    a.tile_expert = h->tile_expert;
+    a.tile_target = h->tile_target;
+    a.pool = pool;
+    a.scales = pool_scales;
+    a.scale_kind = scale_kind(flags);
+    a.scale_mn = (flags & EP_SCALE_MN_MAJOR) ? 1 : 0;
+    a.scale_ld = scale_ld_of(h->cap);
+    a.max_tiles = h->max_tiles;
+    a.arrival = h->arrival;
+    a.tile_ready = h->tile_ready;
+    a.seq = h->seq + 1;
+    a.round = round + (ready ? 1u : 0u);
+    a.density = epk::kDensitySparse;
+    return a;
+}
+
+void after_dispatch(ep_handle* h, const epk::DispatchArgs& a, uint32_t* seq_out) {
+    h->seq = a.seq;
+    h->round = a.round;
+    if (seq_out) *seq_out = a.seq;
+}
+
+}  // namespace
+
+ep_status ep_layout(ep_handle* h, const int32_t* topk_idx, const float* topk_weights,
+                    int32_t num_tokens, hipStream_t stream, uint32_t* epoch_out) {
+    ep_status cs = check_layout(h, topk_idx, topk_weights, num_tokens);
+    if (cs != EP_OK) return cs;
+    ep_status ws = wait_lease(h, stream);
+    if (ws != EP_OK) return ws;
+    ep_status st = hip_status(epk::launch_layout(layout_args(h, topk_idx, topk_weights, num_tokens), stream));
+    if (st != EP_OK) return st;
+    after_layout(h, num_tokens, stream, epoch_out);
     return EP_OK;
 }
 
@@ -364,44 +435,48 @@ ep_status ep_dispatch(ep_handle* h, const void* x, int32_t hidden, void* pool,
         if (seq_out) *seq_out = h->seq;
         return EP_OK;
     }
-    if (fp8 && (hidden % 128 != 0 || !pool_scales || !scales_aligned(pool_scales, flags)))
-        return EP_ERR_INVALID_ARGUMENT;
-    if (!fp8 && pool_scales) return EP_ERR_INVALID_ARGUMENT;
-    if (h->T < 0 || h->lease) return EP_ERR_HANDLE_STATE;
-    if (h->T > 0 && (!x || !pool || !aligned16(x) || !aligned16(pool)))
-        return EP_ERR_INVALID_ARGUMENT;
+    ep_status cs = check_dispatch(h, h->T, x, hidden, pool, pool_scales, flags);
+    if (cs != EP_OK) return cs;
     if (ready && capture_without_layout(h, stream)) return EP_ERR_UNSUPPORTED;
     ep_status ws = wait_lease(h, stream);
     if (ws != EP_OK) return ws;
-    epk::DispatchArgs a{};
-    a.x = x;
-    a.T = h->T;
-    a.K = h->cfg.top_k;
-    a.H = hidden;
-    a.BM = h->cfg.block_m;
-    a.E = h->cfg.num_experts;
-    a.slot_to_row = h->slot_to_row;
-    a.tile_expert = h->tile_expert;
-    a.tile_target = h->tile_target;
-    a.pool = pool;
-    a.scales = pool_scales;
-    a.scale_kind = scale_kind(flags);
-    a.scale_mn = (flags & EP_SCALE_MN_MAJOR) ? 1 : 0;
-    a.scale_ld = scale_ld_of(h->cap);
-    a.max_tiles = h->max_tiles;
-    a.arrival = h->arrival;
-    a.tile_ready = h->tile_ready;
-    a.seq = h->seq + 1;
-    a.round = h->round + (ready ? 1u : 0u);
+    epk::DispatchArgs a = dispatch_args(h, h->T, h->round, x, hidden, pool, pool_scales, flags);
     // launch shape of the bf16 dispatch (dense routing: one workgroup per
     // token segment), from the current layout's report as for ep_combine
     const bool shape_depends = !fp8 && !ready && epk::dispatch_shape_uses_density(a.T, a.H, a.K);
-    a.density = shape_depends ? current_density(h, true, stream) : epk::kDensitySparse;
+    if (shape_depends) a.density = current_density(h, true, stream);
     ep_status st = hip_status(epk::launch_dispatch(a, fp8, ready, stream));
     if (st != EP_OK) return st;
-    h->seq = a.seq;
-    h->round = a.round;
-    if (seq_out) *seq_out = a.seq;
+    after_dispatch(h, a, seq_out);
+    return EP_OK;
+}
+
+ep_status ep_layout_dispatch(ep_handle* h, const int32_t* topk_idx, const float* topk_weights,
+                             int32_t num_tokens, const void* x, int32_t hidden, void* pool,
+                             void* pool_scales, uint32_t flags, hipStream_t stream,
+                             uint32_t* epoch_out, uint32_t* seq_out) {
+    ep_status cs = check_layout(h, topk_idx, topk_weights, num_tokens);
+    if (cs != EP_OK) return cs;
+    if (flags & EP_DISPATCH_BORROW) return EP_ERR_UNSUPPORTED;
+    cs = check_dispatch(h, num_tokens, x, hidden, pool, pool_scales, flags);
+    if (cs != EP_OK) return cs;
+    const bool fp8 = (flags & EP_DISPATCH_FP8) != 0;
+    const bool ready = (flags & EP_DISPATCH_TILE_READY) != 0;
+    const int64_t slots = (int64_t)num_tokens * h->cfg.top_k;
+    if (ready || num_tokens == 0 || slots > epk::kLayoutSlotsPerBlock) {
+        // the two calls, one after the other (the arguments are already checked)
+        ep_status st = ep_layout(h, topk_idx, topk_weights, num_tokens, stream, epoch_out);
+        if (st != EP_OK) return st;
+        return ep_dispatch(h, x, hidden, pool, pool_scales, flags, stream, seq_out);
+    }
+    ep_status ws = wait_lease(h, stream);
+    if (ws != EP_OK) return ws;
+    const epk::LayoutArgs la = layout_args(h, topk_idx, topk_weights, num_tokens);
+    const epk::DispatchArgs a = dispatch_args(h, num_tokens, 0u, x, hidden, pool, pool_scales, flags);
+    ep_status st = hip_status(epk::launch_layout_dispatch(la, a, fp8, stream));
+    if (st != EP_OK) return st;
+    after_layout(h, num_tokens, stream, epoch_out);
+    after_dispatch(h, a, seq_out);
     return EP_OK;
 }
 

@@ -143,6 +143,10 @@ struct CastBackArgs {
 };
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
+// The one-workgroup layout and the dispatch of its tokens in one launch
+// (la.S <= kLayoutSlotsPerBlock, T > 0, no streaming release): the same
+// results as launch_layout followed by launch_dispatch.
+hipError_t launch_layout_dispatch(const LayoutArgs& la, const DispatchArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_dispatch(const DispatchArgs& a, bool fp8, bool tile_ready, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_combine_gated(const CombineArgs& a, hipStream_t stream);

@@ -76,6 +76,11 @@ constexpr int kLayoutWaves = kLayoutThreads / kWave;
 constexpr int kSlotsPerLane = kLayoutSlotsPerBlock / kLayoutThreads;   // slots per lane
 constexpr int kWaveSlots = kLayoutSlotsPerBlock / kLayoutWaves;       // slots per wave
 
+// Dynamic LDS of the rank launch: s_base, s_cnt, s_off, s_tmp and the per-wave counts.
+inline size_t layout_rank_lds(int E) {
+    return sizeof(int) * (size_t)(3 * E + 1 + kLayoutWaves) + sizeof(uint16_t) * (size_t)kLayoutWaves * E;
+}
+
 __device__ __forceinline__ int uniform_i(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // The hardware hands workgroup b to XCD b mod 8.  This bijection of [0, G)
@@ -217,13 +222,18 @@ __device__ __forceinline__ void report_density(const LayoutArgs& a, int rows) {
                        __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// Layout ranks.  FUSED: the whole layout in this one workgroup (nb == 1, no
-// histogram launch).  Otherwise launch 2 of the multi-workgroup layout: the
-// workgroup sums the histograms of the workgroups before it and of all of
-// them, scans tiles over experts, and ranks its own kLayoutSlotsPerBlock slots.  Every
+// Layout ranks, run by workgroup b of nb (kLayoutThreads threads).  FUSED:
+// the whole layout in this one workgroup (nb == 1, b == 0, no histogram
+// launch).  Otherwise launch 2 of the multi-workgroup layout: the workgroup
+// sums the histograms of the workgroups before it and of all of them, scans
+// tiles over experts, and ranks its own kLayoutSlotsPerBlock slots.  Every
 // workgroup writes its share of the tile metadata and of the padding rows.
-template <bool FUSED>
-__global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, int nb, int lg_tpe) {
+// ROWS_ONLY (with FUSED): only the pool row of every slot, into rows_out (LDS,
+// S entries, -1 for a masked slot); nothing is written to global memory.
+template <bool FUSED, bool ROWS_ONLY>
+__device__ __forceinline__ void layout_rank_body(const LayoutArgs& a, int nb, int lg_tpe, int b,
+                                                 int32_t* rows_out) {
+    static_assert(FUSED || !ROWS_ONLY, "rows only for the one-workgroup layout");
     extern __shared__ int smem[];
     __shared__ int s_rows;                              // real rows (density report)
     const int E = a.E, BM = a.BM;
@@ -234,7 +244,6 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
     uint16_t* wc = (uint16_t*)(s_tmp + kLayoutWaves);   // [16][E] per-wave counts, then next ranks
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int w = uniform_i(tid / kWave);
-    const int b = (int)blockIdx.x;
     const int nbits = key_bits(E);
     const int base = b * kLayoutSlotsPerBlock + w * kWaveSlots;
     if (tid == 0) s_rows = 0;                           // ordered before the adds by the barriers below
@@ -246,7 +255,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
 #pragma unroll
     for (int j = 0; j < kSlotsPerLane; ++j) {
         const int s = base + j * kWave + lane;
-        wv[j] = (s < a.S && a.topk_w) ? a.topk_w[s] : 0.0f;
+        wv[j] = (!ROWS_ONLY && s < a.S && a.topk_w) ? a.topk_w[s] : 0.0f;
     }
     for (int i = tid; i < kLayoutWaves * E; i += kLayoutThreads) wc[i] = 0;
 
@@ -305,17 +314,19 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
             wc[w * E + key[i]] += (uint16_t)__popcll(m[i]);
         if constexpr (FUSED) nvalid += __popcll(__ballot(key[i] < E));
     }
-    if (FUSED && lane == 0 && nvalid) atomicAdd(&s_rows, nvalid);
+    if (FUSED && !ROWS_ONLY && lane == 0 && nvalid) atomicAdd(&s_rows, nvalid);
     // The handle's copy of the weights (this wave's slots, as the keys).  On
     // gfx9 a wait for a load also waits for every store issued before it, so
     // global stores are kept after the last global load is consumed.
+    if constexpr (!ROWS_ONLY) {
 #pragma unroll
-    for (int j = 0; j < kSlotsPerLane; ++j) {
-        const int s = base + j * kWave + lane;
-        if (s < a.S && a.weights) a.weights[s] = wv[j];
+        for (int j = 0; j < kSlotsPerLane; ++j) {
+            const int s = base + j * kWave + lane;
+            if (s < a.S && a.weights) a.weights[s] = wv[j];
+        }
     }
     __syncthreads();
-    if (FUSED && tid == 0) report_density(a, s_rows);
+    if (FUSED && !ROWS_ONLY && tid == 0) report_density(a, s_rows);
 
     // exclusive prefix of the per-wave counts over waves; the last running sum
     // is the expert's count in this workgroup (E <= kLayoutThreads)
@@ -331,7 +342,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
         }
     }
     if constexpr (FUSED) {
-        if (a.error && __ballot(bad) && lane == 0) atomicOr(a.error, 1u);
+        if (!ROWS_ONLY && a.error && __ballot(bad) && lane == 0) atomicOr(a.error, 1u);
         const int tiles = (tid < E) ? (run + BM - 1) / BM : 0;
         // with E <= 64 wave 0 holds every expert and scans without a barrier
         const int off = E <= kWave ? wave_exclusive_scan(tiles, total)
@@ -361,13 +372,19 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
         if (s < a.S) {
             if (k < E) {
                 const int row = s_base[k] + cur + __popcll(m[i] & lanemask_lt());
-                a.slot_to_row[s] = row;
-                a.recv_token[row] = s / a.K;
+                if constexpr (ROWS_ONLY) {
+                    rows_out[s] = row;
+                } else {
+                    a.slot_to_row[s] = row;
+                    a.recv_token[row] = s / a.K;
+                }
             } else {
-                a.slot_to_row[s] = -1;
+                if constexpr (ROWS_ONLY) rows_out[s] = -1;
+                else a.slot_to_row[s] = -1;
             }
         }
     }
+    if constexpr (ROWS_ONLY) return;
 
     // Tile metadata and padding rows, expert by expert (expert e's tiles are
     // [s_off[e], s_off[e+1]) and its padding rows follow its s_cnt[e] real
@@ -425,6 +442,11 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
         }
         if (tid == 0) *a.num_tiles = s_off[E];
     }
+}
+
+template <bool FUSED>
+__global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, int nb, int lg_tpe) {
+    layout_rank_body<FUSED, false>(a, nb, lg_tpe, (int)blockIdx.x, nullptr);
 }
 
 // ------------------------------------------------------------- dispatch ---
@@ -525,8 +547,11 @@ __device__ __forceinline__ bool load_rows(const int32_t* s2r, int t, int K, int 
 // round-robin.  In streaming mode ipb is a whole number of tokens.  With MANY
 // an item's first slot group is loaded ahead and the later groups' rows are
 // read as they are stored (an item is never skipped).
+// Workgroup bid of the dispatch; s2r is the slot -> pool row map (the
+// handle's, or one a fused layout has just built in LDS).
 template <int KT, bool STREAM, bool MANY>
-__global__ __launch_bounds__(1024) void k_dispatch_bf16(DispatchArgs a, int nseg, int ipb) {
+__device__ __forceinline__ void dispatch_bf16_body(const DispatchArgs& a, int nseg, int ipb, int bid,
+                                                   const int32_t* s2r) {
     constexpr int U = kDispatchChunks;
     const int lane = threadIdx.x & (kWave - 1);
     const int w = uniform_i(threadIdx.x / kWave);
@@ -541,14 +566,14 @@ __global__ __launch_bounds__(1024) void k_dispatch_bf16(DispatchArgs a, int nseg
         if (threadIdx.x == 0) s_done = 0u;
         __syncthreads();
     }
-    const int i0 = (int)blockIdx.x * ipb;
+    const int i0 = bid * ipb;
     const int i1 = min(a.T * nseg, i0 + ipb);
     // software-pipelined as in the FP8 dispatch: the next item's rows and x
     // segment are loaded before the current one is stored
     auto fetch = [&](int it_, int (&r)[KT], u32x4 (&v_)[U]) -> bool {
         const int t_ = it_ / nseg;
         const int seg_ = it_ - t_ * nseg;
-        if (!load_rows<KT>(a.slot_to_row, t_, a.K, 0, r) && !MANY) return false;
+        if (!load_rows<KT>(s2r, t_, a.K, 0, r) && !MANY) return false;
         const int c0_ = seg_ * (kWave * U) + lane;
         const u32x4* src_ = x + (int64_t)t_ * n16;
 #pragma unroll
@@ -576,7 +601,7 @@ __global__ __launch_bounds__(1024) void k_dispatch_bf16(DispatchArgs a, int nseg
         const int c0 = seg * (kWave * U) + lane;
         const int ngroups = slot_groups<MANY, KT>(a.K);
         for (int g = 0; g < ngroups; ++g) {
-            if (MANY && g > 0) load_rows<KT>(a.slot_to_row, t, a.K, g * KT, rows);
+            if (MANY && g > 0) load_rows<KT>(s2r, t, a.K, g * KT, rows);
 #pragma unroll
             for (int k = 0; k < KT; ++k) {
                 if (rows[k] < 0) continue;
@@ -590,6 +615,11 @@ __global__ __launch_bounds__(1024) void k_dispatch_bf16(DispatchArgs a, int nseg
         }
     }
     if constexpr (STREAM) release_chunk(a, i0 / nseg, i1 / nseg, &s_done);
+}
+
+template <int KT, bool STREAM, bool MANY>
+__global__ __launch_bounds__(1024) void k_dispatch_bf16(DispatchArgs a, int nseg, int ipb) {
+    dispatch_bf16_body<KT, STREAM, MANY>(a, nseg, ipb, (int)blockIdx.x, a.slot_to_row);
 }
 
 // bf16 dispatch for dense routing (4 or more rows per token) without the
@@ -818,7 +848,8 @@ __device__ __forceinline__ void store_scales(const DispatchArgs& a, const int (&
 // UE8M0 exponent (stored as a byte, or as the float 2^e).  U: 16-channel
 // units per lane per work item.
 template <int KT, bool STREAM, bool F32Q, int U, bool MANY>
-__global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg, int ipb) {
+__device__ __forceinline__ void dispatch_fp8_body(const DispatchArgs& a, int nseg, int ipb, int bid, int nblk,
+                                                  const int32_t* s2r) {
     const int lane = threadIdx.x & (kWave - 1);
     const int w = uniform_i(threadIdx.x / kWave);
     const int nunit = a.H / 16;          // 16 channels (32 bytes in, 16 bytes out) per unit
@@ -839,8 +870,7 @@ __global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg,
     // L2 before they are written back, instead of in pieces from all eight
     // (measured 1-11 % faster for the float flavours at 16384 tokens; bf16
     // and UE8M0 keep the round-robin, which measured slightly faster there).
-    const int blk = a.scale_kind != kScaleUe8m0 ? xcd_contiguous_block((int)blockIdx.x, (int)gridDim.x)
-                                                : (int)blockIdx.x;
+    const int blk = a.scale_kind != kScaleUe8m0 ? xcd_contiguous_block(bid, nblk) : bid;
     const int i0 = blk * ipb;
     const int i1 = min(a.T * nseg, i0 + ipb);
     // a wave's items are software-pipelined: the next item's rows and x
@@ -848,7 +878,7 @@ __global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg,
     auto fetch = [&](int it_, int (&r)[KT], u32x4 (&l)[U], u32x4 (&h)[U]) -> bool {
         const int t_ = it_ / nseg;
         const int seg_ = it_ - t_ * nseg;
-        if (!load_rows<KT>(a.slot_to_row, t_, a.K, 0, r) && !MANY) return false;
+        if (!load_rows<KT>(s2r, t_, a.K, 0, r) && !MANY) return false;
         const int u0_ = seg_ * (kWave * U) + lane;
         const u32x4* src_ = x + (int64_t)t_ * (a.H / 8);
 #pragma unroll
@@ -956,7 +986,7 @@ __global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg,
                 int rg[KT];
 #pragma unroll
                 for (int k = 0; k < KT; ++k) rg[k] = rows[k];
-                if (MANY && g > 0) load_rows<KT>(a.slot_to_row, t, a.K, g * KT, rg);
+                if (MANY && g > 0) load_rows<KT>(s2r, t, a.K, g * KT, rg);
                 if (c < nunit) {
 #pragma unroll
                     for (int k = 0; k < KT; ++k) {
@@ -969,6 +999,11 @@ __global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg,
         }
     }
     if constexpr (STREAM) release_chunk(a, i0 / nseg, i1 / nseg, &s_done);
+}
+
+template <int KT, bool STREAM, bool F32Q, int U, bool MANY>
+__global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg, int ipb) {
+    dispatch_fp8_body<KT, STREAM, F32Q, U, MANY>(a, nseg, ipb, (int)blockIdx.x, (int)gridDim.x, a.slot_to_row);
 }
 
 // -------------------------------------------------------------- combine ---
@@ -1660,6 +1695,41 @@ __global__ __launch_bounds__(256) void k_cast_back(CastBackArgs a, int nseg) {
     }
 }
 
+// ----------------------------------- layout and dispatch in one launch ---
+
+// For at most kLayoutSlotsPerBlock slots (decode-sized batches): workgroup 0
+// runs the whole one-workgroup layout, writing every array the layout writes,
+// while every other workgroup builds the slot -> pool row map by itself in
+// LDS from topk_idx, with the same code (a slot's row depends only on the
+// routing), and then dispatches its share of the items.  One launch and one
+// trip through topk_idx instead of a layout kernel the dispatch has to wait
+// for.
+template <int KT, bool MANY>
+__global__ __launch_bounds__(kLayoutThreads) void k_layout_dispatch_bf16(LayoutArgs la, DispatchArgs a, int nseg,
+                                                                        int ipb) {
+    __shared__ int32_t s2r[kLayoutSlotsPerBlock];
+    if (blockIdx.x == 0) {
+        layout_rank_body<true, false>(la, 1, 0, 0, nullptr);
+        return;
+    }
+    layout_rank_body<true, true>(la, 1, 0, 0, s2r);
+    __syncthreads();
+    dispatch_bf16_body<KT, false, MANY>(a, nseg, ipb, (int)blockIdx.x - 1, s2r);
+}
+
+template <int KT, bool F32Q, int U, bool MANY>
+__global__ __launch_bounds__(kLayoutThreads) void k_layout_dispatch_fp8(LayoutArgs la, DispatchArgs a, int nseg,
+                                                                       int ipb) {
+    __shared__ int32_t s2r[kLayoutSlotsPerBlock];
+    if (blockIdx.x == 0) {
+        layout_rank_body<true, false>(la, 1, 0, 0, nullptr);
+        return;
+    }
+    layout_rank_body<true, true>(la, 1, 0, 0, s2r);
+    __syncthreads();
+    dispatch_fp8_body<KT, false, F32Q, U, MANY>(a, nseg, ipb, (int)blockIdx.x - 1, (int)gridDim.x - 1, s2r);
+}
+
 // ------------------------------------------------------------- launchers ---
 
 // Items per workgroup: one per wave of 4, or the streaming chunk's whole tokens.
@@ -1764,8 +1834,7 @@ hipError_t combine_bwd_kt(const CombineBwdArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
-    const size_t lds_rank = sizeof(int) * (size_t)(3 * a.E + 1 + kLayoutWaves) +
-                            sizeof(uint16_t) * (size_t)kLayoutWaves * a.E;
+    const size_t lds_rank = layout_rank_lds(a.E);
     if (a.S <= kLayoutSlotsPerBlock) {
         hipLaunchKernelGGL((k_layout_rank<true>), dim3(1), dim3(kLayoutThreads), lds_rank, stream,
                            a, 1, 0);
@@ -1787,6 +1856,28 @@ hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int KT, bool MANY>
+hipError_t layout_dispatch_kt(const LayoutArgs& la, const DispatchArgs& a, bool fp8, hipStream_t st) {
+    const int per_seg = fp8 ? kWave * kFp8Units * 16 : kWave * kDispatchChunks * 8;  // channels
+    const int nseg = (a.H + per_seg - 1) / per_seg;
+    const int ipb = kLayoutWaves;                   // one item per wave
+    const int64_t items = (int64_t)a.T * nseg;
+    const int grid = 1 + (int)((items + ipb - 1) / ipb);
+    const size_t lds = layout_rank_lds(la.E);
+    if (fp8) {
+        if (a.scale_kind == kScaleF32)
+            hipLaunchKernelGGL((k_layout_dispatch_fp8<KT, true, kFp8Units, MANY>), dim3(grid), dim3(kLayoutThreads),
+                               lds, st, la, a, nseg, ipb);
+        else
+            hipLaunchKernelGGL((k_layout_dispatch_fp8<KT, false, kFp8Units, MANY>), dim3(grid), dim3(kLayoutThreads),
+                               lds, st, la, a, nseg, ipb);
+    } else {
+        hipLaunchKernelGGL((k_layout_dispatch_bf16<KT, MANY>), dim3(grid), dim3(kLayoutThreads), lds, st, la, a,
+                           nseg, ipb);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_dispatch(const DispatchArgs& a, bool fp8, bool tile_ready, hipStream_t stream) {
     if (a.T == 0) return hipSuccess;
     if (a.K <= 1) return dispatch_kt<1, false>(a, fp8, tile_ready, stream);
@@ -1794,6 +1885,15 @@ hipError_t launch_dispatch(const DispatchArgs& a, bool fp8, bool tile_ready, hip
     if (a.K <= 4) return dispatch_kt<4, false>(a, fp8, tile_ready, stream);
     if (a.K <= kSlotGroup) return dispatch_kt<kSlotGroup, false>(a, fp8, tile_ready, stream);
     return dispatch_kt<kSlotGroup, true>(a, fp8, tile_ready, stream);
+}
+
+hipError_t launch_layout_dispatch(const LayoutArgs& la, const DispatchArgs& a, bool fp8, hipStream_t stream) {
+    if (a.T == 0 || la.S > kLayoutSlotsPerBlock) return hipErrorInvalidValue;
+    if (a.K <= 1) return layout_dispatch_kt<1, false>(la, a, fp8, stream);
+    if (a.K <= 2) return layout_dispatch_kt<2, false>(la, a, fp8, stream);
+    if (a.K <= 4) return layout_dispatch_kt<4, false>(la, a, fp8, stream);
+    if (a.K <= kSlotGroup) return layout_dispatch_kt<kSlotGroup, false>(la, a, fp8, stream);
+    return layout_dispatch_kt<kSlotGroup, true>(la, a, fp8, stream);
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {

@@ -228,6 +228,24 @@ ep_status ep_dispatch(ep_handle* h, const void* x, int32_t hidden, void* pool,
  * ep_combine and ep_handle_destroy return EP_ERR_HANDLE_STATE until
  * ep_borrow_release.  The caller keeps x alive and unchanged meanwhile. */
 
+/* ep_layout followed by ep_dispatch in one call, for batches small enough
+ * that launch latency dominates (instagit DeepEP low-latency page,
+ * "Low-Latency Dispatch Kernel" and "API Signature and Return Values": the
+ * decoding dispatch takes x and topk_idx together and returns the per-expert
+ * rows, their counts and the handle).  Arguments as for the two calls (x must have
+ * num_tokens rows); EP_DISPATCH_BORROW is EP_ERR_UNSUPPORTED.  For at most
+ * 2048 slots (num_tokens * top_k) and without EP_DISPATCH_TILE_READY the two
+ * run as one kernel launch: one workgroup writes the layout while every other
+ * workgroup builds the slot -> pool row map by itself from topk_idx and
+ * dispatches its share; otherwise this calls ep_layout and then ep_dispatch.
+ * The device results, the epoch (epoch_out) and the sequence number (seq_out,
+ * may be NULL) are those of the two calls.  Every argument is checked before
+ * anything is enqueued. */
+ep_status ep_layout_dispatch(ep_handle* h, const int32_t* topk_idx, const float* topk_weights,
+                             int32_t num_tokens, const void* x, int32_t hidden, void* pool,
+                             void* pool_scales, uint32_t flags, hipStream_t stream,
+                             uint32_t* epoch_out, uint32_t* seq_out);
+
 /* Weighted sum back in original token order ([WEIGHTS], [ROUND]).
  *   epoch       the value ep_layout returned; else EP_ERR_HANDLE_STATE.
  *   expert_out  device bf16 [capacity_rows, hidden]; only real rows are read.

@@ -92,6 +92,8 @@ def test_null_handle_calls_are_rejected():
     assert lib.ep_layout(None, None, None, 0, None, None) == ep.EP_ERR_INVALID_ARGUMENT
     assert lib.ep_dispatch(None, None, 128, None, None, 0, None, None) == ep.EP_ERR_INVALID_ARGUMENT
     assert lib.ep_combine(None, 1, None, 128, None, None) == ep.EP_ERR_INVALID_ARGUMENT
+    assert lib.ep_layout_dispatch(None, None, None, 0, None, 128, None, None, 0, None, None, None) \
+        == ep.EP_ERR_INVALID_ARGUMENT
     assert lib.ep_handle_destroy(None) == ep.EP_OK
     assert lib.ep_pool_capacity_rows(None) == -1 and lib.ep_max_tiles(None) == -1
     assert lib.ep_handle_create(None, None) == ep.EP_ERR_INVALID_ARGUMENT
