@@ -549,9 +549,11 @@ __device__ __forceinline__ bool load_rows(const int32_t* s2r, int t, int K, int 
 // read as they are stored (an item is never skipped).
 // Workgroup bid of the dispatch; s2r is the slot -> pool row map (the
 // handle's, or one a fused layout has just built in LDS).
-template <int KT, bool STREAM, bool MANY>
+// PRE: the x segment of the wave's first item is already in pre (loaded by
+// the caller before it built s2r, so that the two waits overlap).
+template <int KT, bool STREAM, bool MANY, bool PRE = false>
 __device__ __forceinline__ void dispatch_bf16_body(const DispatchArgs& a, int nseg, int ipb, int bid,
-                                                   const int32_t* s2r) {
+                                                   const int32_t* s2r, const u32x4 (&pre)[kDispatchChunks]) {
     constexpr int U = kDispatchChunks;
     const int lane = threadIdx.x & (kWave - 1);
     const int w = uniform_i(threadIdx.x / kWave);
@@ -585,7 +587,16 @@ __device__ __forceinline__ void dispatch_bf16_body(const DispatchArgs& a, int ns
     };
     int rows_n[KT];
     u32x4 v_n[U];
-    bool any_n = (i0 + w < i1) && fetch(i0 + w, rows_n, v_n);
+    bool any_n = false;
+    if (i0 + w < i1) {
+        if constexpr (PRE) {
+            any_n = load_rows<KT>(s2r, (i0 + w) / nseg, a.K, 0, rows_n) || MANY;
+#pragma unroll
+            for (int u = 0; u < U; ++u) v_n[u] = pre[u];
+        } else {
+            any_n = fetch(i0 + w, rows_n, v_n);
+        }
+    }
     for (int it = i0 + w; it < i1; it += nw) {
         const int t = it / nseg;
         const int seg = it - t * nseg;
@@ -619,7 +630,8 @@ __device__ __forceinline__ void dispatch_bf16_body(const DispatchArgs& a, int ns
 
 template <int KT, bool STREAM, bool MANY>
 __global__ __launch_bounds__(1024) void k_dispatch_bf16(DispatchArgs a, int nseg, int ipb) {
-    dispatch_bf16_body<KT, STREAM, MANY>(a, nseg, ipb, (int)blockIdx.x, a.slot_to_row);
+    const u32x4 none[kDispatchChunks] = {};
+    dispatch_bf16_body<KT, STREAM, MANY>(a, nseg, ipb, (int)blockIdx.x, a.slot_to_row, none);
 }
 
 // bf16 dispatch for dense routing (4 or more rows per token) without the
@@ -847,9 +859,12 @@ __device__ __forceinline__ void store_scales(const DispatchArgs& a, const int (&
 // F32Q: float32 scale amax / 448 and codes of x * (448 / amax); otherwise the
 // UE8M0 exponent (stored as a byte, or as the float 2^e).  U: 16-channel
 // units per lane per work item.
-template <int KT, bool STREAM, bool F32Q, int U, bool MANY>
+// PRE: the x units of the wave's first item are already in pre_lo / pre_hi
+// (loaded by the caller before it built s2r).
+template <int KT, bool STREAM, bool F32Q, int U, bool MANY, bool PRE = false>
 __device__ __forceinline__ void dispatch_fp8_body(const DispatchArgs& a, int nseg, int ipb, int bid, int nblk,
-                                                  const int32_t* s2r) {
+                                                  const int32_t* s2r, const u32x4 (&pre_lo)[U],
+                                                  const u32x4 (&pre_hi)[U]) {
     const int lane = threadIdx.x & (kWave - 1);
     const int w = uniform_i(threadIdx.x / kWave);
     const int nunit = a.H / 16;          // 16 channels (32 bytes in, 16 bytes out) per unit
@@ -896,7 +911,19 @@ __device__ __forceinline__ void dispatch_fp8_body(const DispatchArgs& a, int nse
     };
     int rows_n[KT];
     u32x4 lo_n[U], hi_n[U];
-    bool any_n = (i0 + w < i1) && fetch(i0 + w, rows_n, lo_n, hi_n);
+    bool any_n = false;
+    if (i0 + w < i1) {
+        if constexpr (PRE) {
+            any_n = load_rows<KT>(s2r, (i0 + w) / nseg, a.K, 0, rows_n) || MANY;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                lo_n[u] = pre_lo[u];
+                hi_n[u] = pre_hi[u];
+            }
+        } else {
+            any_n = fetch(i0 + w, rows_n, lo_n, hi_n);
+        }
+    }
     for (int it = i0 + w; it < i1; it += nw) {
         const int t = it / nseg;
         const int seg = it - t * nseg;
@@ -1003,7 +1030,9 @@ __device__ __forceinline__ void dispatch_fp8_body(const DispatchArgs& a, int nse
 
 template <int KT, bool STREAM, bool F32Q, int U, bool MANY>
 __global__ __launch_bounds__(1024) void k_dispatch_fp8(DispatchArgs a, int nseg, int ipb) {
-    dispatch_fp8_body<KT, STREAM, F32Q, U, MANY>(a, nseg, ipb, (int)blockIdx.x, (int)gridDim.x, a.slot_to_row);
+    const u32x4 none[U] = {};
+    dispatch_fp8_body<KT, STREAM, F32Q, U, MANY>(a, nseg, ipb, (int)blockIdx.x, (int)gridDim.x, a.slot_to_row,
+                                                 none, none);
 }
 
 // -------------------------------------------------------------- combine ---
@@ -1707,14 +1736,29 @@ __global__ __launch_bounds__(256) void k_cast_back(CastBackArgs a, int nseg) {
 template <int KT, bool MANY>
 __global__ __launch_bounds__(kLayoutThreads) void k_layout_dispatch_bf16(LayoutArgs la, DispatchArgs a, int nseg,
                                                                         int ipb) {
+    constexpr int U = kDispatchChunks;
     __shared__ int32_t s2r[kLayoutSlotsPerBlock];
     if (blockIdx.x == 0) {
         layout_rank_body<true, false>(la, 1, 0, 0, nullptr);
         return;
     }
+    // the x segment of this wave's first item is loaded before the layout's
+    // keys, so that the two memory waits overlap
+    const int lane = threadIdx.x & (kWave - 1);
+    const int bid = (int)blockIdx.x - 1;
+    const int it0 = bid * ipb + uniform_i(threadIdx.x / kWave);
+    u32x4 pre[U] = {};
+    if (it0 < a.T * nseg) {
+        const int t = it0 / nseg, n16 = a.H / 8;
+        const int c0 = (it0 - t * nseg) * (kWave * U) + lane;
+        const u32x4* src = (const u32x4*)a.x + (int64_t)t * n16;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (c0 + u * kWave < n16) pre[u] = src[c0 + u * kWave];
+    }
     layout_rank_body<true, true>(la, 1, 0, 0, s2r);
     __syncthreads();
-    dispatch_bf16_body<KT, false, MANY>(a, nseg, ipb, (int)blockIdx.x - 1, s2r);
+    dispatch_bf16_body<KT, false, MANY, true>(a, nseg, ipb, bid, s2r, pre);
 }
 
 template <int KT, bool F32Q, int U, bool MANY>
@@ -1725,9 +1769,30 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_dispatch_fp8(LayoutAr
         layout_rank_body<true, false>(la, 1, 0, 0, nullptr);
         return;
     }
+    // the x units of this wave's first item are loaded before the layout's
+    // keys, so that the two memory waits overlap (the item as the dispatch
+    // body assigns it)
+    const int lane = threadIdx.x & (kWave - 1);
+    const int bid = (int)blockIdx.x - 1, nblk = (int)gridDim.x - 1;
+    const int blk = a.scale_kind != kScaleUe8m0 ? xcd_contiguous_block(bid, nblk) : bid;
+    const int it0 = blk * ipb + uniform_i(threadIdx.x / kWave);
+    u32x4 lo[U] = {}, hi[U] = {};
+    if (it0 < a.T * nseg) {
+        const int t = it0 / nseg, nunit = a.H / 16;
+        const int u0 = (it0 - t * nseg) * (kWave * U) + lane;
+        const u32x4* src = (const u32x4*)a.x + (int64_t)t * (a.H / 8);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = u0 + u * kWave;
+            if (c < nunit) {
+                lo[u] = src[2 * c];
+                hi[u] = src[2 * c + 1];
+            }
+        }
+    }
     layout_rank_body<true, true>(la, 1, 0, 0, s2r);
     __syncthreads();
-    dispatch_fp8_body<KT, false, F32Q, U, MANY>(a, nseg, ipb, (int)blockIdx.x - 1, (int)gridDim.x - 1, s2r);
+    dispatch_fp8_body<KT, false, F32Q, U, MANY, true>(a, nseg, ipb, bid, nblk, s2r, lo, hi);
 }
 
 // ------------------------------------------------------------- launchers ---
