@@ -180,3 +180,64 @@ def test_layout_dispatch_rejections():
     assert h.num_tokens < 0
     assert h.sync_status() == ep.EP_OK
     h.close()
+
+
+def test_layout_dispatch_in_graph():
+    """ep_layout_dispatch + ep_combine captured in a HIP graph and replayed on
+    new inputs written into the captured buffers: every replay's layout,
+    pool, scales and y equal an eager run's (two fused calls per replay)."""
+    import combine_ep_layout_amd as ep
+    say("[layout+dispatch] captured in a graph, 3 replays")
+    cfg = CONFIGS["decode"].replace(tokens=200, hidden=1024)
+    T, K, H = cfg.tokens, cfg.top_k, cfg.hidden
+    h = new_handle(cfg)
+    cap = h.capacity_rows
+    idx = torch.empty(T, K, dtype=torch.int32, device=dev())
+    w = torch.empty(T, K, dtype=torch.float32, device=dev())
+    x = torch.empty(T, H, dtype=torch.bfloat16, device=dev())
+    eo = torch.empty(cap, H, dtype=torch.bfloat16, device=dev())
+    pool, sc = _pool(h, H, True)
+    y = torch.empty(T, H, dtype=torch.bfloat16, device=dev())
+
+    def load(seed):
+        d = generate(cfg, seed)
+        idx.copy_(torch.from_numpy(d["topk_idx"]))
+        w.copy_(torch.from_numpy(d["topk_weights"]))
+        x.copy_(to_dev_bf16(d["x"]))
+        eo.copy_(torch.randn(cap, H, generator=torch.Generator().manual_seed(seed)).to(torch.bfloat16))
+        return d
+
+    def step():
+        e, _ = h.layout_dispatch(idx, w, x, pool, sc, fp8=True)
+        h.combine(e, eo, y)
+
+    load(0)
+    s = torch.cuda.Stream()                              # default priority
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.synchronize()
+    h.set_density_hint(ep.EP_DENSITY_DENSE)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+        step()
+    torch.cuda.synchronize()
+    for seed in (1, 2, 3):
+        d = load(seed)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (h.array("slot_to_pool_row").clone(), pool.clone(), sc.clone(), y.clone())
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], h.array("slot_to_pool_row"))
+        L = oracle.layout(d["topk_idx"], cfg.num_experts, cfg.block_m)
+        assert np.array_equal(got[0].cpu().numpy(), L["slot_to_pool_row"])
+        assert torch.equal(got[1], pool) and torch.equal(got[2], sc)
+        assert torch.equal(got[3].view(torch.int16), y.view(torch.int16))
+        say(f"  replay with seed {seed} matches the eager step")
+    assert h.sync_status() == ep.EP_OK
+    del g
+    h.close()
