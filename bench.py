@@ -765,11 +765,13 @@ def ceiling_bench(cfg, steps: int, warmup: int) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20; 200 for the launch-bound tiny and decode workloads)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--cpu-reps", type=int, default=None,
+                    help="oracle passes, median taken (default 3 for prefill and stream, 11 otherwise)")
     ap.add_argument("--cpu-tokens", type=int, default=-1,
                     help="tokens of the CPU-oracle sample (default: all for bf16, 1024 for FP8)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -796,6 +798,10 @@ def main() -> int:
                     help="print the streaming dispatch / tile consumer overlap measurement instead "
                          "(default workload: stream)")
     args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 200 if args.config in ("tiny", "decode") else 20
+    if args.cpu_reps is None:
+        args.cpu_reps = 3 if args.config in ("prefill", "stream") else 11
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of EP dispatch/combine; runs on more than "
