@@ -498,7 +498,7 @@ __device__ void release_chunk(const DispatchArgs& a, int t0, int t1, uint32_t* s
 // leave no dirty line behind, which keeps a later device-scope release (and
 // the end-of-kernel write-back) cheap, and they count as complete only once
 // every XCD can see them, which the streaming release relies on.
-enum StoreMode { kStoreNonTemporal, kStoreDevice, kStoreDeviceNonTemporal };
+enum StoreMode { kStoreNonTemporal, kStoreDeviceNonTemporal };
 
 template <StoreMode MODE>
 __device__ __forceinline__ void store_row(u32x4* row, int row_bytes, int c, const u32x4& v) {
@@ -506,16 +506,17 @@ __device__ __forceinline__ void store_row(u32x4* row, int row_bytes, int c, cons
         __builtin_nontemporal_store(v, row + c);
     } else {
         __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(row, (short)0, row_bytes, 0x00020000);
-        __builtin_amdgcn_raw_buffer_store_b128(
-            v, r, c * 16, 0, MODE == kStoreDevice ? kAuxDevice : kAuxDevice | kAuxNonTemporal);
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, c * 16, 0, kAuxDevice | kAuxNonTemporal);
     }
 }
 
-// Pool rows: device-scope non-temporal stores, plain device-scope ones with
-// the streaming release (measured faster there).
-template <bool STREAM>
+// Pool rows, with or without the streaming release: device-scope
+// non-temporal stores.  (Device-scope stores without the non-temporal hint
+// made the streaming dispatch faster only when a cache flush ran between
+// steps: they leave the rows dirty in the last-level cache, and the flush
+// then writes them back; back to back they were 11 % slower.)
 __device__ __forceinline__ void store_pool(u32x4* row, int row_bytes, int c, const u32x4& v) {
-    store_row<STREAM ? kStoreDevice : kStoreDeviceNonTemporal>(row, row_bytes, c, v);
+    store_row<kStoreDeviceNonTemporal>(row, row_bytes, c, v);
 }
 
 // Slot groups.  A kernel holds the pool rows (and weights) of at most KT <= 8
@@ -620,7 +621,7 @@ __device__ __forceinline__ void dispatch_bf16_body(const DispatchArgs& a, int ns
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int c = c0 + u * kWave;
-                    if (c < n16) store_pool<STREAM>(dst, a.H * 2, c, v[u]);
+                    if (c < n16) store_pool(dst, a.H * 2, c, v[u]);
                 }
             }
         }
@@ -678,7 +679,7 @@ __global__ __launch_bounds__(kWave * kDenseDispatchWaves) void k_dispatch_bf16_d
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int c = c0 + u * kWave;
-            if (c < n16) store_pool<false>(dst, a.H * 2, c, v[u]);
+            if (c < n16) store_pool(dst, a.H * 2, c, v[u]);
         }
     }
 }
@@ -1018,7 +1019,7 @@ __device__ __forceinline__ void dispatch_fp8_body(const DispatchArgs& a, int nse
 #pragma unroll
                     for (int k = 0; k < KT; ++k) {
                         if (rg[k] < 0) continue;
-                        store_pool<STREAM>(pool + (int64_t)rg[k] * nunit, a.H, c, q);
+                        store_pool(pool + (int64_t)rg[k] * nunit, a.H, c, q);
                     }
                 }
                 store_scales<KT, STREAM>(a, rg, c, nunit, ngrp, pack8, sbyte, sval);
