@@ -49,9 +49,9 @@ constexpr int kDispatchChunks = 2;      // bf16 dispatch: 16-byte chunks per lan
 constexpr int kFp8Units = 1;            // FP8 dispatch: 16-channel units per lane per item
 constexpr int kFp8StreamUnits = 2;      // the same with the streaming release
 constexpr int kCombineChunks = 2;       // combine: 16-byte chunks per lane per item
-constexpr int kDenseDispatchWaves = 4;  // bf16 dispatch, dense routing: waves per (token, segment)
-constexpr int64_t kDenseDispatchMinBytes = int64_t(64) << 20;  // ... for x of at least this size
+constexpr int64_t kDenseDispatchMinBytes = int64_t(64) << 20;  // bf16 dispatch: dense-routing shape from this size of x
 constexpr int kStreamTokens = 2;        // streaming dispatch: tokens per chunk (one workgroup)
+constexpr int kStageGrid = 8192;        // read pass over x before the dense-routing dispatch: workgroups
 constexpr int kStreamThreads = 256;     // streaming dispatch: threads per workgroup
 constexpr int kCombineResidentWaves = 8;   // combine grids up to this many waves per CU: full occupancy
 constexpr int kCombineDenseLds = 55296;    // unused LDS per combine workgroup for dense routing: 2 per CU
@@ -636,52 +636,43 @@ __global__ __launch_bounds__(1024) void k_dispatch_bf16(DispatchArgs a, int nseg
 }
 
 // bf16 dispatch for dense routing (4 or more rows per token) without the
-// streaming release: one workgroup per (token, row segment), its waves
-// splitting the token's slots (wave w stores slots w, w + waves, ...).  Each
-// wave loads the segment once (the other waves of the workgroup find it in
-// the caches) and stores it to at most KT / waves rows.  With fewer bytes per
-// wave, the workgroups in flight cover a narrow window of tokens, and the
-// pool is written faster than by waves that each store all of a token's rows
-// (16384 tokens x top-8, hidden 7168: 383 against 416 us with the caches
-// flushed, 343 against 349 us back to back).  With sparse routing most of
-// its waves would have nothing to store, so k_dispatch_bf16 serves that.
+// streaming release, in two launches.  First a read pass streams x through
+// the caches into the last-level cache (MALL); then one workgroup per (token,
+// 1 KB row segment) has wave k store the segment to slot k's row, one 16-byte
+// access per lane.  Each wave holds 1 KB of stores, so the workgroups in
+// flight cover a narrow window of tokens and the pool is written at close to
+// the rate of sequential writes; their x loads hit the MALL.  Without the
+// read pass the same loads go to HBM in the middle of the write stream and
+// stall the writers (16384 tokens x top-8, hidden 7168, caches flushed: 508
+// against 345 us for both launches; back to back 304 / 338 us).  With
+// sparse routing most of its waves would have nothing to store, so
+// k_dispatch_bf16 serves that.
+
+// The read pass: every 16-byte chunk of x loaded once with plain (cached)
+// loads, several in flight per lane, and folded into a value nothing reads.
+__global__ __launch_bounds__(256) void k_stage_x(const u32x4* x, int64_t n16) {
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    const int64_t stride = (int64_t)gridDim.x * 256;
+#pragma unroll 4
+    for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < n16; c += stride) acc ^= x[c];
+    // a data-dependent branch keeps the loads; it never writes memory
+    if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9E3779B9u) __builtin_amdgcn_s_sleep(1);
+}
+
 template <int KT>
-__global__ __launch_bounds__(kWave * kDenseDispatchWaves) void k_dispatch_bf16_dense(DispatchArgs a, int nseg) {
-    constexpr int WAVES = KT < kDenseDispatchWaves ? KT : kDenseDispatchWaves;
-    constexpr int SPW = KT / WAVES;                 // slots per wave
-    constexpr int U = kDispatchChunks;
+__global__ __launch_bounds__(kWave * KT) void k_dispatch_bf16_dense(DispatchArgs a, int nseg) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int w = uniform_i(threadIdx.x / kWave);
+    const int k = uniform_i(threadIdx.x / kWave);
     const int t = (int)blockIdx.x / nseg;
     const int seg = (int)blockIdx.x - t * nseg;
+    if (k >= a.K) return;
+    const int row = a.slot_to_row[t * a.K + k];
+    if (row < 0) return;
     const int n16 = a.H / 8;
-    int rows[SPW];
-    bool any = false;
-#pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-        const int k = w + j * WAVES;
-        rows[j] = k < a.K ? a.slot_to_row[t * a.K + k] : -1;
-        any |= rows[j] >= 0;
-    }
-    if (!any) return;                               // uniform per wave
-    const int c0 = seg * (kWave * U) + lane;
-    const u32x4* src = (const u32x4*)a.x + (int64_t)t * n16;
-    u32x4 v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int c = c0 + u * kWave;
-        if (c < n16) v[u] = src[c];
-    }
-#pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-        if (rows[j] < 0) continue;
-        u32x4* dst = (u32x4*)a.pool + (int64_t)rows[j] * n16;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int c = c0 + u * kWave;
-            if (c < n16) store_pool(dst, a.H * 2, c, v[u]);
-        }
-    }
+    const int c = seg * kWave + lane;
+    if (c >= n16) return;
+    const u32x4 v = ((const u32x4*)a.x)[(int64_t)t * n16 + c];
+    store_pool((u32x4*)a.pool + (int64_t)row * n16, a.H * 2, c, v);
 }
 
 // --- FP8 e4m3fn with UE8M0 scales, from bf16 bit patterns, integer only ---
@@ -1828,9 +1819,11 @@ hipError_t dispatch_kt(const DispatchArgs& a, bool fp8, bool stream, hipStream_t
         if (stream) {
             hipLaunchKernelGGL((k_dispatch_bf16<KT, true, MANY>), dim3(grid), block, lds, st, a, nseg, ipb);
         } else if (!MANY && a.density == kDensityDense && dispatch_shape_uses_density(a.T, a.H, a.K)) {
-            constexpr int waves = KT < kDenseDispatchWaves ? KT : kDenseDispatchWaves;
-            hipLaunchKernelGGL((k_dispatch_bf16_dense<KT>), dim3((unsigned)items), dim3(kWave * waves), 0, st,
-                               a, nseg);
+            const int dseg = (a.H / 8 + kWave - 1) / kWave;
+            hipLaunchKernelGGL(k_stage_x, dim3(kStageGrid), dim3(256), 0, st, (const u32x4*)a.x,
+                               (int64_t)a.T * (a.H / 8));
+            hipLaunchKernelGGL((k_dispatch_bf16_dense<KT>), dim3((unsigned)((int64_t)a.T * dseg)), dim3(kWave * KT), 0,
+                               st, a, dseg);
         } else {
             hipLaunchKernelGGL((k_dispatch_bf16<KT, false, MANY>), dim3(grid), block, lds, st, a, nseg, ipb);
         }
