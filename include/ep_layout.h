@@ -214,8 +214,9 @@ ep_status ep_layout(ep_handle* h, const int32_t* topk_idx, const float* topk_wei
  * Launch shape: a bf16 dispatch without EP_DISPATCH_TILE_READY, with top_k up
  * to 8 and at least 64 MiB of x, takes its shape from the current layout's
  * routing density as ep_combine does (and may wait for the layout kernel's
- * report on the host in the same way); the pool is the same in every
- * shape. */
+ * report on the host in the same way).  For dense routing that shape is two
+ * launches on `stream`: a read pass over x, then the pool stores.  The pool
+ * is the same in every shape. */
 ep_status ep_dispatch(ep_handle* h, const void* x, int32_t hidden, void* pool,
                       void* pool_scales, uint32_t flags, hipStream_t stream,
                       uint32_t* seq_out);
