@@ -102,6 +102,75 @@ def test_step_in_graph(name, tokens, hidden, fp8):
     h.close()
 
 
+def test_dense_routing_step_in_graph():
+    """The dense-routing bf16 dispatch (a read pass over x, then the pool
+    stores: two launches) captured with its layout and combine: 8192 tokens x
+    hidden 4096 x top-4 (64 MiB of x), the handle's shape hint set to the
+    density its warm-up layout reported.  Each replay on new inputs equals an
+    eager run of a second handle on the same inputs, compared on the device:
+    the row map, y, and every real pool row."""
+    import combine_ep_layout_amd as ep
+    say("[graph] dense-routing bf16 dispatch, 8192 x 4096 top-4")
+    cfg = CONFIGS["prefill"].replace(tokens=8192, hidden=4096, top_k=4)
+    T, K, H = cfg.tokens, cfg.top_k, cfg.hidden
+    h = new_handle(cfg)
+    ref = new_handle(cfg)
+    cap = h.capacity_rows
+    idx = torch.empty(T, K, dtype=torch.int32, device=dev())
+    w = torch.empty(T, K, dtype=torch.float32, device=dev())
+    x = torch.empty(T, H, dtype=torch.bfloat16, device=dev())
+    eo = torch.empty(cap, H, dtype=torch.bfloat16, device=dev())
+    pool, _ = h.new_pool(H)
+    pool_ref, _ = ref.new_pool(H)
+
+    def load(seed):
+        d = generate(cfg, seed)
+        idx.copy_(torch.from_numpy(d["topk_idx"]))
+        w.copy_(torch.from_numpy(d["topk_weights"]))
+        x.copy_(to_dev_bf16(d["x"]))
+        g = torch.Generator(device=dev())
+        g.manual_seed(seed)
+        eo.copy_(torch.randn(cap, H, generator=g, device=dev()).to(torch.bfloat16))
+
+    load(0)
+    s = torch.cuda.Stream()                              # default priority
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                           # warm-up outside the capture
+        epoch = h.layout(idx, w)
+        h.dispatch(x, pool)
+        y = h.combine(epoch, eo)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert h.layout_density() == ep.EP_DENSITY_DENSE
+    h.set_density_hint(ep.EP_DENSITY_DENSE)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        epoch = h.layout(idx, w)
+        h.dispatch(x, pool)
+        h.combine(epoch, eo, y)
+    torch.cuda.synchronize()
+    for seed in (1, 2, 3):
+        load(seed)
+        pool.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e_ref = ref.layout(idx, w)
+        ref.dispatch(x, pool_ref)
+        y_ref = ref.combine(e_ref, eo)
+        torch.cuda.synchronize()
+        assert torch.equal(h.array("slot_to_pool_row"), ref.array("slot_to_pool_row"))
+        assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
+        real = torch.nonzero(ref.array("pool_recv_token") >= 0).flatten()
+        assert real.numel() == int((idx >= 0).sum())
+        assert torch.equal(pool.view(torch.int16)[real], pool_ref.view(torch.int16)[real])
+        say(f"  replay with seed {seed} matches the eager run ({real.numel()} rows)")
+    assert h.sync_status() == 0 and ref.sync_status() == 0
+    del g
+    h.close()
+    ref.close()
+
+
 def test_streaming_dispatch_and_consumer_in_graph():
     """Layout -> streaming FP8 dispatch -> tile consumer captured on one
     stream and replayed on new inputs.  A replay repeats the captured round
