@@ -71,19 +71,23 @@ def _full_size_dispatch(name, fp8):
     h.close()
 
 
-@pytest.mark.parametrize("top_k,hidden", [(1, 4096), (2, 4096), (4, 4096), (8, 4096), (3, 4224), (8, 4224)])
-def test_bf16_dispatch_shapes_write_the_same_pool(top_k, hidden):
+@pytest.mark.parametrize("name,tokens,top_k,hidden", [("prefill", 8192, 1, 4096), ("prefill", 8192, 2, 4096),
+                                                     ("prefill", 8192, 4, 4096), ("prefill", 8192, 8, 4096),
+                                                     ("prefill", 8192, 3, 4224), ("prefill", 8192, 8, 4224),
+                                                     ("share", 16384, 8, 2048)])
+def test_bf16_dispatch_shapes_write_the_same_pool(name, tokens, top_k, hidden):
     """The bf16 dispatch's two launch shapes (a read pass over x, then one
     workgroup per token segment for dense routing; waves over tokens
     otherwise), each forced with the density hint on the same layout, against
     the oracle's layout: every real row is its token's row of x, every
     padding row keeps its poison.  8192 tokens x hidden 4096 (64 MiB of x,
     where the shape depends on the density), and hidden 4224, whose rows end
-    in a partial segment; then the shape the handle takes by itself, for
-    this routing."""
+    in a partial segment; the share routing (about one real row per token)
+    forced into the dense shape as well; then the shape the handle takes by
+    itself, for this routing."""
     import combine_ep_layout_amd as ep
-    say(f"[dispatch bf16] both launch shapes, top_k={top_k}, hidden={hidden}")
-    cfg = CONFIGS["prefill"].replace(tokens=8192, hidden=hidden, top_k=top_k)
+    say(f"[dispatch bf16] both launch shapes, {name} routing, {tokens} tokens, top_k={top_k}, hidden={hidden}")
+    cfg = CONFIGS[name].replace(tokens=tokens, hidden=hidden, top_k=top_k)
     d = generate(cfg, 5)
     L = oracle.layout(d["topk_idx"], cfg.num_experts, cfg.block_m)
     recv = L["pool_recv_token"]
