@@ -18,11 +18,11 @@
 // writes the codes (FP8; instagit DeepEP low-latency page, "FP8 and
 // Quantization Support").  UE8M0 codes come from gfx950's scaled conversion
 // instruction wherever it equals the exact integer encoder, which is kept for
-// the rest.  With the streaming release, each workgroup takes a chunk of two
-// tokens in token order, stores its rows with device-scope stores, and the
-// last of its waves to see its own stores complete raises the arrival count
-// of every tile the chunk wrote; the add that completes a tile stores the
-// sequence number into tile_ready[tile].
+// the rest.  With the streaming release, each workgroup takes one token, in
+// token order, with one wave per row segment; it stores the rows with
+// device-scope stores, and the last of its waves to see its own stores
+// complete raises the arrival count of every tile the token wrote; the add
+// that completes a tile stores the sequence number into tile_ready[tile].
 //
 // Combine is token-major too: a wave gathers one segment of the token's k
 // expert rows, accumulates w * o in fp32 with one fused multiply-add per slot
@@ -47,12 +47,11 @@ namespace {
 // streaming dispatch's chunk.
 constexpr int kDispatchChunks = 2;      // bf16 dispatch: 16-byte chunks per lane per item
 constexpr int kFp8Units = 1;            // FP8 dispatch: 16-channel units per lane per item
-constexpr int kFp8StreamUnits = 2;      // the same with the streaming release
+constexpr int kFp8StreamUnits = 1;      // the same with the streaming release
 constexpr int kCombineChunks = 2;       // combine: 16-byte chunks per lane per item
 constexpr int64_t kDenseDispatchMinBytes = int64_t(64) << 20;  // bf16 dispatch: dense-routing shape from this size of x
-constexpr int kStreamTokens = 2;        // streaming dispatch: tokens per chunk (one workgroup)
+constexpr int kStreamTokens = 1;        // streaming dispatch: tokens per chunk (one workgroup, a wave per segment)
 constexpr int kStageGrid = 8192;        // read pass over x before the dense-routing dispatch: workgroups
-constexpr int kStreamThreads = 256;     // streaming dispatch: threads per workgroup
 constexpr int kCombineResidentWaves = 8;   // combine grids up to this many waves per CU: full occupancy
 constexpr int kCombineDenseLds = 55296;    // unused LDS per combine workgroup for dense routing: 2 per CU
 constexpr int kBwdChunks = 2;           // combine backward: 16-byte chunks per lane in flight
@@ -1804,7 +1803,8 @@ hipError_t dispatch_kt(const DispatchArgs& a, bool fp8, bool stream, hipStream_t
     const int64_t items = (int64_t)a.T * nseg;
     int grid = (int)((items + ipb - 1) / ipb);
     const size_t lds = 0;
-    const dim3 block(stream ? kStreamThreads : 256);
+    // streaming: one wave per item of the chunk (at most 16)
+    const dim3 block(stream ? kWave * (ipb < 16 ? ipb : 16) : 256);
     if (fp8) {
         const bool f32q = a.scale_kind == kScaleF32;
         if (stream && f32q)
