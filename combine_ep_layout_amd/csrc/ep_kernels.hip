@@ -450,7 +450,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_rank(LayoutArgs a, in
 
 // ------------------------------------------------------------- dispatch ---
 
-// Streaming release of one chunk (a few consecutive tokens, one workgroup),
+// Streaming release of one chunk (kStreamTokens consecutive tokens, one workgroup),
 // without a workgroup barrier or a cache write-back.  All of a streaming
 // dispatch's stores (pool rows and scales) are device-scope stores, which the
 // XCD's L2 writes through, so a store counts as complete (vmcnt) only once it
@@ -1788,7 +1788,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout_dispatch_fp8(LayoutAr
 
 // ------------------------------------------------------------- launchers ---
 
-// Items per workgroup: one per wave of 4, or the streaming chunk's whole tokens.
+// Items per workgroup: one per wave of 4, or every segment of the streaming chunk's tokens.
 inline int items_per_block(int nseg, bool stream) {
     return stream ? kStreamTokens * nseg : 4;
 }
