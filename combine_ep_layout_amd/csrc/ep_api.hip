@@ -570,6 +570,9 @@ ep_status ep_combine_backward(const ep_handle* h, uint32_t epoch, const void* gr
     a.weights = h->weights;
     a.grad_eo = grad_expert_out;
     a.grad_w = grad_weights;
+    a.num_cu = h->num_cu;
+    // launch shape from the layout's routing density, as ep_combine
+    a.density = current_density(h, epk::combine_bwd_shape_uses_density(h->T, a.K, h->num_cu), stream);
     return hip_status(epk::launch_combine_bwd(a, stream));
 }
 

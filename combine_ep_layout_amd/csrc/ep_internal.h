@@ -108,6 +108,8 @@ struct CombineBwdArgs {
     const float* weights;
     void* grad_eo;              // bf16 [cap, H], real rows written
     float* grad_w;              // fp32 [T, K]
+    int32_t density;            // Density of the layout: the launch shape
+    int32_t num_cu;
 };
 
 struct ConsumeArgs {
@@ -163,6 +165,9 @@ bool combine_shape_uses_density(int T, int H, int num_cu);
 // depends on the routing density for these sizes (top_k up to 8 and at least
 // 64 MiB of x).
 bool dispatch_shape_uses_density(int T, int H, int K);
+// Whether the combine backward's launch shape depends on the routing density
+// (top_k from 5 to 8, on grids that are not resident at once).
+bool combine_bwd_shape_uses_density(int T, int K, int num_cu);
 
 // Workgroups the multi-workgroup layout path needs for S slots.
 inline int layout_blocks(int64_t S) {

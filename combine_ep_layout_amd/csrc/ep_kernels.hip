@@ -55,8 +55,7 @@ constexpr int kStageGrid = 8192;        // read pass over x before the dense-rou
 constexpr int kCombineResidentWaves = 8;   // combine grids up to this many waves per CU: full occupancy
 constexpr int kCombineDenseLds = 55296;    // unused LDS per combine workgroup for dense routing: 2 per CU
 constexpr int kBwdChunks = 2;           // combine backward: 16-byte chunks per lane in flight
-constexpr int kCastLds = 32768;         // cast back: unused LDS per workgroup for power-of-two scales
-constexpr int kCastLdsMinGrid = 16384;  // ... on grids of at least this many workgroups
+constexpr int kBwdDenseLds = 55296;     // unused LDS per combine-backward workgroup for dense routing: 2 per CU
 constexpr int kCastUnits = 2;           // cast back: 16-channel units per lane per item
 constexpr int kGateTokens = 16;         // gated combine: most tokens per workgroup (<= 64)
 constexpr int kGateWaves = 16;          // gated combine: most waves per workgroup
@@ -1632,9 +1631,18 @@ __global__ __launch_bounds__(256) void k_tile_consume(ConsumeArgs a) {
 // dispatch's flavours and layouts.  One work item is one wave over up to
 // 64 * kCastUnits units of 16 channels of one row: 16 bytes of codes in,
 // 32 bytes of bf16 out per unit, the group's scale read once per unit.
+// A lane's 32 output bytes are not next to its neighbours', so the wave
+// passes each group of 64 decoded units through LDS (its own 2 KB per group)
+// and stores them as two 1 KB runs, one 16-byte chunk per lane: every store
+// instruction then writes whole 128-byte lines (146048 rows at hidden 7168,
+// UE8M0 scales: 588 -> 543 us; float32 scales 680 -> 656 us).  A wave's
+// LDS accesses run in order, so between its writes and its reads only the
+// compiler has to be kept from reordering them.
 __global__ __launch_bounds__(256) void k_cast_back(CastBackArgs a, int nseg) {
     constexpr int U = kCastUnits;
+    __shared__ u32x4 s_stage[4][U][2 * kWave];          // per wave and unit group
     const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
     const int64_t items = a.rows * nseg;
     for (int64_t it = (int64_t)blockIdx.x * 4 + (threadIdx.x / kWave); it < items;
          it += (int64_t)gridDim.x * 4) {
@@ -1652,9 +1660,11 @@ __global__ __launch_bounds__(256) void k_cast_back(CastBackArgs a, int nseg) {
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int c = seg * (kWave * U) + u * kWave + lane;
-            if (c >= nunit) continue;
-            const int g = c >> 3;
+            const int c0 = seg * (kWave * U) + u * kWave;    // first unit of the group
+            if (c0 >= nunit) continue;                       // uniform per wave
+            const int c = c0 + lane;
+            const bool act = c < nunit;
+            const int g = (act ? c : 0) >> 3;                // lanes past the row decode nothing stored
             u32x4 o0, o1;
             // a power-of-two scale goes through the hardware conversion: every
             // UE8M0 byte, and float scales that are exactly 2^e (the flavour's
@@ -1709,8 +1719,19 @@ __global__ __launch_bounds__(256) void k_cast_back(CastBackArgs a, int nseg) {
                     else { o1[2 * (i - 2)] = lo; o1[2 * (i - 2) + 1] = hi; }
                 }
             }
-            store_row<kStoreNonTemporal>(dst, a.H * 2, 2 * c, o0);
-            store_row<kStoreNonTemporal>(dst, a.H * 2, 2 * c + 1, o1);
+            u32x4* st = s_stage[wv][u];
+            st[2 * lane] = o0;                               // unit c0 + lane: chunks 2 lane, 2 lane + 1
+            st[2 * lane + 1] = o1;
+            // other lanes' writes are read next: keep the compiler from moving
+            // the reads above the writes (the hardware runs them in order)
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_wave_barrier();
+            const u32x4 r0 = st[lane];
+            const u32x4 r1 = st[kWave + lane];
+            const int n16 = 2 * nunit;                       // 16-byte chunks per row
+            if (2 * c0 + lane < n16) store_row<kStoreNonTemporal>(dst, a.H * 2, 2 * c0 + lane, r0);
+            if (2 * c0 + kWave + lane < n16)
+                store_row<kStoreNonTemporal>(dst, a.H * 2, 2 * c0 + kWave + lane, r1);
         }
     }
 }
@@ -1882,7 +1903,17 @@ template <int KT, bool MANY>
 hipError_t combine_bwd_kt(const CombineBwdArgs& a, hipStream_t st) {
     if constexpr (!MANY) {
         const int nseg = (a.H / 8 + kWave * kBwdChunks - 1) / (kWave * kBwdChunks);
-        hipLaunchKernelGGL((k_combine_bwd_slots<KT>), dim3(a.T), dim3(kWave * KT), 0, st, a, nseg);
+        // Dense routing: at most two workgroups per compute unit, capped by
+        // unused LDS, so fewer rows are written at once (16384 tokens x
+        // top-8, hidden 7168: 734 -> 714 us back to back, 774 -> 759 us with
+        // the caches flushed; 32768 x top-8, hidden 4096: 804 -> 794 us).
+        // Sparse routing would lose half its speed that way (8192 tokens,
+        // one row each on average: 31 -> 64 us) and keeps full occupancy.
+        // The results are the same in both shapes.
+        const size_t lds = KT == kSlotGroup && a.density == kDensityDense &&
+                                   combine_bwd_shape_uses_density(a.T, a.K, a.num_cu)
+                               ? kBwdDenseLds : 0;
+        hipLaunchKernelGGL((k_combine_bwd_slots<KT>), dim3(a.T), dim3(kWave * KT), lds, st, a, nseg);
     } else {
         const int grid = (a.T + 3) / 4;
         hipLaunchKernelGGL((k_combine_bwd<KT, MANY>), dim3(grid), dim3(256), 0, st, a);
@@ -1983,20 +2014,20 @@ hipError_t launch_cast_back(const CastBackArgs& a, hipStream_t stream) {
     const int64_t items = a.rows * nseg;
     int64_t grid = (items + 3) / 4;
     if (grid > (1 << 20)) grid = 1 << 20;          // grid-stride beyond a million workgroups
-    // Power-of-two scales decode through the hardware conversion and a large
-    // cast back is memory-bound: unused LDS caps it at five workgroups per
-    // compute unit (160 KB of LDS each), so fewer rows are in flight at once,
-    // which measured 6-11 % faster on grids of 16384 workgroups and up (16384
-    // rows at hidden 7168).  Small grids are
-    // latency-bound and arbitrary float32 scales take the ALU-heavy software
-    // decode; both keep every wave they can get.
-    const size_t lds = a.scale_kind != kScaleF32 && grid >= kCastLdsMinGrid ? kCastLds : 0;
-    hipLaunchKernelGGL(k_cast_back, dim3((uint32_t)grid), dim3(256), lds, stream, a, nseg);
+    // Full occupancy: with whole-line stores the cast back measured fastest
+    // with every wave it can get (UE8M0 543 us against 548 / 603 us at six /
+    // five workgroups per compute unit).
+    hipLaunchKernelGGL(k_cast_back, dim3((uint32_t)grid), dim3(256), 0, stream, a, nseg);
     return hipGetLastError();
 }
 
 bool dispatch_shape_uses_density(int T, int H, int K) {
     return T > 0 && K <= kSlotGroup && (int64_t)T * H * 2 >= kDenseDispatchMinBytes;
+}
+
+bool combine_bwd_shape_uses_density(int T, int K, int num_cu) {
+    // one workgroup of kSlotGroup waves per token; four fit a compute unit
+    return T > 0 && K > 4 && K <= kSlotGroup && (int64_t)T > (int64_t)num_cu * 4;
 }
 
 bool combine_shape_uses_density(int T, int H, int num_cu) {

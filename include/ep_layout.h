@@ -282,8 +282,8 @@ ep_status ep_combine_gated(const ep_handle* h, uint32_t epoch, const void* exper
                            int32_t hidden, void* y, uint32_t round, uint32_t spin_limit_us,
                            hipStream_t stream);
 
-/* Launch-shape hint of ep_combine, ep_dispatch_backward and the bf16
- * ep_dispatch.  EP_DENSITY_AUTO (the default) takes the current layout's
+/* Launch-shape hint of ep_combine, ep_dispatch_backward, ep_combine_backward
+ * and the bf16 ep_dispatch.  EP_DENSITY_AUTO (the default) takes the current layout's
  * reported density as described at ep_combine (waiting for it if needed; the
  * dense shape under graph capture).  EP_DENSITY_SPARSE or EP_DENSITY_DENSE fix
  * the shape for the handle's later calls, which then never wait: for callers
@@ -326,7 +326,10 @@ ep_status ep_fp8_cast_back(const void* q, const void* scales, uint32_t flags, in
  *                    <grad_y[t], expert_out[row(t,k)]> accumulated in double
  *                    (bf16 x bf16 products are exact) and rounded once to
  *                    float; 0 for masked slots.
- * hidden % 8 == 0.  Rejected while a borrowed view is out. */
+ * hidden % 8 == 0.  Rejected while a borrowed view is out.  For top_k 5..8
+ * on batches too large to be resident at once the launch shape follows the
+ * layout's reported routing density exactly as at ep_combine (same wait, same
+ * hint); the results are the same in every shape. */
 ep_status ep_combine_backward(const ep_handle* h, uint32_t epoch, const void* grad_y,
                               const void* expert_out, int32_t hidden, void* grad_expert_out,
                               float* grad_weights, hipStream_t stream);

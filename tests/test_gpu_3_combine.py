@@ -161,13 +161,15 @@ def test_nan_padding_is_never_read():
 
 @pytest.mark.parametrize("sync", [True, False])
 def test_combine_after_dense_and_sparse_layouts(sync):
-    """The plain combine and the dispatch backward take their launch shape
-    from the density of the current layout (two workgroups per compute unit
-    for 4 or more rows per token, full occupancy below), waiting for the
-    layout kernel's report when it has not arrived; the results do not
-    depend on it.  One handle alternates a dense and a sparse routing of the
-    same size, with or without a synchronisation after each layout, and every
-    combine and dispatch backward is compared with the oracle."""
+    """The plain combine, the dispatch backward and the combine backward take
+    their launch shape from the density of the current layout (two
+    workgroups per compute unit for 4 or more rows per token, full occupancy
+    below), waiting for the layout kernel's report when it has not arrived;
+    the results do not depend on it.  One handle alternates a dense and a
+    sparse routing of the same size, with or without a synchronisation after
+    each layout, and every combine, dispatch backward and combine backward is
+    compared with the oracle (gradient rows bit for bit, weight gradients
+    within the bound of the backward tests)."""
     say(f"[combine] alternating dense / sparse layouts on one handle, 6000 tokens, sync={sync}")
     dense = CONFIGS["stream"].replace(tokens=6000, hidden=1024, mask_frac=0.0, fp8=False,
                                       tile_ready=False)
@@ -189,6 +191,23 @@ def test_combine_after_dense_and_sparse_layouts(sync):
         gx = h.dispatch_backward(epoch, to_dev_bf16(eo))
         assert np.array_equal(bits_of(gx), oracle.dispatch_backward(eo, L["slot_to_pool_row"],
                                                                       cfg.tokens, cfg.top_k))
-        say(f"  layout {it}: {rows / cfg.tokens:.2f} rows per token, combine and dispatch backward match")
+        gy = bf16_from_f32(rng.standard_normal((cfg.tokens, cfg.hidden), dtype=np.float32))
+        geo = torch.zeros((h.capacity_rows, cfg.hidden), dtype=torch.bfloat16, device=dev())
+        _, gw = h.combine_backward(epoch, to_dev_bf16(gy), to_dev_bf16(eo), geo)
+        geo_or, gw_or = oracle.combine_backward(gy, eo, L["slot_to_pool_row"], d["topk_weights"],
+                                                grad_eo_init=np.zeros((h.capacity_rows, cfg.hidden),
+                                                                      np.uint16))
+        assert np.array_equal(bits_of(geo), geo_or)
+        s2r = L["slot_to_pool_row"].reshape(cfg.tokens, cfg.top_k)
+        valid = s2r >= 0
+        got = gw.cpu().numpy()
+        assert (got[~valid] == 0).all()
+        ts, ks = np.nonzero(valid)
+        absum = np.abs(bf16_to_f32(gy[ts]).astype(np.float64) *
+                       bf16_to_f32(eo[s2r[ts, ks]]).astype(np.float64)).sum(1)
+        bound = (np.spacing(np.abs(gw_or[ts, ks])).astype(np.float64) +
+                 2 * cfg.hidden * 2.0 ** -53 * absum)
+        assert np.all(np.abs(got[ts, ks].astype(np.float64) - gw_or[ts, ks]) <= bound)
+        say(f"  layout {it}: {rows / cfg.tokens:.2f} rows per token, combine and both backward calls match")
     assert h.sync_status() == 0
     h.close()
