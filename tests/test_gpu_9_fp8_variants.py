@@ -240,6 +240,32 @@ def test_cast_back_every_code(kind, mn):
     assert np.array_equal(bits_of(out), want)
 
 
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("mn", [False, True])
+def test_cast_back_ragged_unit_groups(kind, mn):
+    """The cast back stores each group of 64 decoded 16-channel units as two
+    1 KB runs; a row's last group may hold fewer units (hidden 640: 40,
+    896: 56, 1152: 8, 1920: 56) or exactly fill it (hidden 65536, the
+    largest), so only part of the runs is stored.  Every code value, random
+    scales, rows against the oracle bit for bit."""
+    import combine_ep_layout_amd as ep
+    rng = np.random.default_rng(31)
+    for H, rows in ((640, 37), (896, 29), (1152, 33), (1920, 21), (65536, 3)):
+        say(f"[fp8var] cast back ragged groups kind={kind} mn={mn} hidden={H} rows={rows}")
+        G = H // 128
+        q = rng.integers(0, 256, size=(rows, H), dtype=np.uint8)
+        if kind == "ue8m0":
+            rm = rng.integers(100, 160, size=(rows, G), dtype=np.uint8)
+        elif kind == "pow2_f32":
+            rm = oracle.pow2_scales_from_ue8m0(rng.integers(100, 160, size=(rows, G)).astype(np.uint8))
+        else:
+            rm = np.abs(rng.standard_normal((rows, G))).astype(np.float32) + np.float32(0.01)
+        s_host = oracle.scales_to_mn_major(rm, rows + 3) if mn else rm
+        s_dev = torch.from_numpy(s_host.view(np.int32) if s_host.dtype == np.uint32 else s_host).to(dev())
+        out = ep.cast_back(torch.from_numpy(q).to(dev()), s_dev, kind, mn, rows=rows)
+        assert np.array_equal(bits_of(out), oracle.cast_back(q, s_host, kind, mn)), H
+
+
 def test_fp8_variant_rejections():
     import combine_ep_layout_amd as ep
     say("[fp8var] rejections")
