@@ -283,9 +283,9 @@ ep_status ep_combine_gated(const ep_handle* h, uint32_t epoch, const void* exper
                            hipStream_t stream);
 
 /* Launch-shape hint of ep_combine, ep_dispatch_backward, ep_combine_backward
- * and the bf16 ep_dispatch.  EP_DENSITY_AUTO (the default) takes the current layout's
- * reported density as described at ep_combine (waiting for it if needed; the
- * dense shape under graph capture).  EP_DENSITY_SPARSE or EP_DENSITY_DENSE fix
+ * and the bf16 ep_dispatch.  EP_DENSITY_AUTO (the default) takes the current
+ * layout's reported density as described at ep_combine (waiting for it if
+ * needed; the dense shape under graph capture).  EP_DENSITY_SPARSE or EP_DENSITY_DENSE fix
  * the shape for the handle's later calls, which then never wait: for callers
  * that capture these calls in a HIP graph, that enqueue far ahead of the GPU
  * (whose calls would otherwise wait for the layout kernel to run), or that
