@@ -500,8 +500,8 @@ class EpHandle:
         return counts, int(nt[0])
 
     def set_density_hint(self, hint: int) -> None:
-        """EP_DENSITY_AUTO / _SPARSE / _DENSE: launch shape of the combine calls and of
-        the bf16 dispatch of at least 64 MiB of x."""
+        """EP_DENSITY_AUTO / _SPARSE / _DENSE: launch shape of the combine calls (forward
+        and both backward calls) and of the bf16 dispatch of at least 64 MiB of x."""
         _check(_lib.ep_set_density_hint(self._h, int(hint)), "ep_set_density_hint")
 
     def layout_density(self, stream=None) -> int:

@@ -144,6 +144,42 @@ def test_backward_top_k_above_8(top_k):
     h.close()
 
 
+@pytest.mark.parametrize("name", ["stream", "share"])
+def test_combine_backward_every_launch_shape(name):
+    """combine_grads runs two workgroups per compute unit for dense routing
+    and full occupancy for sparse routing (batches too large to be resident
+    at once).  Both shapes forced by the density hint, and the shape the
+    layout's report picks, give bit-identical gradient rows and weight
+    gradients, which match the oracle (dense: 4096 tokens x top-8 of 128
+    experts; sparse: 4096 tokens with 16 of 128 experts kept)."""
+    import combine_ep_layout_amd as ep
+    cfg = CONFIGS[name].replace(tokens=4096, hidden=1024, fp8=False, tile_ready=False)
+    say(f"[backward] every launch shape, {name} routing, {cfg.tokens} tokens")
+    d = generate(cfg, 21)
+    L = oracle.layout(d["topk_idx"], cfg.num_experts, cfg.block_m)
+    eo, gy, s2r, valid = _rows_and_grads(cfg, L)
+    h = new_handle(cfg)
+    epoch = h.layout(*device_routing(d))
+    assert h.layout_density() == (ep.EP_DENSITY_DENSE if name == "stream" else ep.EP_DENSITY_SPARSE)
+    cap, H = h.capacity_rows, cfg.hidden
+    outs = []
+    for hint in (ep.EP_DENSITY_AUTO, ep.EP_DENSITY_DENSE, ep.EP_DENSITY_SPARSE):
+        h.set_density_hint(hint)
+        geo = torch.full((cap, H), POISON_BF16 - 0x10000, dtype=torch.int16, device=dev()).view(torch.bfloat16)
+        _, gw = h.combine_backward(epoch, to_dev_bf16(gy), to_dev_bf16(eo), geo)
+        outs.append((bits_of(geo), gw.cpu().numpy()))
+    h.set_density_hint(ep.EP_DENSITY_AUTO)
+    for geo_b, gw_b in outs[1:]:
+        assert np.array_equal(geo_b, outs[0][0])
+        assert np.array_equal(gw_b.view(np.uint32), outs[0][1].view(np.uint32))
+    geo_or, gw_or = oracle.combine_backward(gy, eo, L["slot_to_pool_row"], d["topk_weights"],
+                                            grad_eo_init=np.full((cap, H), POISON_BF16, np.uint16))
+    assert np.array_equal(outs[0][0], geo_or)
+    _check_grad_w(outs[0][1], gw_or, gy, eo, s2r, valid)
+    assert h.sync_status() == ep.EP_OK
+    h.close()
+
+
 def test_backward_edges_and_rejections():
     import combine_ep_layout_amd as ep
     say("[backward] edges and rejections")
