@@ -86,3 +86,34 @@ def test_max_tokens_top32():
     assert diff.max() <= 1
     assert h.sync_status() == ep.EP_OK
     h.close()
+
+
+@pytest.mark.parametrize("kind,mn", [("ue8m0", False), ("f32", True)])
+def test_cast_back_grid_stride(kind, mn):
+    """A cast back of more work items than the grid holds (4.3 M rows of one
+    128-channel group: 4.3 M one-wave items against a grid capped at 2^20
+    four-wave workgroups), so some waves take a second item and reuse their
+    LDS staging.  Rows at the start, around the wrap point (item 4 * 2^20)
+    and at the end, and a random sample, against the oracle bit for bit."""
+    import combine_ep_layout_amd as ep
+    rows, H = 4_300_000, 128
+    say(f"[limits] cast back grid stride kind={kind} mn={mn} rows={rows}")
+    g = torch.Generator(device=dev())
+    g.manual_seed(13)
+    q = torch.randint(0, 256, (rows, H), generator=g, device=dev(), dtype=torch.int32).to(torch.uint8)
+    if kind == "ue8m0":
+        rm = torch.randint(100, 160, (rows, 1), generator=g, device=dev(), dtype=torch.int32).to(torch.uint8)
+    else:
+        rm = torch.rand((rows, 1), generator=g, device=dev()) + 0.01
+    # MN-major float scales: [groups, ld] with ld = rows
+    s_dev = rm.t().contiguous() if mn else rm
+    out = ep.cast_back(q, s_dev, kind, mn, rows=rows)
+    wrap = 4 * (1 << 20)
+    rng = np.random.default_rng(3)
+    pick = np.unique(np.concatenate([np.arange(0, 2000), np.arange(wrap - 1000, wrap + 1000),
+                                     np.arange(rows - 2000, rows), rng.integers(0, rows, 5000)]))
+    idx = torch.from_numpy(pick).to(dev())
+    q_h = q[idx].cpu().numpy()
+    s_h = rm[idx].cpu().numpy()
+    want = oracle.cast_back(q_h, s_h, kind, False)
+    assert np.array_equal(bits_of(out[idx]), want)
