@@ -284,3 +284,61 @@ def test_capture_without_layout_is_refused():
     assert h.sync_status() == ep.EP_OK
     del g, g2
     h.close()
+
+
+def test_backward_in_graph():
+    """combine_grads and dispatch_grads captured in a HIP graph after an eager
+    layout (the density hint left at auto, so the capture takes the dense
+    shape without waiting) and replayed on new grad_y / expert rows written
+    into the captured buffers: every replay equals eager calls on the same
+    inputs bit for bit (gradient rows, weight gradients, grad_x)."""
+    import combine_ep_layout_amd as ep
+    say("[graph] combine_grads + dispatch_grads, 4096 tokens x top-8, hidden 1024")
+    cfg = CONFIGS["stream"].replace(tokens=4096, hidden=1024, fp8=False, tile_ready=False)
+    T, K, H = cfg.tokens, cfg.top_k, cfg.hidden
+    d = generate(cfg, 8)
+    h = new_handle(cfg)
+    cap = h.capacity_rows
+    epoch = h.layout(torch.from_numpy(d["topk_idx"]).to(dev()), torch.from_numpy(d["topk_weights"]).to(dev()))
+    gy = torch.empty(T, H, dtype=torch.bfloat16, device=dev())
+    eo = torch.empty(cap, H, dtype=torch.bfloat16, device=dev())
+    geo = torch.zeros(cap, H, dtype=torch.bfloat16, device=dev())
+    gw = torch.zeros(T, K, dtype=torch.float32, device=dev())
+    gx = torch.zeros(T, H, dtype=torch.bfloat16, device=dev())
+
+    def load(seed):
+        gen = torch.Generator(device=dev())
+        gen.manual_seed(seed)
+        gy.copy_(torch.randn(T, H, generator=gen, device=dev()).to(torch.bfloat16))
+        eo.copy_(torch.randn(cap, H, generator=gen, device=dev()).to(torch.bfloat16))
+
+    load(0)
+    s = torch.cuda.Stream()                              # default priority
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                           # warm-up outside the capture
+        ep.ep_combine_backward(h.raw, epoch, gy, eo, geo, gw)
+        ep.ep_dispatch_backward(h.raw, epoch, geo, gx)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        ep.ep_combine_backward(h.raw, epoch, gy, eo, geo, gw)
+        ep.ep_dispatch_backward(h.raw, epoch, geo, gx)
+    torch.cuda.synchronize()
+    for seed in (1, 2, 3):
+        load(seed)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        geo_e = torch.zeros_like(geo)
+        _, gw_e = h.combine_backward(epoch, gy, eo, geo_e)
+        gx_e = h.dispatch_backward(epoch, geo_e)
+        torch.cuda.synchronize()
+        real = torch.from_numpy(np.flatnonzero(h.array("pool_recv_token").cpu().numpy() >= 0)).to(dev())
+        assert torch.equal(geo[real].view(torch.int16), geo_e[real].view(torch.int16))
+        assert torch.equal(gw.view(torch.int32), gw_e.view(torch.int32))
+        assert torch.equal(gx.view(torch.int16), gx_e.view(torch.int16))
+        say(f"  replay with seed {seed} matches the eager calls")
+    assert h.sync_status() == 0
+    del g
+    h.close()
