@@ -1724,7 +1724,7 @@ __global__ __launch_bounds__(256) void k_cast_back(CastBackArgs a, int nseg) {
             st[2 * lane + 1] = o1;
             // other lanes' writes are read next: keep the compiler from moving
             // the reads above the writes (the hardware runs them in order)
-            asm volatile("" ::: "memory");
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
             __builtin_amdgcn_wave_barrier();
             const u32x4 r0 = st[lane];
             const u32x4 r1 = st[kWave + lane];
